@@ -1,0 +1,179 @@
+"""fp64 oracle: matching-pursuit encode and hierarchical coded decode attention.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring). Everything is computed
+in float64 from the exact values of the (bf16 / fp16 / fp32) inputs.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = ["unpack_codes", "pack_codes", "mp_encode", "decode_attn",
+           "select_topk", "selected_count"]
+
+
+# ---------------------------------------------------------------------------
+# Code words
+# ---------------------------------------------------------------------------
+def unpack_codes(words: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Split packed 32-bit code words into (atom index int64, coefficient
+    float64). Bits 0-15 hold the uint16 atom index, bits 16-31 the IEEE
+    binary16 coefficient (review page, FAQ on the 15x figure: a vector is
+    stored as the indices and coefficients of its atoms)."""
+    w = np.asarray(words, dtype=np.uint32)
+    idx = (w & np.uint32(0xFFFF)).astype(np.int64)
+    coef = (w >> np.uint32(16)).astype(np.uint16).view(np.float16).astype(np.float64)
+    return idx, coef
+
+
+def pack_codes(idx: np.ndarray, coef: np.ndarray) -> np.ndarray:
+    """Pack atom indices and coefficients into 32-bit words; the coefficient
+    is rounded to binary16 with round-to-nearest-even (NumPy's float16 cast).
+    Reading: the pursuit runs on unrounded coefficients and rounding happens
+    only here, when the code is stored."""
+    i = np.asarray(idx).astype(np.uint32)
+    c = np.asarray(coef, dtype=np.float64).astype(np.float16)
+    return (i | (c.view(np.uint16).astype(np.uint32) << np.uint32(16))).astype(np.uint32)
+
+
+# ---------------------------------------------------------------------------
+# Encode: projection-based greedy pursuit (matching pursuit, no refit)
+# ---------------------------------------------------------------------------
+def mp_encode(X: np.ndarray, D: np.ndarray, K: int, *, trace: bool = False,
+              block: int = 512):
+    """Greedy pursuit of each row of X over the atoms (rows) of D.
+
+    Review page, Summary and Strengths: a projection-based greedy pursuit
+    replaces OMP to avoid least-squares refits. Per vector x:
+        r_0 = x
+        for k = 0 .. K-1:
+            c_a   = <r_k, d_a>           for every atom a
+            a_k   = smallest a with |c_a| maximal   (np.argmax takes the first)
+            g_k   = c_{a_k}                          (projection coefficient)
+            r_k+1 = r_k - g_k * d_{a_k}
+    Readings (the pages are silent): the coefficient is <r, d> with no
+    division by |d|^2 (atoms are unit-norm); an atom may be picked again;
+    ties go to the lowest atom index; coefficients are kept unrounded during
+    the pursuit.
+
+    Vectors are independent, so rows are processed `block` at a time; each
+    row goes through exactly the steps above.
+
+    Returns (idx int64 [n,K], gamma float64 [n,K], resid_norm float64 [n]);
+    with trace=True also the residual norms before each step [n, K+1].
+    """
+    X = np.asarray(X, dtype=np.float64)
+    D = np.asarray(D, dtype=np.float64)
+    n = X.shape[0]
+    idx = np.zeros((n, K), dtype=np.int64)
+    gam = np.zeros((n, K), dtype=np.float64)
+    rn = np.zeros(n, dtype=np.float64)
+    tr = np.zeros((n, K + 1), dtype=np.float64) if trace else None
+    for s in range(0, n, block):
+        e = min(n, s + block)
+        R = X[s:e].copy()
+        rows = np.arange(e - s)
+        for k in range(K):
+            if trace:
+                tr[s:e, k] = np.linalg.norm(R, axis=1)
+            C = R @ D.T
+            a = np.argmax(np.abs(C), axis=1)
+            g = C[rows, a]
+            R = R - g[:, None] * D[a]
+            idx[s:e, k] = a
+            gam[s:e, k] = g
+        rn[s:e] = np.linalg.norm(R, axis=1)
+        if trace:
+            tr[s:e, K] = rn[s:e]
+    if trace:
+        return idx, gam, rn, tr
+    return idx, gam, rn
+
+
+# ---------------------------------------------------------------------------
+# Decode: query-aware hierarchical sparsity over coded keys and values
+# ---------------------------------------------------------------------------
+def selected_count(T: int, top_num: int, top_den: int) -> int:
+    """m = ceil(T * num / den) in integer arithmetic, clamped to [1, T].
+    Reading of "the top 10%" (review page, Summary): a ceiling, never empty."""
+    return max(1, min(T, -(-T * top_num // top_den)))
+
+
+def select_topk(scores: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest entries of each row, ties to the lower index,
+    returned in ascending index order. (The 'top 10%' step of the review
+    page's Summary, as a stand-alone operation.)"""
+    s = np.atleast_2d(np.asarray(scores, dtype=np.float64))
+    out = np.zeros((s.shape[0], k), dtype=np.int64)
+    for r in range(s.shape[0]):
+        order = np.argsort(-s[r], kind="stable")
+        out[r] = np.sort(order[:k])
+    return out
+
+
+def decode_attn(q, dk, dv, key_codes, val_codes, klow: int, khigh: int,
+                top_num: int, top_den: int, scale: float):
+    """Hierarchical coded decode attention for one layer.
+
+    Review page, Summary: query-aware hierarchical sparsity scores all tokens
+    at Klow atoms and refines the top 10% to Khigh. FAQ: 3 atoms score most
+    tokens. Abstract page: each key/value is a linear combination of static
+    dictionary vectors, so <q, k_t> = sum_j kappa_tj <q, d_{i_tj}>.
+
+    Inputs: q [B,Hq,d]; dk, dv [N,d]; key_codes, val_codes uint32
+    [B,Hkv,T,K]. For each batch b and query head h (KV head g = h // G,
+    G = Hq / Hkv):
+        u      = scale * (Dk q_h)                         [N]
+        s_low  = sum_{j<klow}  kappa_tj * u[i_tj]         every t < T
+        S      = the m tokens with the largest s_low, ties to lower t,
+                 m = ceil(T*num/den)
+        s_high = sum_{j<khigh} kappa_tj * u[i_tj]         t in S
+        p      = softmax over S of s_high
+        w[a]   = sum_{t in S} p_t sum_{j<K} kappa^v_tj [i^v_tj == a]
+        out_h  = Dv^T w
+    Readings: the softmax runs over S only (unselected tokens are dropped);
+    selection is per query head; the key code's first klow slots are the
+    "low" atoms; values use all K slots; the scale multiplies the scores.
+
+    Returns a dict of float64 arrays: u [B,Hq,N], s_low [B,Hq,T],
+    sel int64 [B,Hq,m] ascending, s_high [B,Hq,m], p [B,Hq,m],
+    w [B,Hq,N], out [B,Hq,d], and m.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    dk = np.asarray(dk, dtype=np.float64)
+    dv = np.asarray(dv, dtype=np.float64)
+    B, Hq, d = q.shape
+    _, Hkv, T, K = key_codes.shape
+    N = dk.shape[0]
+    G = Hq // Hkv
+    m = selected_count(T, top_num, top_den)
+    res = {k: None for k in ("u", "s_low", "sel", "s_high", "p", "w", "out")}
+    res["u"] = np.zeros((B, Hq, N))
+    res["s_low"] = np.zeros((B, Hq, T))
+    res["sel"] = np.zeros((B, Hq, m), dtype=np.int64)
+    res["s_high"] = np.zeros((B, Hq, m))
+    res["p"] = np.zeros((B, Hq, m))
+    res["w"] = np.zeros((B, Hq, N))
+    res["out"] = np.zeros((B, Hq, d))
+    res["m"] = m
+    for b in range(B):
+        for g in range(Hkv):
+            ki, kc = unpack_codes(key_codes[b, g])
+            vi, vc = unpack_codes(val_codes[b, g])
+            for h in range(g * G, (g + 1) * G):
+                u = scale * (dk @ q[b, h])
+                s_low = (kc[:, :klow] * u[ki[:, :klow]]).sum(axis=1)
+                order = np.argsort(-s_low, kind="stable")
+                S = np.sort(order[:m])
+                s_high = (kc[S, :khigh] * u[ki[S, :khigh]]).sum(axis=1)
+                e = np.exp(s_high - s_high.max())
+                p = e / e.sum()
+                w = np.bincount(vi[S].ravel(), weights=(p[:, None] * vc[S]).ravel(),
+                                minlength=N)
+                res["u"][b, h] = u
+                res["s_low"][b, h] = s_low
+                res["sel"][b, h] = S
+                res["s_high"][b, h] = s_high
+                res["p"][b, h] = p
+                res["w"][b, h] = w
+                res["out"][b, h] = dv.T @ w
+    return res

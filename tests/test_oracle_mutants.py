@@ -1,0 +1,85 @@
+"""Planted mistakes: each mutant is the oracle's own source with one plausible
+error written in (a flipped sign, a dropped term, a wrong index or count, a
+different tie rule ...). Every mutant must fail at least one pin, which shows
+the pins constrain the oracle rather than restate it. All of this runs on the
+CPU and touches nothing outside a throw-away module namespace."""
+import inspect
+import types
+
+import pytest
+
+import oracle.sdkv_oracle as src_mod
+from tests import oracle_pins as pins
+
+SRC = inspect.getsource(src_mod)
+
+ENCODE_MUTANTS = {
+    "update_sign": ("R = R - g[:, None] * D[a]", "R = R + g[:, None] * D[a]"),
+    "argmax_no_abs": ("a = np.argmax(np.abs(C), axis=1)", "a = np.argmax(C, axis=1)"),
+    "ties_to_last": ("a = np.argmax(np.abs(C), axis=1)",
+                     "a = C.shape[1] - 1 - np.argmax(np.abs(C)[:, ::-1], axis=1)"),
+    "normalised_coef": ("g = C[rows, a]", "g = C[rows, a] / (D[a] ** 2).sum(axis=1)"),
+    "stale_residual": ("C = R @ D.T", "C = X[s:e] @ D.T"),
+    "one_step_short": ("for k in range(K):\n            if trace:",
+                       "for k in range(K - 1):\n            if trace:"),
+}
+
+DECODE_MUTANTS = {
+    "low_uses_khigh": ("s_low = (kc[:, :klow] * u[ki[:, :klow]])",
+                       "s_low = (kc[:, :khigh] * u[ki[:, :khigh]])"),
+    "high_uses_klow": ("s_high = (kc[S, :khigh] * u[ki[S, :khigh]])",
+                       "s_high = (kc[S, :klow] * u[ki[S, :klow]])"),
+    "floor_count": ("return max(1, min(T, -(-T * top_num // top_den)))",
+                    "return max(1, min(T, T * top_num // top_den))"),
+    "ties_to_higher": ('order = np.argsort(-s_low, kind="stable")',
+                       'order = (T - 1 - np.argsort(-s_low[::-1], kind="stable"))'),
+    "softmax_all_tokens": ("p = e / e.sum()",
+                           "p = e / (e.sum() + np.exp(np.delete(s_low, S) - s_high.max()).sum())"),
+    "no_scale": ("u = scale * (dk @ q[b, h])", "u = (dk @ q[b, h])"),
+    "gqa_modulo": ("for h in range(g * G, (g + 1) * G):", "for h in range(g, Hq, Hkv):"),
+    "values_khigh_only": ("w = np.bincount(vi[S].ravel(), weights=(p[:, None] * vc[S]).ravel(),",
+                          "w = np.bincount(vi[S][:, :khigh].ravel(), weights=(p[:, None] * vc[S][:, :khigh]).ravel(),"),
+    "unweighted_values": ("weights=(p[:, None] * vc[S]).ravel()", "weights=(vc[S] / len(S)).ravel()"),
+    "value_dict_is_key_dict": ('res["out"][b, h] = dv.T @ w', 'res["out"][b, h] = dk.T @ w'),
+}
+
+
+def build(mutation):
+    old, new = mutation
+    assert old in SRC, old
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(SRC.replace(old, new), "<mutant>", "exec"), mod.__dict__)
+    return mod
+
+
+def _fails(checks, fn):
+    for chk in checks:
+        try:
+            chk(fn)
+        except Exception:
+            return True
+    return False
+
+
+@pytest.mark.parametrize("name", sorted(ENCODE_MUTANTS))
+def test_encode_mutant_is_caught(name):
+    m = build(ENCODE_MUTANTS[name])
+    caught = _fails(pins.ENCODE_CHECKS, lambda X, D, K: m.mp_encode(X, D, K))
+    if not caught:
+        try:
+            pins.check_energy_identity(lambda X, D, K: m.mp_encode(X, D, K, trace=True))
+        except Exception:
+            caught = True
+    assert caught, f"no pin catches encode mutant {name}"
+
+
+@pytest.mark.parametrize("name", sorted(DECODE_MUTANTS))
+def test_decode_mutant_is_caught(name):
+    m = build(DECODE_MUTANTS[name])
+    assert _fails(pins.DECODE_CHECKS, m.decode_attn), f"no pin catches decode mutant {name}"
+
+
+def test_unmutated_source_passes():
+    m = build(("import numpy as np", "import numpy as np"))
+    assert not _fails(pins.DECODE_CHECKS, m.decode_attn)
+    assert not _fails(pins.ENCODE_CHECKS, lambda X, D, K: m.mp_encode(X, D, K))
