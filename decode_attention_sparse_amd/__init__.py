@@ -1,0 +1,294 @@
+"""Python binding of libsdkv (dictionary-coded KV cache on MI355X).
+
+Argument marshalling only: every computation runs in the HIP kernels of
+libsdkv.so, reached through its C ABI (include/sdkv.h). PyTorch supplies
+device memory and the current HIP stream. Importing works without a GPU;
+calling a compute entry point needs the built library and a GPU, and raises
+if either is missing (there is no CPU fallback).
+
+Entry points (same names as the C ABI):
+  sdkv_encode(x, dictionary, K, ...)        greedy pursuit codes
+  sdkv_decode_attn(q, dk, dv, key_codes, val_codes, ...)
+  sdkv_select_topk(scores, k, ...)
+Code words are carried in torch.int32 tensors holding the uint32 bit
+patterns (atom index in bits 0-15, binary16 coefficient in bits 16-31).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsdkv.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "sdkv.h")
+
+SDKV_OK, SDKV_ERR_NULL, SDKV_ERR_SHAPE, SDKV_ERR_DTYPE = 0, 1, 2, 3
+SDKV_ERR_UNSUPPORTED, SDKV_ERR_WORKSPACE, SDKV_ERR_DEVICE = 4, 5, 6
+SDKV_BF16, SDKV_F32 = 0, 1
+
+c_void_p, c_int32, c_int64, c_float = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+c_size_t = ctypes.c_size_t
+
+
+class EncodeArgs(ctypes.Structure):
+    _fields_ = [("x", c_void_p), ("x_dtype", c_int32), ("dict", c_void_p),
+                ("dict_dtype", c_int32), ("n", c_int64), ("d", c_int32),
+                ("n_atoms", c_int32), ("K", c_int32), ("codes", c_void_p),
+                ("coef_f32", c_void_p), ("resid_norm", c_void_p),
+                ("low_plane", c_void_p), ("klow", c_int32)]
+
+
+class AttnArgs(ctypes.Structure):
+    _fields_ = [("q", c_void_p), ("q_dtype", c_int32), ("dk", c_void_p),
+                ("dv", c_void_p), ("dict_dtype", c_int32), ("n_atoms", c_int32),
+                ("B", c_int32), ("Hq", c_int32), ("Hkv", c_int32), ("d", c_int32),
+                ("T", c_int64), ("key_low", c_void_p), ("key_codes", c_void_p),
+                ("val_codes", c_void_p), ("K", c_int32), ("klow", c_int32),
+                ("khigh", c_int32), ("top_num", c_int64), ("top_den", c_int64),
+                ("scale", c_float), ("out", c_void_p), ("u", c_void_p),
+                ("s_low", c_void_p), ("sel", c_void_p), ("s_high", c_void_p),
+                ("w", c_void_p)]
+
+
+class SdkvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib().sdkv_status_str(status).decode() if _LIB else str(status)
+        super().__init__(f"{where}: status {status} ({msg})")
+
+
+_LIB = None
+
+
+def _lib():
+    """Load libsdkv.so from the package directory (built by
+    `python -m decode_attention_sparse_amd.build`)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m decode_attention_sparse_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER
+        lib.sdkv_abi_version.restype = c_int32
+        lib.sdkv_status_str.restype = ctypes.c_char_p
+        lib.sdkv_status_str.argtypes = [c_int32]
+        lib.sdkv_selected_count.restype = c_int64
+        lib.sdkv_selected_count.argtypes = [c_int64, c_int64, c_int64]
+        lib.sdkv_encode_workspace.restype = c_int32
+        lib.sdkv_encode_workspace.argtypes = [P(EncodeArgs), P(c_size_t)]
+        lib.sdkv_encode.restype = c_int32
+        lib.sdkv_encode.argtypes = [P(EncodeArgs), c_void_p, c_size_t, c_void_p]
+        lib.sdkv_decode_attn_workspace.restype = c_int32
+        lib.sdkv_decode_attn_workspace.argtypes = [P(AttnArgs), P(c_size_t)]
+        lib.sdkv_decode_attn.restype = c_int32
+        lib.sdkv_decode_attn.argtypes = [P(AttnArgs), c_void_p, c_size_t, c_void_p]
+        lib.sdkv_select_topk_workspace.restype = c_int32
+        lib.sdkv_select_topk_workspace.argtypes = [c_int64, c_int64, c_int64, P(c_size_t)]
+        lib.sdkv_select_topk.restype = c_int32
+        lib.sdkv_select_topk.argtypes = [c_void_p, c_int64, c_int64, c_int64, c_int64,
+                                         c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+        _LIB = lib
+    return _LIB
+
+
+def lib():
+    return _lib()
+
+
+def _check(status: int, where: str):
+    if status != SDKV_OK:
+        raise SdkvError(status, where)
+
+
+# ---------------------------------------------------------------------------
+# torch marshalling helpers
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return SDKV_BF16
+    if t.dtype == torch.float32:
+        return SDKV_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t, name):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+class Workspace:
+    """A reusable device workspace (a uint8 torch tensor that grows on demand)."""
+
+    def __init__(self, device=None):
+        self.buf = None
+        self.device = device
+
+    def get(self, nbytes: int):
+        torch = _torch()
+        nbytes = max(int(nbytes), 256)
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device or "cuda")
+        return self.buf
+
+
+def _ws(workspace, nbytes):
+    if workspace is None:
+        workspace = Workspace()
+    buf = workspace.get(nbytes)
+    return buf.data_ptr(), buf.numel()
+
+
+# ---------------------------------------------------------------------------
+# Entry points
+# ---------------------------------------------------------------------------
+def selected_count(T: int, top_num: int, top_den: int) -> int:
+    return int(_lib().sdkv_selected_count(T, top_num, top_den))
+
+
+def sdkv_encode(x, dictionary, K: int, *, codes=None, coef_f32=None, resid_norm=None,
+                low_plane=None, klow: int = 0, workspace: Optional[Workspace] = None,
+                stream=None):
+    """Greedy-pursuit codes of the rows of x [n, d] over `dictionary`
+    [n_atoms, d] (bf16 or fp32 GPU tensors). Output tensors are allocated
+    when not given: codes int32 [n, K]; pass coef_f32=True / resid_norm=True /
+    low_plane=True (with klow) to request the optional outputs."""
+    torch = _torch()
+    n, d = x.shape
+    dev = x.device
+    if codes is None:
+        codes = torch.empty((n, K), dtype=torch.int32, device=dev)
+    if coef_f32 is True:
+        coef_f32 = torch.empty((n, K), dtype=torch.float32, device=dev)
+    if resid_norm is True:
+        resid_norm = torch.empty((n,), dtype=torch.float32, device=dev)
+    if low_plane is True:
+        low_plane = torch.empty((n, klow), dtype=torch.int32, device=dev)
+    a = EncodeArgs(x=_dev(x, "x"), x_dtype=_dtype_code(x), dict=_dev(dictionary, "dictionary"),
+                   dict_dtype=_dtype_code(dictionary), n=n, d=d, n_atoms=dictionary.shape[0],
+                   K=K, codes=_dev(codes, "codes"),
+                   coef_f32=_dev(coef_f32 if coef_f32 is not False else None, "coef_f32"),
+                   resid_norm=_dev(resid_norm if resid_norm is not False else None, "resid_norm"),
+                   low_plane=_dev(low_plane if low_plane is not False else None, "low_plane"),
+                   klow=klow)
+    nb = c_size_t(0)
+    _check(_lib().sdkv_encode_workspace(ctypes.byref(a), ctypes.byref(nb)), "sdkv_encode_workspace")
+    wp, wn = _ws(workspace, nb.value)
+    _check(_lib().sdkv_encode(ctypes.byref(a), ctypes.c_void_p(wp), wn, _stream(stream)),
+           "sdkv_encode")
+    res = {"codes": codes}
+    if coef_f32 is not None and coef_f32 is not False:
+        res["coef_f32"] = coef_f32
+    if resid_norm is not None and resid_norm is not False:
+        res["resid_norm"] = resid_norm
+    if low_plane is not None and low_plane is not False:
+        res["low_plane"] = low_plane
+    return res
+
+
+def attn_args(q, dk, dv, key_codes, val_codes, klow, khigh, top_num, top_den, scale, out,
+              key_low=None, u=None, s_low=None, sel=None, s_high=None, w=None) -> AttnArgs:
+    B, Hq, d = q.shape
+    _, Hkv, T, K = key_codes.shape
+    return AttnArgs(q=_dev(q, "q"), q_dtype=_dtype_code(q), dk=_dev(dk, "dk"), dv=_dev(dv, "dv"),
+                    dict_dtype=_dtype_code(dk), n_atoms=dk.shape[0], B=B, Hq=Hq, Hkv=Hkv, d=d,
+                    T=T, key_low=_dev(key_low, "key_low"), key_codes=_dev(key_codes, "key_codes"),
+                    val_codes=_dev(val_codes, "val_codes"), K=K, klow=klow, khigh=khigh,
+                    top_num=top_num, top_den=top_den, scale=scale, out=_dev(out, "out"),
+                    u=_dev(u, "u"), s_low=_dev(s_low, "s_low"), sel=_dev(sel, "sel"),
+                    s_high=_dev(s_high, "s_high"), w=_dev(w, "w"))
+
+
+def decode_attn_workspace_bytes(args: AttnArgs) -> int:
+    nb = c_size_t(0)
+    _check(_lib().sdkv_decode_attn_workspace(ctypes.byref(args), ctypes.byref(nb)),
+           "sdkv_decode_attn_workspace")
+    return nb.value
+
+
+def sdkv_decode_attn(q, dk, dv, key_codes, val_codes, *, klow: int, khigh: int,
+                     top_num: int = 1, top_den: int = 10, scale: Optional[float] = None,
+                     key_low=None, out=None, debug: bool = False,
+                     workspace: Optional[Workspace] = None, stream=None):
+    """Hierarchical coded decode attention. q [B,Hq,d] bf16; dk, dv
+    [n_atoms,d] bf16/fp32; key_codes, val_codes int32 [B,Hkv,T,K]; optional
+    key_low int32 [B,Hkv,T,klow]. Returns out fp32 [B,Hq,d], or with
+    debug=True a dict that also holds u, s_low, sel, s_high and w."""
+    torch = _torch()
+    B, Hq, d = q.shape
+    T = key_codes.shape[2]
+    dev = q.device
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    dbg = {}
+    if debug:
+        m = selected_count(T, top_num, top_den)
+        N = dk.shape[0]
+        dbg = dict(u=torch.empty((B, Hq, N), dtype=torch.float32, device=dev),
+                   s_low=torch.empty((B, Hq, T), dtype=torch.float32, device=dev),
+                   sel=torch.empty((B, Hq, m), dtype=torch.int32, device=dev),
+                   s_high=torch.empty((B, Hq, m), dtype=torch.float32, device=dev),
+                   w=torch.empty((B, Hq, N), dtype=torch.float32, device=dev))
+    a = attn_args(q, dk, dv, key_codes, val_codes, klow, khigh, top_num, top_den, scale, out,
+                  key_low=key_low, **dbg)
+    wp, wn = _ws(workspace, decode_attn_workspace_bytes(a))
+    _check(_lib().sdkv_decode_attn(ctypes.byref(a), ctypes.c_void_p(wp), wn, _stream(stream)),
+           "sdkv_decode_attn")
+    if debug:
+        dbg["out"] = out
+        return dbg
+    return out
+
+
+def sdkv_select_topk(scores, k: int, *, idx_out=None, thr_out=None,
+                     workspace: Optional[Workspace] = None, stream=None):
+    """Indices (int32, ascending) of the k largest entries of each row of the
+    fp32 GPU tensor `scores` [rows, n] (rows may be strided: row stride =
+    scores.stride(0)); ties to the lower index. Returns (idx, thr)."""
+    torch = _torch()
+    if scores.dim() == 1:
+        scores = scores[None]
+    rows, n = scores.shape
+    if scores.dtype != torch.float32 or not scores.is_cuda or scores.stride(1) != 1:
+        raise ValueError("scores must be a GPU float32 tensor with unit column stride")
+    ld = scores.stride(0) if rows > 1 else n
+    if idx_out is None:
+        idx_out = torch.empty((rows, k), dtype=torch.int32, device=scores.device)
+    if thr_out is True:
+        thr_out = torch.empty((rows,), dtype=torch.float32, device=scores.device)
+    nb = c_size_t(0)
+    _check(_lib().sdkv_select_topk_workspace(rows, n, k, ctypes.byref(nb)),
+           "sdkv_select_topk_workspace")
+    wp, wn = _ws(workspace, nb.value)
+    thr_ptr = thr_out.data_ptr() if thr_out is not None and thr_out is not False else None
+    _check(_lib().sdkv_select_topk(ctypes.c_void_p(scores.data_ptr()), rows, n, ld, k,
+                                   ctypes.c_void_p(_dev(idx_out, "idx_out")),
+                                   ctypes.c_void_p(thr_ptr), ctypes.c_void_p(wp), wn,
+                                   _stream(stream)), "sdkv_select_topk")
+    return idx_out, (thr_out if thr_ptr else None)
+
+
+__all__ = ["sdkv_encode", "sdkv_decode_attn", "sdkv_select_topk", "selected_count",
+           "Workspace", "SdkvError", "lib", "LIB_PATH", "HEADER", "EncodeArgs", "AttnArgs",
+           "attn_args", "decode_attn_workspace_bytes"]

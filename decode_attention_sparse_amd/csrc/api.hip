@@ -1,0 +1,175 @@
+// Exported C ABI of libsdkv (declared in include/sdkv.h): argument
+// validation, workspace sizing and dispatch. Validation is complete before
+// anything is enqueued, so an error leaves every output untouched. No
+// exception escapes: every entry point is wrapped in a catch-all.
+#include <math.h>
+
+#include <algorithm>
+
+#include "sdkv_internal.h"
+
+using namespace sdkv;
+
+namespace sdkv {
+
+sdkv_status coresident_blocks(const void* kernel, int threads, size_t dyn_lds, int* out) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SDKV_ERR_DEVICE;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return SDKV_ERR_DEVICE;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, dyn_lds) != hipSuccess)
+    return SDKV_ERR_DEVICE;
+  *out = cus * per_cu;
+  return SDKV_OK;
+}
+
+}  // namespace sdkv
+
+static bool valid_dtype(int32_t t) { return t == SDKV_BF16 || t == SDKV_F32; }
+
+static sdkv_status check_encode(const sdkv_encode_args* a) {
+  if (!a || !a->x || !a->dict || !a->codes) return SDKV_ERR_NULL;
+  if (!valid_dtype(a->x_dtype) || !valid_dtype(a->dict_dtype)) return SDKV_ERR_DTYPE;
+  if (a->n < 1 || (a->d != 64 && a->d != 128)) return SDKV_ERR_SHAPE;
+  if (a->n_atoms < 1 || a->n_atoms > 65536) return SDKV_ERR_SHAPE;
+  if (a->K < 1 || a->K > 32) return SDKV_ERR_SHAPE;
+  if (a->low_plane && (a->klow < 1 || a->klow > a->K)) return SDKV_ERR_SHAPE;
+  if (a->n > ((int64_t)1 << 40)) return SDKV_ERR_UNSUPPORTED;
+  return SDKV_OK;
+}
+
+static sdkv_status check_attn(const sdkv_attn_args* a) {
+  if (!a || !a->q || !a->dk || !a->dv || !a->key_codes || !a->val_codes || !a->out)
+    return SDKV_ERR_NULL;
+  if (!valid_dtype(a->q_dtype) || !valid_dtype(a->dict_dtype)) return SDKV_ERR_DTYPE;
+  if (a->B < 1 || a->Hq < 1 || a->Hkv < 1 || a->Hq % a->Hkv != 0) return SDKV_ERR_SHAPE;
+  if (a->d != 64 && a->d != 128) return SDKV_ERR_SHAPE;
+  if (a->T < 1 || a->T > 0x7FFFFFFF) return SDKV_ERR_SHAPE;
+  if (a->n_atoms < 1 || a->n_atoms > 65536) return SDKV_ERR_SHAPE;
+  if (a->K < 1 || a->K > 32) return SDKV_ERR_SHAPE;
+  if (a->klow < 1 || a->klow > a->khigh || a->khigh > a->K) return SDKV_ERR_SHAPE;
+  if (a->top_num < 1 || a->top_den < a->top_num || a->top_den > 0x7FFFFFFF) return SDKV_ERR_SHAPE;
+  if (!isfinite(a->scale)) return SDKV_ERR_SHAPE;
+  if (a->q_dtype != SDKV_BF16) return SDKV_ERR_UNSUPPORTED;
+  if (a->n_atoms > kMaxAtomsDecode) return SDKV_ERR_UNSUPPORTED;
+  if ((int64_t)a->B * a->Hq > 0x7FFFFFFF / 64) return SDKV_ERR_UNSUPPORTED;
+  return SDKV_OK;
+}
+
+extern "C" {
+
+int32_t sdkv_abi_version(void) { return SDKV_ABI_VERSION; }
+
+const char* sdkv_status_str(sdkv_status s) {
+  switch (s) {
+    case SDKV_OK: return "ok";
+    case SDKV_ERR_NULL: return "required pointer is NULL";
+    case SDKV_ERR_SHAPE: return "size or count out of range";
+    case SDKV_ERR_DTYPE: return "unknown dtype code";
+    case SDKV_ERR_UNSUPPORTED: return "valid arguments outside the supported range";
+    case SDKV_ERR_WORKSPACE: return "workspace too small";
+    case SDKV_ERR_DEVICE: return "HIP runtime or launch error";
+    default: return "unknown status";
+  }
+}
+
+int64_t sdkv_selected_count(int64_t T, int64_t top_num, int64_t top_den) {
+  if (T < 1 || top_num < 1 || top_den < top_num || T > 0x7FFFFFFF || top_den > 0x7FFFFFFF) return 0;
+  const int64_t m = (T * top_num + top_den - 1) / top_den;
+  return std::max<int64_t>(1, std::min<int64_t>(T, m));
+}
+
+sdkv_status sdkv_encode_workspace(const sdkv_encode_args* args, size_t* bytes) {
+  try {
+    if (!bytes) return SDKV_ERR_NULL;
+    sdkv_status s = check_encode(args);
+    if (s != SDKV_OK) return s;
+    EncodePlan p;
+    s = plan_encode(args, &p);
+    if (s != SDKV_OK) return s;
+    *bytes = p.total;
+    return SDKV_OK;
+  } catch (...) {
+    return SDKV_ERR_DEVICE;
+  }
+}
+
+sdkv_status sdkv_encode(const sdkv_encode_args* args, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    sdkv_status s = check_encode(args);
+    if (s != SDKV_OK) return s;
+    EncodePlan p;
+    s = plan_encode(args, &p);
+    if (s != SDKV_OK) return s;
+    if (p.total > 0 && !ws) return SDKV_ERR_NULL;
+    if (ws_bytes < p.total) return SDKV_ERR_WORKSPACE;
+    return launch_encode(args, p, ws, (hipStream_t)stream);
+  } catch (...) {
+    return SDKV_ERR_DEVICE;
+  }
+}
+
+sdkv_status sdkv_decode_attn_workspace(const sdkv_attn_args* args, size_t* bytes) {
+  try {
+    if (!bytes) return SDKV_ERR_NULL;
+    sdkv_status s = check_attn(args);
+    if (s != SDKV_OK) return s;
+    DecodePlan p;
+    s = plan_decode(args, &p);
+    if (s != SDKV_OK) return s;
+    *bytes = p.total;
+    return SDKV_OK;
+  } catch (...) {
+    return SDKV_ERR_DEVICE;
+  }
+}
+
+sdkv_status sdkv_decode_attn(const sdkv_attn_args* args, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    sdkv_status s = check_attn(args);
+    if (s != SDKV_OK) return s;
+    DecodePlan p;
+    s = plan_decode(args, &p);
+    if (s != SDKV_OK) return s;
+    if (!ws) return SDKV_ERR_NULL;
+    if (ws_bytes < p.total) return SDKV_ERR_WORKSPACE;
+    return launch_decode(args, p, ws, (hipStream_t)stream);
+  } catch (...) {
+    return SDKV_ERR_DEVICE;
+  }
+}
+
+sdkv_status sdkv_select_topk_workspace(int64_t rows, int64_t n, int64_t k, size_t* bytes) {
+  try {
+    if (!bytes) return SDKV_ERR_NULL;
+    if (rows < 1 || n < 1 || k < 1 || k > n) return SDKV_ERR_SHAPE;
+    if (n > ((int64_t)1 << 23) || rows > 0x7FFFFFFF) return SDKV_ERR_UNSUPPORTED;
+    TopkPlan p;
+    sdkv_status s = plan_topk(rows, n, k, &p);
+    if (s != SDKV_OK) return s;
+    *bytes = p.total;
+    return SDKV_OK;
+  } catch (...) {
+    return SDKV_ERR_DEVICE;
+  }
+}
+
+sdkv_status sdkv_select_topk(const float* scores, int64_t rows, int64_t n, int64_t ld, int64_t k,
+                             int32_t* idx_out, float* thr_out, void* ws, size_t ws_bytes,
+                             void* stream) {
+  try {
+    if (!scores || !idx_out) return SDKV_ERR_NULL;
+    if (rows < 1 || n < 1 || k < 1 || k > n || ld < n) return SDKV_ERR_SHAPE;
+    if (n > ((int64_t)1 << 23) || rows > 0x7FFFFFFF) return SDKV_ERR_UNSUPPORTED;
+    TopkPlan p;
+    sdkv_status s = plan_topk(rows, n, k, &p);
+    if (s != SDKV_OK) return s;
+    if (!ws) return SDKV_ERR_NULL;
+    if (ws_bytes < p.total) return SDKV_ERR_WORKSPACE;
+    return launch_topk(scores, ld, idx_out, thr_out, p, ws, (hipStream_t)stream);
+  } catch (...) {
+    return SDKV_ERR_DEVICE;
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,172 @@
+// Device-side helpers shared by the libsdkv kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdkv {
+
+// --- MFMA operand types (v_mfma_f32_16x16x32_{bf16,f16}) -------------------
+// Lane layout (wave64) of the 16x16x32 shapes, as used throughout:
+//   A (16 x 32): lane l holds row l%16, k = 8*(l/16) .. 8*(l/16)+7
+//   B (32 x 16): lane l holds col l%16, k = 8*(l/16) .. 8*(l/16)+7
+//   C (16 x 16): lane l holds rows 4*(l/16)+i (i < 4), col l%16
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// --- number formats ---------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+// float -> bf16 bits, round to nearest even (finite inputs)
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+  _Float16 h = (_Float16)f;  // v_cvt_f16_f32, round to nearest even
+  return (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+// code word: index in bits 0-15, binary16 coefficient in bits 16-31
+__device__ __forceinline__ uint32_t code_idx(uint32_t w) { return w & 0xFFFFu; }
+__device__ __forceinline__ float code_coef(uint32_t w) { return f16_bits_to_f32(w >> 16); }
+
+// Order-preserving map float -> uint32 (larger float -> larger key). Finite
+// scores never map to 0, which marks "no token" in the select kernels.
+__device__ __forceinline__ uint32_t float_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  u = (u == 0x80000000u) ? 0u : u;  // -0 and +0 compare equal
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// --- wave / block primitives ------------------------------------------------
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+// sum within aligned groups of G lanes (G = 16 or 32)
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int o = G / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Exclusive scan over the block (NW waves). `tmp` holds >= NW words of LDS.
+// Returns the exclusive prefix; *total receives the block total.
+template <int NW>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* tmp, uint32_t* total) {
+  const uint32_t inc = wave_incl_scan(v);
+  if (lane_id() == 63) tmp[wave_id()] = inc;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const uint32_t s = tmp[i];
+    base += (i < wave_id()) ? s : 0u;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + inc - v;
+}
+template <int NW>
+__device__ __forceinline__ float block_max(float v, float* tmp) {
+  v = wave_max(v);
+  if (lane_id() == 0) tmp[wave_id()] = v;
+  __syncthreads();
+  float r = tmp[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) r = fmaxf(r, tmp[i]);
+  __syncthreads();
+  return r;
+}
+template <int NW>
+__device__ __forceinline__ float block_sum(float v, float* tmp) {
+  v = wave_sum(v);
+  if (lane_id() == 0) tmp[wave_id()] = v;
+  __syncthreads();
+  float r = 0.f;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) r += tmp[i];
+  __syncthreads();
+  return r;
+}
+
+// --- cross-workgroup barrier among the `n` workgroups sharing `ctr` -----------
+// Only used in cooperative launches (all workgroups co-resident). The spin is
+// bounded: after ~2^24 polls the workgroup gives up, records the failure in
+// *err and continues, so a wave can never wait forever.
+__device__ __forceinline__ void group_barrier(uint32_t* ctr, uint32_t target, uint32_t* err) {
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t spins = 0;
+    while (__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++spins > (1u << 24)) {
+        __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  __threadfence();
+}
+
+__device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Workgroup -> logical tile mapping that keeps consecutive logical tiles on
+// one XCD: the dispatcher hands workgroup ids to the 8 XCDs round-robin, so
+// id i runs on XCD i % 8. When nb is a multiple of 8, XCD x gets the
+// contiguous logical range [x*nb/8, (x+1)*nb/8). A bijection either way.
+__device__ __forceinline__ int xcd_tile(int bid, int nb) {
+  return (nb % 8 == 0) ? (bid % 8) * (nb / 8) + bid / 8 : bid;
+}
+
+}  // namespace sdkv

@@ -1,0 +1,75 @@
+// Host-side plans and launcher declarations inside libsdkv (not exported).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "../../include/sdkv.h"
+
+namespace sdkv {
+
+// Planning assumes an MI355X: 256 compute units. The same plan (and so the
+// same workspace size) is used on any device; the launch code splits a
+// cooperative grid into smaller row batches if the device holds fewer
+// co-resident workgroups.
+constexpr int kPlanCUs = 256;
+constexpr int kRowThreads = 512;
+constexpr int kMaxSPT = 64;                                // keys per thread
+constexpr int64_t kMaxChunk = (int64_t)kRowThreads * kMaxSPT;  // 32768 tokens
+constexpr int kMaxRowP = 64;   // workgroups per decode row
+constexpr int kMaxAtomsDecode = 32768;
+constexpr int kWdvSub = 256;   // atoms per MFMA sub-chunk in the W.Dv kernel
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct DecodePlan {
+  int64_t rows = 0;      // B * Hq
+  int64_t m = 0;         // selected tokens per row
+  int P = 1;             // workgroups per row
+  int64_t chunk = 0;     // tokens per workgroup
+  int spt = 0;           // keys per thread (template instance)
+  int lpt = 16;          // lanes per token in the rescore/value loops
+  int nrt = 0;           // 16-row tiles in the W.Dv kernel
+  int nsub = 1;          // 256-atom sub-chunks per W.Dv workgroup
+  int nchunks = 0;       // atom chunks in the W.Dv kernel
+  // workspace byte offsets
+  size_t off_u = 0, off_sel = 0, off_shigh = 0, off_wpart = 0, off_stats = 0;
+  size_t off_zero = 0, zero_bytes = 0;  // [ghist | xchg | bar | err], cleared per call
+  size_t off_ghist = 0, off_xchg = 0, off_bar = 0, off_err = 0, off_opart = 0;
+  size_t total = 0;
+};
+
+sdkv_status plan_decode(const sdkv_attn_args* a, DecodePlan* p);
+sdkv_status launch_decode(const sdkv_attn_args* a, const DecodePlan& p, void* ws,
+                          hipStream_t stream);
+
+struct TopkPlan {
+  int64_t rows = 0, n = 0, k = 0;
+  int P = 1;
+  int64_t chunk = 0;
+  int spt = 0;
+  size_t off_ghist = 0, off_xchg = 0, off_bar = 0, off_err = 0, zero_bytes = 0;
+  size_t total = 0;
+};
+sdkv_status plan_topk(int64_t rows, int64_t n, int64_t k, TopkPlan* p);
+sdkv_status launch_topk(const float* scores, int64_t ld, int32_t* idx, float* thr,
+                        const TopkPlan& p, void* ws, hipStream_t stream);
+
+struct EncodePlan {
+  int64_t n = 0;
+  int npad = 0;          // atoms padded to the sweep tile
+  int rows_per_wg = 0;
+  int64_t nwg = 0;
+  size_t off_dh = 0, off_r = 0, off_rh = 0, off_scale = 0;
+  size_t total = 0;
+};
+sdkv_status plan_encode(const sdkv_encode_args* a, EncodePlan* p);
+sdkv_status launch_encode(const sdkv_encode_args* a, const EncodePlan& p, void* ws,
+                          hipStream_t stream);
+
+// Largest number of co-resident workgroups for a kernel on the current device.
+sdkv_status coresident_blocks(const void* kernel, int threads, size_t dyn_lds, int* out);
+
+}  // namespace sdkv

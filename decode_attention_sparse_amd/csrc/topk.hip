@@ -1,0 +1,145 @@
+// Stand-alone exact top-k select over fp32 score rows (the "top 10%" step of
+// the review page's Summary of "LLM Inference in a Flash!", exposed alone).
+// Output: indices of the k largest scores per row, ties to the lower index,
+// ascending; optionally the k-th largest score.
+#include "select_core.h"
+#include "sdkv_internal.h"
+
+namespace sdkv {
+
+constexpr int kTopkMaxP = 256;
+
+struct TopkArgs {
+  const float* s;
+  int64_t ld, n, k, chunk;
+  int P, row0, nrows;
+  int32_t* idx;
+  float* thr;
+  uint32_t* ghist;  // [rows, 3, 2048]
+  uint32_t* xchg;   // [rows, P, 2]
+  uint32_t* bar;    // [rows]
+  uint32_t* err;
+};
+
+__global__ __launch_bounds__(256) void k_fill_zero(uint32_t* p, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0u;
+}
+
+template <int SPT>
+__global__ __launch_bounds__(SB) void k_topk(TopkArgs a) {
+  __shared__ SelShared sh;
+  const int tid = threadIdx.x;
+  const int L = xcd_tile(blockIdx.x, a.nrows * a.P);
+  const int p = L % a.P;
+  const int64_t row = a.row0 + L / a.P;
+  const int64_t t0 = (int64_t)p * a.chunk;
+  const int64_t t1 = min(a.n, t0 + a.chunk);
+  const float* src = a.s + row * a.ld;
+  uint32_t key[SPT];
+#pragma unroll
+  for (int j = 0; j < SPT; ++j) {
+    const int64_t t = t0 + (int64_t)j * SB + tid;
+    key[j] = (t < t1) ? float_key(src[t]) : 0u;
+  }
+  SelGroup grp;
+  grp.P = a.P;
+  grp.p = p;
+  grp.ghist = a.ghist + row * 3 * 2048;
+  grp.xchg = a.xchg + row * a.P * 2;
+  grp.bar = a.bar + row;
+  grp.err = a.err;
+  uint32_t offset, count, tau;
+  const uint64_t sel = radix_select<SPT>(key, (uint32_t)a.k, sh, grp, &offset, &count, &tau);
+  int32_t* out = a.idx + row * a.k;
+  ordered_ranks<SPT>(sel, sh, [&](int j, uint32_t r) {
+    const int64_t pos = (int64_t)offset + r;
+    if (pos < a.k) out[pos] = (int32_t)(t0 + (int64_t)j * SB + tid);
+  });
+  if (a.thr && p == 0 && tid == 0) a.thr[row] = key_float(tau);
+}
+
+static int topk_spt(int64_t chunk) {
+  const int64_t need = (chunk + SB - 1) / SB;
+  for (int s : {4, 16, 64})
+    if (need <= s) return s;
+  return 0;
+}
+
+sdkv_status plan_topk(int64_t rows, int64_t n, int64_t k, TopkPlan* p) {
+  TopkPlan q;
+  q.rows = rows;
+  q.n = n;
+  q.k = k;
+  const int64_t p_min = (n + kMaxChunk - 1) / kMaxChunk;
+  const int64_t p_par = std::max<int64_t>(1, kPlanCUs / std::max<int64_t>(1, rows));
+  const int64_t p_cap = std::max<int64_t>(1, (n + 2047) / 2048);
+  const int64_t P = std::max(p_min, std::min(p_par, p_cap));
+  if (P > kTopkMaxP) return SDKV_ERR_UNSUPPORTED;
+  q.P = (int)P;
+  q.chunk = (n + P - 1) / P;
+  q.spt = topk_spt(q.chunk);
+  if (q.spt == 0) return SDKV_ERR_UNSUPPORTED;
+  size_t off = 0;
+  q.off_ghist = off;  off += (q.P > 1) ? (size_t)rows * 3 * 2048 * 4 : 0;
+  q.off_xchg = off;   off += (size_t)rows * q.P * 2 * 4;
+  q.off_bar = off;    off += (size_t)rows * 4;
+  q.off_err = off;    off += 4;
+  q.zero_bytes = align_up(off, 256);
+  q.total = q.zero_bytes;
+  *p = q;
+  return SDKV_OK;
+}
+
+static const void* pick_topk_kernel(int spt) {
+  if (spt == 4) return (const void*)&k_topk<4>;
+  if (spt == 16) return (const void*)&k_topk<16>;
+  if (spt == 64) return (const void*)&k_topk<64>;
+  return nullptr;
+}
+
+sdkv_status launch_topk(const float* scores, int64_t ld, int32_t* idx, float* thr,
+                        const TopkPlan& p, void* ws, hipStream_t stream) {
+  char* base = (char*)ws;
+  const int64_t zw = (int64_t)(p.zero_bytes / 4);
+  hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)std::min<int64_t>(1024, (zw + 255) / 256)),
+                     dim3(256), 0, stream, (uint32_t*)base, zw);
+  if (hipGetLastError() != hipSuccess) return SDKV_ERR_DEVICE;
+  TopkArgs a;
+  a.s = scores;
+  a.ld = ld;
+  a.n = p.n;
+  a.k = p.k;
+  a.chunk = p.chunk;
+  a.P = p.P;
+  a.idx = idx;
+  a.thr = thr;
+  a.ghist = (uint32_t*)(base + p.off_ghist);
+  a.xchg = (uint32_t*)(base + p.off_xchg);
+  a.bar = (uint32_t*)(base + p.off_bar);
+  a.err = (uint32_t*)(base + p.off_err);
+  const void* kfn = pick_topk_kernel(p.spt);
+  if (!kfn) return SDKV_ERR_UNSUPPORTED;
+  int64_t batch = p.rows;
+  if (p.P > 1) {
+    int cap = 0;
+    sdkv_status st = coresident_blocks(kfn, SB, 0, &cap);
+    if (st != SDKV_OK) return st;
+    batch = std::min<int64_t>(p.rows, cap / p.P);
+    if (batch < 1) return SDKV_ERR_UNSUPPORTED;
+  }
+  // rows per launch also bounded so the grid size fits an int
+  batch = std::min<int64_t>(batch, (int64_t)1 << 20);
+  for (int64_t r0 = 0; r0 < p.rows; r0 += batch) {
+    a.row0 = (int)r0;
+    a.nrows = (int)std::min<int64_t>(batch, p.rows - r0);
+    void* args[] = {&a};
+    const dim3 grid((unsigned)(a.nrows * p.P)), block(SB);
+    hipError_t e = (p.P > 1) ? hipLaunchCooperativeKernel(kfn, grid, block, args, 0, stream)
+                             : hipLaunchKernel(kfn, grid, block, args, 0, stream);
+    if (e != hipSuccess) return SDKV_ERR_DEVICE;
+  }
+  return SDKV_OK;
+}
+
+}  // namespace sdkv

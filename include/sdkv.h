@@ -1,0 +1,165 @@
+/*
+ * sdkv.h -- C ABI of libsdkv: a dictionary-coded KV cache for AMD MI355X
+ * (gfx950): greedy-pursuit encode and query-aware hierarchical decode
+ * attention over coded keys and values.
+ *
+ * Method: "LLM Inference in a Flash!" (abstract page; review page, Summary,
+ * Strengths and FAQ). Each key or value vector is stored as K (atom index,
+ * coefficient) pairs over a static per-layer, per-stream dictionary of
+ * unit-norm atoms (32,768 atoms, K = 16 on the pages). Decode scores every
+ * cached token with its first Klow atoms, keeps the top fraction of tokens
+ * and rescores those with Khigh atoms.
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers on the current HIP device,
+ *    row-major and densely packed in the layout stated per argument. The
+ *    caller owns every buffer, including the workspace; the library never
+ *    allocates, frees or synchronises.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Every call only enqueues work on that stream and returns at once.
+ *  - Code word: one uint32 per (index, coefficient) pair; bits 0-15 hold the
+ *    atom index (uint16), bits 16-31 the IEEE binary16 coefficient.
+ *  - Validation happens before anything is enqueued; on any error nothing
+ *    is written. Kernel launch failures are reported as SDKV_ERR_DEVICE
+ *    (faults inside an already-enqueued kernel surface at the caller's next
+ *    synchronisation, as for any HIP kernel). No C++ exception crosses the
+ *    ABI. The library keeps no mutable global state (calls are reentrant);
+ *    two calls that share a workspace must not overlap in time.
+ *  - Inputs must be finite. Code indices must be < n_atoms; other indices
+ *    give unspecified (but in-bounds) results.
+ */
+#ifndef SDKV_H
+#define SDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define SDKV_API __attribute__((visibility("default")))
+#else
+#define SDKV_API
+#endif
+
+#define SDKV_ABI_VERSION 1
+
+typedef int32_t sdkv_status;
+#define SDKV_OK 0
+#define SDKV_ERR_NULL 1        /* a required pointer is NULL               */
+#define SDKV_ERR_SHAPE 2       /* a size or count is out of range          */
+#define SDKV_ERR_DTYPE 3       /* unknown dtype code                       */
+#define SDKV_ERR_UNSUPPORTED 4 /* valid, but outside what the kernels take */
+#define SDKV_ERR_WORKSPACE 5   /* workspace smaller than the query result  */
+#define SDKV_ERR_DEVICE 6      /* a HIP runtime call or launch failed      */
+
+/* dtype codes */
+#define SDKV_BF16 0
+#define SDKV_F32 1
+
+/* ------------------------------------------------------------------------
+ * Encode: greedy projection pursuit (review page, Summary and Strengths: a
+ * greedy pursuit that projects onto one atom per step and, unlike OMP, never
+ * re-solves a least-squares problem). For every input vector x:
+ *     r = x;  for k < K:  a_k = argmax_a |<r, d_a>|  (lowest a on ties),
+ *                          g_k = <r, d_{a_k}>,  r -= g_k d_{a_k}.
+ * Atoms are expected to have unit norm (the coefficient is not divided by
+ * |d|^2). The argmax is found with an fp16 matrix-core screen of all atoms
+ * followed by an exact fp32 re-check of the best candidates; g_k and the
+ * residual are fp32.
+ * ---------------------------------------------------------------------- */
+typedef struct sdkv_encode_args {
+  const void* x;        /* [n, d] vectors, dtype x_dtype (SDKV_BF16/F32)  */
+  int32_t x_dtype;
+  const void* dict;     /* [n_atoms, d] atoms, dtype dict_dtype           */
+  int32_t dict_dtype;
+  int64_t n;            /* number of vectors, >= 1                        */
+  int32_t d;            /* 64 or 128                                      */
+  int32_t n_atoms;      /* 1 .. 65536                                     */
+  int32_t K;            /* code length, 1 .. 32                           */
+  uint32_t* codes;      /* OUT [n, K] code words, pursuit order; required */
+  float* coef_f32;      /* OUT [n, K] unrounded g_k, or NULL              */
+  float* resid_norm;    /* OUT [n] |r_K|_2, or NULL                       */
+  uint32_t* low_plane;  /* OUT [n, klow] first klow code words, or NULL   */
+  int32_t klow;         /* 1 .. K when low_plane != NULL                  */
+} sdkv_encode_args;
+
+/* Bytes of device workspace sdkv_encode needs for these arguments. */
+SDKV_API sdkv_status sdkv_encode_workspace(const sdkv_encode_args* args, size_t* bytes);
+SDKV_API sdkv_status sdkv_encode(const sdkv_encode_args* args, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/* ------------------------------------------------------------------------
+ * Decode attention for one layer and one decode step (review page, Summary:
+ * every token gets a cheap score from its first Klow = 3 atoms and only the
+ * best tenth is rescored with Khigh = 16; FAQ: three atoms suffice to score
+ * most tokens; abstract page: keys and values are linear combinations of
+ * static dictionary vectors). For batch b and query head h (KV head
+ * g = h / (Hq/Hkv)):
+ *   u       = scale * Dk q_h                                   [n_atoms]
+ *   s_low_t = sum_{j<klow}  kappa_tj u[i_tj]                   all t < T
+ *   S       = the m = ceil(T*top_num/top_den) tokens with largest s_low,
+ *             ties to the lower token index
+ *   s_high_t= sum_{j<khigh} kappa_tj u[i_tj]                   t in S
+ *   p       = softmax_S(s_high);  w[a] = sum_{t in S} p_t sum_{j<K}
+ *             kappa^v_tj [i^v_tj == a];  out_h = Dv^T w
+ * Unselected tokens do not enter the softmax.
+ * ---------------------------------------------------------------------- */
+typedef struct sdkv_attn_args {
+  const void* q;        /* [B, Hq, d] queries; q_dtype must be SDKV_BF16  */
+  int32_t q_dtype;
+  const void* dk;       /* [n_atoms, d] key dictionary, dict_dtype        */
+  const void* dv;       /* [n_atoms, d] value dictionary, dict_dtype      */
+  int32_t dict_dtype;
+  int32_t n_atoms;      /* 1 .. 32768                                     */
+  int32_t B, Hq, Hkv;   /* >= 1, Hq % Hkv == 0                            */
+  int32_t d;            /* 64 or 128                                      */
+  int64_t T;            /* cached tokens, >= 1                            */
+  const uint32_t* key_low;   /* [B, Hkv, T, klow] first klow key words, or
+                                NULL to read them from key_codes          */
+  const uint32_t* key_codes; /* [B, Hkv, T, K] key code words             */
+  const uint32_t* val_codes; /* [B, Hkv, T, K] value code words           */
+  int32_t K;            /* 1 .. 32                                        */
+  int32_t klow, khigh;  /* 1 <= klow <= khigh <= K                        */
+  int64_t top_num, top_den; /* selected fraction, 0 < top_num <= top_den  */
+  float scale;          /* softmax scale, finite                          */
+  float* out;           /* OUT [B, Hq, d] fp32; required                  */
+  /* Optional per-stage outputs (NULL to skip):                           */
+  float* u;             /* OUT [B, Hq, n_atoms] scale * Dk q              */
+  float* s_low;         /* OUT [B, Hq, T]                                 */
+  int32_t* sel;         /* OUT [B, Hq, m] selected tokens, ascending      */
+  float* s_high;        /* OUT [B, Hq, m] aligned with sel                */
+  float* w;             /* OUT [B, Hq, n_atoms] normalised value weights  */
+} sdkv_attn_args;
+
+/* m = ceil(T * top_num / top_den), clamped to [1, T]; 0 on bad input. */
+SDKV_API int64_t sdkv_selected_count(int64_t T, int64_t top_num, int64_t top_den);
+
+SDKV_API sdkv_status sdkv_decode_attn_workspace(const sdkv_attn_args* args, size_t* bytes);
+SDKV_API sdkv_status sdkv_decode_attn(const sdkv_attn_args* args, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Top-k select: the "top 10%" step of the decode path on its own (review
+ * page, Summary). For each of `rows` rows of `n` fp32 scores (row stride
+ * `ld` elements, ld >= n), writes the indices of the k largest scores,
+ * ties to the lower index, in ascending index order: idx_out [rows, k].
+ * thr_out (nullable) [rows] receives the k-th largest score.
+ * Limits: 1 <= k <= n <= 2^23.
+ * ---------------------------------------------------------------------- */
+SDKV_API sdkv_status sdkv_select_topk_workspace(int64_t rows, int64_t n, int64_t k,
+                                       size_t* bytes);
+SDKV_API sdkv_status sdkv_select_topk(const float* scores, int64_t rows, int64_t n,
+                             int64_t ld, int64_t k, int32_t* idx_out,
+                             float* thr_out, void* ws, size_t ws_bytes,
+                             void* stream);
+
+SDKV_API const char* sdkv_status_str(sdkv_status s);
+SDKV_API int32_t sdkv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SDKV_H */

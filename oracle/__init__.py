@@ -6,18 +6,17 @@ smoke check and the benchmark's CPU-baseline leg may import or call it; the
 library itself never does and shares no code with it.
 
 Sources (pages of "LLM Inference in a Flash!"):
-  * review page, Summary: each key/value vector is a sparse combination of
-    K=16 atoms of a per-layer, per-stream 32,768-atom dictionary, found by a
-    projection-based greedy pursuit that replaces OMP so no least-squares
-    refit is done; decode scores every token with Klow=3 atoms and refines
-    the top 10% with Khigh=16.
-  * review page, Strengths ("Hardware-aware replacement of OMP"): greedy,
-    refit-free pursuit.
-  * review page, FAQ ("What is the 15x KV cache compression"): vectors are
-    stored as indices plus coefficients of 16 atoms; 3 atoms score most
+  * review page, Summary: every key and value vector is kept as K=16 atoms
+    of a 32,768-atom dictionary that is fixed per layer and per stream; the
+    atoms are chosen greedily, one projection per step, without the
+    least-squares re-solve of OMP; at decode time a Klow=3 score ranks all
+    tokens and the best tenth is rescored with Khigh=16 atoms.
+  * review page, Strengths (on replacing OMP for the hardware): the pursuit
+    is greedy and never refits.
+  * review page, FAQ (on the 15x compression figure): a vector is stored as
+    16 atom indices plus coefficients; three atoms are enough to rank most
     tokens.
-  * abstract page: each KV vector is a linear combination of static
-    dictionary vectors.
+  * abstract page: keys and values are sums of fixed dictionary vectors.
 
 Every function here has a pin in tests/test_oracle_*.py (closed forms,
 invariants, brute force with exact rational arithmetic, hand-worked golden

@@ -42,8 +42,9 @@ def mp_encode(X: np.ndarray, D: np.ndarray, K: int, *, trace: bool = False,
               block: int = 512):
     """Greedy pursuit of each row of X over the atoms (rows) of D.
 
-    Review page, Summary and Strengths: a projection-based greedy pursuit
-    replaces OMP to avoid least-squares refits. Per vector x:
+    Review page, Summary and Strengths: a greedy pursuit projects out one
+    atom per step and, unlike OMP, never re-solves a least-squares problem.
+    Per vector x:
         r_0 = x
         for k = 0 .. K-1:
             c_a   = <r_k, d_a>           for every atom a
@@ -90,7 +91,7 @@ def mp_encode(X: np.ndarray, D: np.ndarray, K: int, *, trace: bool = False,
 
 
 # ---------------------------------------------------------------------------
-# Decode: query-aware hierarchical sparsity over coded keys and values
+# Decode: two-level (Klow then Khigh) scoring over coded keys and values
 # ---------------------------------------------------------------------------
 def selected_count(T: int, top_num: int, top_den: int) -> int:
     """m = ceil(T * num / den) in integer arithmetic, clamped to [1, T].
@@ -111,13 +112,13 @@ def select_topk(scores: np.ndarray, k: int) -> np.ndarray:
 
 
 def decode_attn(q, dk, dv, key_codes, val_codes, klow: int, khigh: int,
-                top_num: int, top_den: int, scale: float):
+                top_num: int, top_den: int, scale: float, sel=None):
     """Hierarchical coded decode attention for one layer.
 
-    Review page, Summary: query-aware hierarchical sparsity scores all tokens
-    at Klow atoms and refines the top 10% to Khigh. FAQ: 3 atoms score most
-    tokens. Abstract page: each key/value is a linear combination of static
-    dictionary vectors, so <q, k_t> = sum_j kappa_tj <q, d_{i_tj}>.
+    Review page, Summary: every token is scored from its first Klow atoms
+    and the best tenth is rescored with Khigh atoms. FAQ: three atoms are
+    enough to rank most tokens. Abstract page: keys and values are sums of
+    fixed dictionary atoms, so <q, k_t> = sum_j kappa_tj <q, d_{i_tj}>.
 
     Inputs: q [B,Hq,d]; dk, dv [N,d]; key_codes, val_codes uint32
     [B,Hkv,T,K]. For each batch b and query head h (KV head g = h // G,
@@ -133,6 +134,11 @@ def decode_attn(q, dk, dv, key_codes, val_codes, klow: int, khigh: int,
     Readings: the softmax runs over S only (unselected tokens are dropped);
     selection is per query head; the key code's first klow slots are the
     "low" atoms; values use all K slots; the scale multiplies the scores.
+
+    `sel` (optional int [B,Hq,m]) replaces the selection step with a given
+    selected set; everything after it is computed as above. The tests use it
+    to re-evaluate the output on another implementation's selection when two
+    selections differ only by tokens tied with the threshold.
 
     Returns a dict of float64 arrays: u [B,Hq,N], s_low [B,Hq,T],
     sel int64 [B,Hq,m] ascending, s_high [B,Hq,m], p [B,Hq,m],
@@ -162,8 +168,11 @@ def decode_attn(q, dk, dv, key_codes, val_codes, klow: int, khigh: int,
             for h in range(g * G, (g + 1) * G):
                 u = scale * (dk @ q[b, h])
                 s_low = (kc[:, :klow] * u[ki[:, :klow]]).sum(axis=1)
-                order = np.argsort(-s_low, kind="stable")
-                S = np.sort(order[:m])
+                if sel is None:
+                    order = np.argsort(-s_low, kind="stable")
+                    S = np.sort(order[:m])
+                else:
+                    S = np.sort(np.asarray(sel[b, h], dtype=np.int64))
                 s_high = (kc[S, :khigh] * u[ki[S, :khigh]]).sum(axis=1)
                 e = np.exp(s_high - s_high.max())
                 p = e / e.sum()

@@ -1,0 +1,100 @@
+"""Shared helpers for the GPU parity tests: host<->device transfer of the
+seeded inputs, and the comparison rules (tolerances) against the oracle.
+
+Tolerances (fixed for this path):
+  * selection: identical sets except tokens whose oracle s_low lies within
+    1e-5 of the oracle's m-th largest s_low;
+  * attention output: relative L2 error <= 2e-3 over the whole tensor;
+  * encode: >= 99.9% of code indices identical, matched coefficients within
+    1e-4 (fp32 output) and within half an fp16 ulp + 1e-4 (packed fp16).
+Intermediate stages use tighter bounds derived from fp32 arithmetic.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+SEL_TOL = 1e-5
+OUT_RTOL = 2e-3
+IDX_AGREE = 0.999
+COEF_TOL = 1e-4
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def to_bf16(a):
+    torch = torch_mod()
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda").to(torch.bfloat16)
+
+
+def to_f32(a):
+    torch = torch_mod()
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda")
+
+
+def to_words(a):
+    torch = torch_mod()
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint32).view(np.int32)).to("cuda")
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def check_selection(sel_gpu, s_low_ref, m, tol=SEL_TOL):
+    """sel_gpu: [rows, m] ascending token ids; s_low_ref: [rows, T] oracle
+    scores. Returns the number of rows whose sets differ (all differences
+    must be threshold ties)."""
+    rows = sel_gpu.shape[0]
+    ndiff = 0
+    for r in range(rows):
+        g = sel_gpu[r].astype(np.int64)
+        assert np.all(np.diff(g) > 0), f"row {r}: selection not strictly ascending"
+        s = s_low_ref[r]
+        order = np.argsort(-s, kind="stable")
+        want = np.sort(order[:m])
+        if not np.array_equal(g, want):
+            thr = s[order[m - 1]]
+            diff = np.setxor1d(g, want)
+            bad = diff[np.abs(s[diff] - thr) > tol]
+            assert bad.size == 0, (f"row {r}: tokens {bad[:8]} differ and are not within "
+                                   f"{tol} of the threshold {thr}")
+            ndiff += 1
+    return ndiff
+
+
+def code_agreement(idx_gpu, idx_ref):
+    """Fraction of identical code indices, position by position."""
+    return float((idx_gpu == idx_ref).mean())
+
+
+def matched_prefix_mask(idx_gpu, idx_ref):
+    """True for positions before the first index mismatch of each vector."""
+    eq = idx_gpu == idx_ref
+    return np.cumprod(eq, axis=1).astype(bool)
+
+
+def unpack_words(w):
+    w = np.asarray(w).view(np.uint32)
+    return (w & 0xFFFF).astype(np.int64), (w >> 16).astype(np.uint16).view(np.float16).astype(np.float64)
+
+
+def f16_half_ulp(x):
+    x = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(x, 2.0 ** -14)))
+    return 2.0 ** (e - 11)

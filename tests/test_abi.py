@@ -1,0 +1,141 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/sdkv.h, and rejects bad arguments with the documented
+status before anything is enqueued (so these calls never touch a device)."""
+import ctypes
+import re
+
+import pytest
+
+import decode_attention_sparse_amd as sd
+import oracle
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+def declared_symbols():
+    txt = open(sd.HEADER).read()
+    return sorted(set(re.findall(r"SDKV_API\s+[\w\s\*]+?\b(sdkv_\w+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = sd.lib()
+    names = declared_symbols()
+    assert len(names) == 9, names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.sdkv_abi_version() == 1
+
+
+def test_status_strings():
+    lib = sd.lib()
+    for s in range(7):
+        assert lib.sdkv_status_str(s)
+    assert lib.sdkv_status_str(99) == b"unknown status"
+
+
+def test_selected_count_matches_oracle():
+    for T in (1, 2, 9, 10, 11, 63, 64, 65, 256, 4096, 131072, 262144):
+        for num, den in ((1, 10), (1, 1), (3, 7), (1, 1000)):
+            assert sd.selected_count(T, num, den) == oracle.selected_count(T, num, den)
+    assert sd.selected_count(0, 1, 10) == 0
+    assert sd.selected_count(10, 2, 1) == 0
+
+
+def good_attn(**kw):
+    a = sd.AttnArgs(q=FAKE, q_dtype=sd.SDKV_BF16, dk=FAKE, dv=FAKE, dict_dtype=sd.SDKV_BF16,
+                    n_atoms=32768, B=1, Hq=32, Hkv=8, d=128, T=131072, key_low=FAKE,
+                    key_codes=FAKE, val_codes=FAKE, K=16, klow=3, khigh=16, top_num=1,
+                    top_den=10, scale=0.0883883, out=FAKE)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def ws_status(a):
+    nb = ctypes.c_size_t(0)
+    return sd.lib().sdkv_decode_attn_workspace(ctypes.byref(a), ctypes.byref(nb)), nb.value
+
+
+def test_decode_workspace_query():
+    st, nb = ws_status(good_attn())
+    assert st == 0 and nb > 0
+    st2, nb2 = ws_status(good_attn(T=4096))
+    assert st2 == 0 and 0 < nb2 < nb
+    assert ws_status(good_attn()) == (st, nb)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("q", None, sd.SDKV_ERR_NULL), ("dk", None, sd.SDKV_ERR_NULL),
+    ("dv", None, sd.SDKV_ERR_NULL), ("key_codes", None, sd.SDKV_ERR_NULL),
+    ("val_codes", None, sd.SDKV_ERR_NULL), ("out", None, sd.SDKV_ERR_NULL),
+    ("d", 96, sd.SDKV_ERR_SHAPE), ("T", 0, sd.SDKV_ERR_SHAPE),
+    ("Hq", 30, sd.SDKV_ERR_SHAPE), ("B", 0, sd.SDKV_ERR_SHAPE),
+    ("klow", 0, sd.SDKV_ERR_SHAPE), ("klow", 17, sd.SDKV_ERR_SHAPE),
+    ("khigh", 17, sd.SDKV_ERR_SHAPE), ("K", 33, sd.SDKV_ERR_SHAPE),
+    ("top_num", 0, sd.SDKV_ERR_SHAPE), ("top_num", 11, sd.SDKV_ERR_SHAPE),
+    ("n_atoms", 70000, sd.SDKV_ERR_SHAPE), ("scale", float("inf"), sd.SDKV_ERR_SHAPE),
+    ("q_dtype", 7, sd.SDKV_ERR_DTYPE), ("dict_dtype", -1, sd.SDKV_ERR_DTYPE),
+    ("q_dtype", sd.SDKV_F32, sd.SDKV_ERR_UNSUPPORTED),
+    ("n_atoms", 40000, sd.SDKV_ERR_UNSUPPORTED),
+])
+def test_decode_validation(field, value, status):
+    a = good_attn(**{field: value})
+    st, _ = ws_status(a)
+    assert st == status
+    # the compute entry point rejects it the same way, before any enqueue
+    assert sd.lib().sdkv_decode_attn(ctypes.byref(a), ctypes.c_void_p(FAKE), 1 << 40, None) == status
+
+
+def test_decode_workspace_errors():
+    a = good_attn()
+    _, nb = ws_status(a)
+    lib = sd.lib()
+    assert lib.sdkv_decode_attn(ctypes.byref(a), None, nb, None) == sd.SDKV_ERR_NULL
+    assert lib.sdkv_decode_attn(ctypes.byref(a), ctypes.c_void_p(FAKE), nb - 1, None) == sd.SDKV_ERR_WORKSPACE
+    assert lib.sdkv_decode_attn(None, ctypes.c_void_p(FAKE), nb, None) == sd.SDKV_ERR_NULL
+    assert lib.sdkv_decode_attn_workspace(ctypes.byref(a), None) == sd.SDKV_ERR_NULL
+
+
+def good_enc(**kw):
+    a = sd.EncodeArgs(x=FAKE, x_dtype=sd.SDKV_BF16, dict=FAKE, dict_dtype=sd.SDKV_BF16,
+                      n=262144, d=128, n_atoms=32768, K=16, codes=FAKE)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("x", None, sd.SDKV_ERR_NULL), ("dict", None, sd.SDKV_ERR_NULL),
+    ("codes", None, sd.SDKV_ERR_NULL), ("d", 32, sd.SDKV_ERR_SHAPE),
+    ("n", 0, sd.SDKV_ERR_SHAPE), ("n_atoms", 65537, sd.SDKV_ERR_SHAPE),
+    ("K", 0, sd.SDKV_ERR_SHAPE), ("K", 33, sd.SDKV_ERR_SHAPE),
+    ("x_dtype", 5, sd.SDKV_ERR_DTYPE),
+])
+def test_encode_validation(field, value, status):
+    a = good_enc(**{field: value})
+    nb = ctypes.c_size_t(0)
+    assert sd.lib().sdkv_encode_workspace(ctypes.byref(a), ctypes.byref(nb)) == status
+    assert sd.lib().sdkv_encode(ctypes.byref(a), ctypes.c_void_p(FAKE), 1 << 40, None) == status
+
+
+def test_encode_low_plane_klow_checked():
+    a = good_enc(low_plane=FAKE, klow=0)
+    nb = ctypes.c_size_t(0)
+    assert sd.lib().sdkv_encode_workspace(ctypes.byref(a), ctypes.byref(nb)) == sd.SDKV_ERR_SHAPE
+    a.klow = 3
+    assert sd.lib().sdkv_encode_workspace(ctypes.byref(a), ctypes.byref(nb)) == 0 and nb.value > 0
+    assert sd.lib().sdkv_encode(ctypes.byref(a), ctypes.c_void_p(FAKE), nb.value - 1, None) == sd.SDKV_ERR_WORKSPACE
+
+
+def test_topk_validation():
+    lib = sd.lib()
+    nb = ctypes.c_size_t(0)
+    assert lib.sdkv_select_topk_workspace(4, 1000, 100, ctypes.byref(nb)) == 0 and nb.value > 0
+    assert lib.sdkv_select_topk_workspace(4, 1000, 1001, ctypes.byref(nb)) == sd.SDKV_ERR_SHAPE
+    assert lib.sdkv_select_topk_workspace(0, 1000, 1, ctypes.byref(nb)) == sd.SDKV_ERR_SHAPE
+    assert lib.sdkv_select_topk_workspace(1, 1 << 24, 1, ctypes.byref(nb)) == sd.SDKV_ERR_UNSUPPORTED
+    V = ctypes.c_void_p
+    assert lib.sdkv_select_topk(None, 4, 1000, 1000, 10, V(FAKE), None, V(FAKE), 1 << 30, None) == sd.SDKV_ERR_NULL
+    assert lib.sdkv_select_topk(V(FAKE), 4, 1000, 999, 10, V(FAKE), None, V(FAKE), 1 << 30, None) == sd.SDKV_ERR_SHAPE
+    assert lib.sdkv_select_topk(V(FAKE), 4, 1000, 1000, 10, V(FAKE), None, None, 1 << 30, None) == sd.SDKV_ERR_NULL
+    assert lib.sdkv_select_topk(V(FAKE), 4, 1000, 1000, 10, V(FAKE), None, V(FAKE), 0, None) == sd.SDKV_ERR_WORKSPACE
