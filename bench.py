@@ -1,0 +1,343 @@
+#!/usr/bin/env python3
+"""Benchmark of the dictionary-coded KV cache on one MI355X.
+
+Metric (two parts):
+  * coded-KV decode attention, context-tokens/s at 128K: one decode step of a
+    Llama-3.1-8B-shaped layer (32 query / 8 KV heads, head_dim 128, 32,768-atom
+    bf16 key and value dictionaries, K=16, Klow=3, Khigh=16, top 10%) over
+    131,072 coded tokens at batch 1; value = B*T / time per step.
+  * KV vectors encoded/s: prefill encode of 32,768 tokens x 8 KV heads x
+    {K, V} = 524,288 bf16 vectors to K=16 codes over their stream's
+    32,768-atom dictionary (reported in the "encode" object).
+
+Inputs are seeded synthetic arrays (synth), resident in HBM before timing.
+Decode rotates through several copies of every input (codes, low plane,
+dictionaries, query) so the 256 MB Infinity Cache cannot serve repeated
+steps. Per-kernel times come from HIP events the library records between
+its kernels on the call's stream.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Prints one JSON line on stdout (progress goes to stderr).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "coded-KV decode attn context-tokens/s/GPU at 128K; KV vectors encoded/s"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA, TFLOP/s
+F16_PEAK_TFLOPS = 2500.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.h = ctypes.CDLL("libamdhip64.so.7")
+        self.h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        self.h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.made = []
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.h.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(e.value)
+        self.made += out
+        return out
+
+    def record(self, e, stream_handle):
+        if self.h.hipEventRecord(ctypes.c_void_p(e), ctypes.c_void_p(stream_handle)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def ms(self, a, b):
+        t = ctypes.c_float()
+        if self.h.hipEventElapsedTime(ctypes.byref(t), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(t.value)
+
+    def close(self):
+        for e in self.made:
+            self.h.hipEventDestroy(ctypes.c_void_p(e))
+        self.made = []
+
+
+def read_traffic(kernel: str, workload: str):
+    """HBM bytes per launch measured with rocprofv3 counters, from the
+    committed summary profiles/traffic_<kernel>_<workload>.md, if its recorded
+    source digest still matches the kernel source; else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and line.strip().startswith("- "):
+            k, v = line.strip()[2:].split(":", 1)
+            vals[k.strip()] = v.strip()
+    src = vals.get("source")
+    digest = vals.get("source_sha256")
+    if not src or not digest:
+        return None
+    with open(os.path.join(ROOT, src), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != digest:
+            return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------------------
+# decode at 128K
+# ---------------------------------------------------------------------------
+def bench_decode(args, torch, sd, synth, ev):
+    case = synth.decode_case("llama_layer_128k")
+    B, Hq, Hkv, T, d, K = case.B, case.Hq, case.Hkv, case.T, case.d, case.K
+    N, m = case.n_atoms, case.m
+    dev = "cuda"
+
+    def up_words(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int32)).to(dev)
+
+    base = dict(q=torch.from_numpy(case.q).to(dev).to(torch.bfloat16),
+                dk=torch.from_numpy(case.dk).to(dev).to(torch.bfloat16),
+                dv=torch.from_numpy(case.dv).to(dev).to(torch.bfloat16),
+                kc=up_words(case.key_codes), vc=up_words(case.val_codes),
+                kl=up_words(case.key_low))
+    set_bytes = sum(t.numel() * t.element_size() for t in base.values())
+    nsets = max(2, int(np.ceil(600e6 / set_bytes)))
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(nsets - 1)]
+    log(f"decode: {nsets} input sets of {set_bytes / 1e6:.1f} MB rotate through the timed steps")
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    ws = sd.Workspace()
+    stream = torch.cuda.current_stream()
+    nstage = 5  # SDKV_DECODE_STAGES + 1
+
+    def step(i, stage_events=None):
+        s = sets[i % nsets]
+        sd.sdkv_decode_attn(s["q"], s["dk"], s["dv"], s["kc"], s["vc"], klow=case.klow,
+                            khigh=case.khigh, top_num=case.top_num, top_den=case.top_den,
+                            scale=case.scale, key_low=s["kl"], out=out, workspace=ws,
+                            stage_events=stage_events)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [ev.create(nstage) for _ in range(args.steps)]
+    t0, t1 = ev.create(2)
+    torch.cuda.synchronize()
+    ev.record(t0, stream.cuda_stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    ev.record(t1, stream.cuda_stream)
+    torch.cuda.synchronize()
+    total_ms = ev.ms(t0, t1)
+    stage_ms = [float(np.mean([ev.ms(e[j], e[j + 1]) for e in evs])) for j in range(nstage - 1)]
+    ms = total_ms / args.steps
+
+    # algorithmic bytes (HBM): what the method must read per step
+    low_b = B * Hkv * T * case.klow * 4
+    refine_b = B * Hq * m * (case.khigh - case.klow) * 4
+    value_b = B * Hq * m * K * 4
+    dict_b = N * d * 2
+    qo_b = B * Hq * d * (2 + 4)
+    stage_bytes = [dict_b + B * Hq * d * 2, low_b + refine_b + value_b, dict_b, B * Hq * d * 4]
+    total_b = sum(stage_bytes)
+    dom = int(np.argmax(stage_ms))
+    names = ["k_utable_bf16", "k_rows", "k_wdv_bf16", "k_reduce_out"]
+    achieved = stage_bytes[dom] / (stage_ms[dom] * 1e-3) / 1e9
+    traffic = read_traffic(names[dom], "llama_layer_128k")
+    res = dict(
+        value=B * T / (ms * 1e-3), ms=ms, stage_ms=dict(zip(names, stage_ms)),
+        roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                  "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                  "traffic": traffic, "kernel": names[dom],
+                  "algorithmic_bytes_per_launch": stage_bytes[dom]},
+        path={"algorithmic_bytes_per_step": total_b, "qo_bytes": qo_b,
+              "achieved_GBs": round(total_b / (ms * 1e-3) / 1e9, 1),
+              "frac": round(total_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        config=dict(B=B, Hq=Hq, Hkv=Hkv, T=T, d=d, n_atoms=N, K=K, klow=case.klow,
+                    khigh=case.khigh, top="1/10", m=m, input_sets=nsets),
+        case=case)
+    return res
+
+
+# ---------------------------------------------------------------------------
+# encode (prefill)
+# ---------------------------------------------------------------------------
+def bench_encode(args, torch, sd, synth, ev):
+    dev = "cuda"
+    streams = []
+    for s in (0, 1):
+        e = synth.encode_case(stream=s)
+        streams.append(dict(x=torch.from_numpy(e.x).to(dev).to(torch.bfloat16),
+                            D=torch.from_numpy(e.dictionary).to(dev).to(torch.bfloat16),
+                            codes=torch.empty((e.x.shape[0], 16), dtype=torch.int32, device=dev),
+                            rn=torch.empty((e.x.shape[0],), dtype=torch.float32, device=dev),
+                            case=e))
+    n_total = sum(s["x"].shape[0] for s in streams)
+    ws = sd.Workspace()
+    stream = torch.cuda.current_stream()
+
+    def step(evsets=None):
+        for j, s in enumerate(streams):
+            sd.sdkv_encode(s["x"], s["D"], 16, codes=s["codes"], resid_norm=s["rn"],
+                           workspace=ws, stage_events=None if evsets is None else evsets[j])
+
+    for _ in range(args.enc_warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[ev.create(3) for _ in streams] for _ in range(args.enc_steps)]
+    t0, t1 = ev.create(2)
+    ev.record(t0, stream.cuda_stream)
+    for i in range(args.enc_steps):
+        step(evs[i])
+    ev.record(t1, stream.cuda_stream)
+    torch.cuda.synchronize()
+    ms = ev.ms(t0, t1) / args.enc_steps
+    kern_ms = float(np.mean([sum(ev.ms(e[1], e[2]) for e in es) for es in evs]))
+    prep_ms = float(np.mean([sum(ev.ms(e[0], e[1]) for e in es) for es in evs]))
+    flops = n_total * 2.0 * 32768 * 128 * 16
+    tflops = flops / (kern_ms * 1e-3) / 1e12
+    return dict(value=n_total / (ms * 1e-3), ms=ms, kernel_ms=kern_ms, prep_ms=prep_ms,
+                roofline={"bound": "mfma", "achieved": round(tflops, 1), "peak": F16_PEAK_TFLOPS,
+                          "unit": "TFLOP/s", "frac": round(tflops / F16_PEAK_TFLOPS, 4),
+                          "traffic": read_traffic("k_encode", "prefill_524k"),
+                          "kernel": "k_encode<128>", "algorithmic_flops_per_step": flops},
+                streams=streams)
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on the host cores
+# ---------------------------------------------------------------------------
+def cpu_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 1) for i in threadpool_info()]
+        return int(max(n)) if n else 1
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline_decode(case, budget_s):
+    import oracle
+    t = time.perf_counter()
+    reps = 0
+    while True:
+        oracle.decode_attn(case.q, case.dk, case.dv, case.key_codes, case.val_codes, case.klow,
+                           case.khigh, case.top_num, case.top_den, case.scale)
+        reps += 1
+        el = time.perf_counter() - t
+        if el >= budget_s or reps >= 20:
+            break
+    per = el / reps
+    return {"value": case.B * case.T / per, "unit": "context-tokens/s", "cores": cpu_threads(),
+            "kind": "oracle",
+            "sample": f"full 128K decode step (all {case.Hq} query heads), {reps} run(s), "
+                      f"{el:.1f} s, fp64 NumPy"}
+
+
+def cpu_baseline_encode(ecase, n_sample, budget_s):
+    import oracle
+    rng = np.random.default_rng(5)
+    pick = np.sort(rng.choice(ecase.x.shape[0], n_sample, replace=False))
+    t = time.perf_counter()
+    oracle.mp_encode(ecase.x[pick], ecase.dictionary, 16)
+    el = time.perf_counter() - t
+    return {"value": n_sample / el, "unit": "vectors/s", "cores": cpu_threads(), "kind": "oracle",
+            "sample": f"{n_sample} seeded vectors of the key stream, {el:.1f} s, fp64 NumPy"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--enc-steps", type=int, default=3)
+    ap.add_argument("--enc-warmup", type=int, default=1)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-encode", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        msg = ("this benchmark runs on one GPU only: the coded-KV path has no "
+               "multi-GPU implementation here (--gpus must be 1)")
+        print(msg, file=sys.stderr)
+        print(json.dumps({"metric": METRIC, "error": msg, "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import decode_attention_sparse_amd as sd
+    import synth
+    if not torch.cuda.is_available():
+        raise SystemExit("no GPU visible")
+    sd.lib()
+    ev = HipEvents()
+    log("decode benchmark (128K context)")
+    dec = bench_decode(args, torch, sd, synth, ev)
+    log(f"  {dec['ms'] * 1e3:.1f} us/step, stages (us): "
+        + ", ".join(f"{k} {v * 1e3:.1f}" for k, v in dec["stage_ms"].items()))
+    enc = None
+    if not args.no_encode:
+        log("encode benchmark (524,288 vectors)")
+        enc = bench_encode(args, torch, sd, synth, ev)
+        log(f"  {enc['ms']:.2f} ms/step, kernel {enc['kernel_ms']:.2f} ms, "
+            f"{enc['value'] / 1e6:.2f} M vectors/s, {enc['roofline']['achieved']} TFLOP/s")
+    cpu = None
+    if not args.no_cpu:
+        log("cpu baseline (fp64 oracle on host cores)")
+        cpu = cpu_baseline_decode(dec["case"], args.cpu_budget)
+        if enc is not None:
+            enc["cpu_baseline"] = cpu_baseline_encode(enc["streams"][0]["case"], 1024,
+                                                      args.cpu_budget)
+    ev.close()
+    line = {
+        "metric": METRIC, "value": round(dec["value"], 1), "unit": "context-tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(dec["ms"], 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded; unit-norm Gaussian bf16 dictionaries, random codes)",
+        "config": {"workload": "llama3.1-8b-shaped layer decode step at 128K context",
+                   **dec["config"], "storage": "bf16 dictionaries/query, uint16+fp16 codes"},
+        "roofline": dec["roofline"],
+        "path_roofline": dec["path"],
+        "stage_us": {k: round(v * 1e3, 2) for k, v in dec["stage_ms"].items()},
+        "cpu_baseline": cpu,
+    }
+    if enc is not None:
+        line["encode"] = {
+            "metric": "KV vectors encoded/s", "value": round(enc["value"], 1),
+            "unit": "vectors/s", "ms_per_step": round(enc["ms"], 3),
+            "steps": args.enc_steps, "warmup": args.enc_warmup,
+            "config": {"workload": "prefill encode, 32768 tokens x 8 KV heads x {K,V}",
+                       "vectors": 524288, "d": 128, "n_atoms": 32768, "K": 16,
+                       "screen": "fp16 MFMA + exact fp32 recheck"},
+            "kernel_ms": round(enc["kernel_ms"], 3), "prep_ms": round(enc["prep_ms"], 3),
+            "roofline": enc["roofline"], "cpu_baseline": enc.get("cpu_baseline"),
+            "dtype": "f32"}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -37,7 +37,8 @@ class EncodeArgs(ctypes.Structure):
                 ("dict_dtype", c_int32), ("n", c_int64), ("d", c_int32),
                 ("n_atoms", c_int32), ("K", c_int32), ("codes", c_void_p),
                 ("coef_f32", c_void_p), ("resid_norm", c_void_p),
-                ("low_plane", c_void_p), ("klow", c_int32)]
+                ("low_plane", c_void_p), ("klow", c_int32),
+                ("stage_events", c_void_p)]
 
 
 class AttnArgs(ctypes.Structure):
@@ -49,7 +50,7 @@ class AttnArgs(ctypes.Structure):
                 ("khigh", c_int32), ("top_num", c_int64), ("top_den", c_int64),
                 ("scale", c_float), ("out", c_void_p), ("u", c_void_p),
                 ("s_low", c_void_p), ("sel", c_void_p), ("s_high", c_void_p),
-                ("w", c_void_p)]
+                ("w", c_void_p), ("stage_events", c_void_p)]
 
 
 class SdkvError(RuntimeError):
@@ -70,6 +71,13 @@ def _lib():
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with "
                               "`python -m decode_attention_sparse_amd.build`")
+        # Load torch's HIP runtime first so that libsdkv binds to the same
+        # runtime instance (both carry the soname libamdhip64.so.7); streams
+        # and events from torch are then valid handles inside the library.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         lib = ctypes.CDLL(LIB_PATH)
         P = ctypes.POINTER
         lib.sdkv_abi_version.restype = c_int32
@@ -165,9 +173,17 @@ def selected_count(T: int, top_num: int, top_den: int) -> int:
     return int(_lib().sdkv_selected_count(T, top_num, top_den))
 
 
+def _events(stage_events):
+    """ctypes array of hipEvent_t handles (ints), or None."""
+    if stage_events is None:
+        return None, None
+    arr = (c_void_p * len(stage_events))(*[int(e) for e in stage_events])
+    return arr, ctypes.cast(arr, c_void_p).value
+
+
 def sdkv_encode(x, dictionary, K: int, *, codes=None, coef_f32=None, resid_norm=None,
                 low_plane=None, klow: int = 0, workspace: Optional[Workspace] = None,
-                stream=None):
+                stream=None, stage_events=None):
     """Greedy-pursuit codes of the rows of x [n, d] over `dictionary`
     [n_atoms, d] (bf16 or fp32 GPU tensors). Output tensors are allocated
     when not given: codes int32 [n, K]; pass coef_f32=True / resid_norm=True /
@@ -190,6 +206,7 @@ def sdkv_encode(x, dictionary, K: int, *, codes=None, coef_f32=None, resid_norm=
                    resid_norm=_dev(resid_norm if resid_norm is not False else None, "resid_norm"),
                    low_plane=_dev(low_plane if low_plane is not False else None, "low_plane"),
                    klow=klow)
+    ev_keep, a.stage_events = _events(stage_events)
     nb = c_size_t(0)
     _check(_lib().sdkv_encode_workspace(ctypes.byref(a), ctypes.byref(nb)), "sdkv_encode_workspace")
     wp, wn = _ws(workspace, nb.value)
@@ -228,7 +245,7 @@ def decode_attn_workspace_bytes(args: AttnArgs) -> int:
 def sdkv_decode_attn(q, dk, dv, key_codes, val_codes, *, klow: int, khigh: int,
                      top_num: int = 1, top_den: int = 10, scale: Optional[float] = None,
                      key_low=None, out=None, debug: bool = False,
-                     workspace: Optional[Workspace] = None, stream=None):
+                     workspace: Optional[Workspace] = None, stream=None, stage_events=None):
     """Hierarchical coded decode attention. q [B,Hq,d] bf16; dk, dv
     [n_atoms,d] bf16/fp32; key_codes, val_codes int32 [B,Hkv,T,K]; optional
     key_low int32 [B,Hkv,T,klow]. Returns out fp32 [B,Hq,d], or with
@@ -252,6 +269,7 @@ def sdkv_decode_attn(q, dk, dv, key_codes, val_codes, *, klow: int, khigh: int,
                    w=torch.empty((B, Hq, N), dtype=torch.float32, device=dev))
     a = attn_args(q, dk, dv, key_codes, val_codes, klow, khigh, top_num, top_den, scale, out,
                   key_low=key_low, **dbg)
+    ev_keep, a.stage_events = _events(stage_events)
     wp, wn = _ws(workspace, decode_attn_workspace_bytes(a))
     _check(_lib().sdkv_decode_attn(ctypes.byref(a), ctypes.c_void_p(wp), wn, _stream(stream)),
            "sdkv_decode_attn")

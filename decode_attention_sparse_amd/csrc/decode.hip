@@ -518,6 +518,8 @@ sdkv_status launch_decode(const sdkv_attn_args* a, const DecodePlan& p, void* ws
   ua.u_dbg = a->u;
   ua.zero = (uint32_t*)(base + p.off_zero);
   ua.zero_words = (int64_t)(p.zero_bytes / 4);
+  void* const* ev = a->stage_events;
+  if (!record_stage(ev, 0, stream)) return SDKV_ERR_DEVICE;
   if (a->dict_dtype == SDKV_BF16) {
     const int grid = (a->n_atoms + 63) / 64;
     hipLaunchKernelGGL(k_utable_bf16, dim3(grid), dim3(256), 0, stream, ua);
@@ -557,6 +559,7 @@ sdkv_status launch_decode(const sdkv_attn_args* a, const DecodePlan& p, void* ws
   ra.err = err;
   const void* kfn = pick_rows_kernel(p.spt, p.lpt);
   if (!kfn) return SDKV_ERR_UNSUPPORTED;
+  if (!record_stage(ev, 1, stream)) return SDKV_ERR_DEVICE;
   int64_t batch = rows;
   if (p.P > 1) {
     int cap = 0;
@@ -593,6 +596,7 @@ sdkv_status launch_decode(const sdkv_attn_args* a, const DecodePlan& p, void* ws
   wa.opart = opart;
   wa.w_out = a->w;
   const dim3 wgrid((unsigned)(p.nchunks * p.nrt));
+  if (!record_stage(ev, 2, stream)) return SDKV_ERR_DEVICE;
   if (a->dict_dtype == SDKV_BF16)
     hipLaunchKernelGGL(k_wdv_bf16, wgrid, dim3(256), 0, stream, wa);
   else
@@ -600,9 +604,11 @@ sdkv_status launch_decode(const sdkv_attn_args* a, const DecodePlan& p, void* ws
   if (hipGetLastError() != hipSuccess) return SDKV_ERR_DEVICE;
 
   const int64_t nout = rows * a->d;
+  if (!record_stage(ev, 3, stream)) return SDKV_ERR_DEVICE;
   hipLaunchKernelGGL(k_reduce_out, dim3((unsigned)((nout + 255) / 256)), dim3(256), 0, stream,
                      (const float*)opart, p.nchunks, nout, a->out);
   if (hipGetLastError() != hipSuccess) return SDKV_ERR_DEVICE;
+  if (!record_stage(ev, 4, stream)) return SDKV_ERR_DEVICE;
   return SDKV_OK;
 }
 

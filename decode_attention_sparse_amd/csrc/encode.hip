@@ -294,6 +294,8 @@ sdkv_status launch_encode(const sdkv_encode_args* a, const EncodePlan& p, void* 
   char* base = (char*)ws;
   uint16_t* dh = (uint16_t*)(base + p.off_dh);
   const int dict_f32 = a->dict_dtype == SDKV_F32;
+  void* const* ev = a->stage_events;
+  if (!record_stage(ev, 0, stream)) return SDKV_ERR_DEVICE;
   {
     const int64_t total = (int64_t)p.npad * a->d;
     const int grid = (int)std::min<int64_t>(2048, (total + 255) / 256);
@@ -319,11 +321,13 @@ sdkv_status launch_encode(const sdkv_encode_args* a, const EncodePlan& p, void* 
   e.low_plane = a->low_plane;
   const int64_t max_grid = 0x7FFFFFFF;
   if (p.nwg > max_grid) return SDKV_ERR_UNSUPPORTED;
+  if (!record_stage(ev, 1, stream)) return SDKV_ERR_DEVICE;
   if (a->d == 128)
     hipLaunchKernelGGL(k_encode<128>, dim3((unsigned)p.nwg), dim3(EB), 0, stream, e);
   else
     hipLaunchKernelGGL(k_encode<64>, dim3((unsigned)p.nwg), dim3(EB), 0, stream, e);
   if (hipGetLastError() != hipSuccess) return SDKV_ERR_DEVICE;
+  if (!record_stage(ev, 2, stream)) return SDKV_ERR_DEVICE;
   return SDKV_OK;
 }
 

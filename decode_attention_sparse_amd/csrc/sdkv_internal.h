@@ -69,6 +69,12 @@ sdkv_status plan_encode(const sdkv_encode_args* a, EncodePlan* p);
 sdkv_status launch_encode(const sdkv_encode_args* a, const EncodePlan& p, void* ws,
                           hipStream_t stream);
 
+// Records caller-provided timing event i on `stream` (no-op without events).
+inline bool record_stage(void* const* ev, int i, hipStream_t stream) {
+  if (!ev) return true;
+  return hipEventRecord((hipEvent_t)ev[i], stream) == hipSuccess;
+}
+
 // Largest number of co-resident workgroups for a kernel on the current device.
 sdkv_status coresident_blocks(const void* kernel, int threads, size_t dyn_lds, int* out);
 

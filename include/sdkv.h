@@ -84,7 +84,13 @@ typedef struct sdkv_encode_args {
   float* resid_norm;    /* OUT [n] |r_K|_2, or NULL                       */
   uint32_t* low_plane;  /* OUT [n, klow] first klow code words, or NULL   */
   int32_t klow;         /* 1 .. K when low_plane != NULL                  */
+  /* Optional stage timing: NULL, or SDKV_ENCODE_STAGES + 1 hipEvent_t
+     handles (created by the caller); event i is recorded on `stream` before
+     stage i and the last one after the final stage. Stages: 0 fp16 screen
+     copy of the dictionary, 1 pursuit.                                   */
+  void* const* stage_events;
 } sdkv_encode_args;
+#define SDKV_ENCODE_STAGES 2
 
 /* Bytes of device workspace sdkv_encode needs for these arguments. */
 SDKV_API sdkv_status sdkv_encode_workspace(const sdkv_encode_args* args, size_t* bytes);
@@ -132,7 +138,14 @@ typedef struct sdkv_attn_args {
   int32_t* sel;         /* OUT [B, Hq, m] selected tokens, ascending      */
   float* s_high;        /* OUT [B, Hq, m] aligned with sel                */
   float* w;             /* OUT [B, Hq, n_atoms] normalised value weights  */
+  /* Optional stage timing: NULL, or SDKV_DECODE_STAGES + 1 hipEvent_t
+     handles (created by the caller); event i is recorded on `stream` before
+     stage i and the last one after the final stage. Stages: 0 U table,
+     1 score/select/rescore/softmax/value weights, 2 W.Dv contraction,
+     3 output reduction. A failed event record returns SDKV_ERR_DEVICE.   */
+  void* const* stage_events;
 } sdkv_attn_args;
+#define SDKV_DECODE_STAGES 4
 
 /* m = ceil(T * top_num / top_den), clamped to [1, T]; 0 on bad input. */
 SDKV_API int64_t sdkv_selected_count(int64_t T, int64_t top_num, int64_t top_den);
