@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256) void k_utable_f32(UArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Row kernel: score -> select -> rescore -> softmax partial -> value weights
+// Row kernel: score -> select -> rescore -> softmax -> value weights -> W
 // ---------------------------------------------------------------------------
 struct RowsArgs {
   const float* U;           // [rows, N]
@@ -109,21 +109,45 @@ struct RowsArgs {
   int row0, nrows;
   int64_t T, m, chunk;
   float* s_low_out;         // optional [rows, T]
-  int32_t* sel;             // [rows, m]
-  float* s_high;            // [rows, m]
-  float* wpart;             // [rows, P, N]
+  int32_t* sel_out;         // optional [rows, m]
+  float* s_high_out;        // optional [rows, m]
+  int32_t* sel;             // [rows, m] workspace list (used when LDS is short)
+  float* s_high;            // [rows, m] workspace
+  float* wpart;             // [rows, P, N] per-workgroup unnormalised weights
   float2* stats;            // [rows, P] (local max, local sum of exp)
-  uint32_t* ghist;          // [rows, 3, 2048]
+  uint32_t* ghist;          // [rows, 2048]
+  uint32_t* cand;           // [rows, P, chunk] threshold-bin candidates
   uint32_t* xchg;           // [rows, P, 2]
   uint32_t* bar;            // [rows]
   uint32_t* err;
 };
 
-template <int SPT, int LPT>
+constexpr int kTokBatch = 4;   // selected tokens per thread per load batch
+constexpr int kListCap = 3456; // selected tokens per workgroup kept in LDS
+
+// Loads the first `nw` words of a code record (record length K words).
+// FAST: K == 16, the record is 64-byte aligned and read as 4 x 16 bytes.
+template <bool FAST>
+__device__ __forceinline__ void load_record(const uint32_t* rec, int K, int nw, uint32_t (&w)[32]) {
+  if (FAST) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 v = ((const u32x4*)rec)[q];
+      w[4 * q] = v[0]; w[4 * q + 1] = v[1]; w[4 * q + 2] = v[2]; w[4 * q + 3] = v[3];
+    }
+  } else {
+    for (int i = 0; i < nw && i < K; ++i) w[i] = rec[i];
+  }
+}
+
+template <int SPT, bool FAST>
 __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   __shared__ float s_u[kMaxAtomsDecode];
   __shared__ SelShared sh;
   __shared__ float s_red[16];
+  __shared__ uint16_t s_lt[kListCap];
+  __shared__ float s_ls[kListCap];
+  __shared__ uint32_t s_qcnt[5 * kMaxRowP + 1];
 
   const int tid = threadIdx.x;
   const int L = xcd_tile(blockIdx.x, a.nrows * a.P);
@@ -133,6 +157,7 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   const int64_t kv = (int64_t)b * a.Hkv + g;
   const int64_t t0 = (int64_t)p * a.chunk;
   const int64_t t1 = min(a.T, t0 + a.chunk);
+  constexpr int AMASK = kMaxAtomsDecode - 1;
 
   // 1. stage this query head's U row in LDS
   {
@@ -143,23 +168,47 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   }
   __syncthreads();
 
-  // 2. s_low of every token in the chunk -> order-preserving keys
+  // 2. s_low of every token in the chunk -> order-preserving keys. Loads are
+  // issued for 8 tokens at a time from clamped (always valid) addresses.
   uint32_t key[SPT];
   {
     const uint32_t* lo = a.low + kv * a.T * a.low_words;
+    const int lw = a.low_words;
 #pragma unroll
-    for (int j = 0; j < SPT; ++j) {
-      const int64_t t = t0 + (int64_t)j * SB + tid;
-      key[j] = 0u;
-      if (t < t1) {
-        const uint32_t* wp = lo + t * a.low_words;
-        float s = 0.f;
-        for (int i = 0; i < a.klow; ++i) {
-          const uint32_t wd = wp[i];
-          s = fmaf(code_coef(wd), s_u[code_idx(wd) & (kMaxAtomsDecode - 1)], s);
+    for (int jb = 0; jb < SPT; jb += 8) {
+      if (FAST) {
+        uint32_t wd[8][4];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const int64_t t = min(t0 + (int64_t)(jb + jj) * SB + tid, a.T - 1);
+          const uint32_t* wp = lo + t * lw;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) wd[jj][i] = wp[min(i, a.klow - 1)];
         }
-        key[j] = float_key(s);
-        if (a.s_low_out) a.s_low_out[(int64_t)row * a.T + t] = s;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const int64_t t = t0 + (int64_t)(jb + jj) * SB + tid;
+          float s = 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (i < a.klow) s = fmaf(code_coef(wd[jj][i]), s_u[code_idx(wd[jj][i]) & AMASK], s);
+          key[jb + jj] = (t < t1) ? float_key(s) : 0u;
+          if (a.s_low_out && t < t1) a.s_low_out[(int64_t)row * a.T + t] = s;
+        }
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const int64_t t = t0 + (int64_t)(jb + jj) * SB + tid;
+          key[jb + jj] = 0u;
+          if (t < t1) {
+            const uint32_t* wp = lo + t * lw;
+            float s = 0.f;
+            for (int i = 0; i < a.klow; ++i)
+              s = fmaf(code_coef(wp[i]), s_u[code_idx(wp[i]) & AMASK], s);
+            key[jb + jj] = float_key(s);
+            if (a.s_low_out) a.s_low_out[(int64_t)row * a.T + t] = s;
+          }
+        }
       }
     }
   }
@@ -168,163 +217,271 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   SelGroup grp;
   grp.P = a.P;
   grp.p = p;
-  grp.ghist = a.ghist + (int64_t)row * 3 * 2048;
+  grp.ghist = a.ghist + (int64_t)row * 2048;
   grp.xchg = a.xchg + (int64_t)row * a.P * 2;
   grp.bar = a.bar + row;
   grp.err = a.err;
+  grp.cand = a.cand + (int64_t)row * a.P * a.chunk;
+  grp.cap = a.chunk;
   uint32_t offset, count, tau;
-  const uint64_t sel = radix_select<SPT>(key, (uint32_t)a.m, sh, grp, &offset, &count, &tau);
+  const uint64_t sel = radix_select<SPT>(key, (uint32_t)a.m, sh, grp, &offset, &count, &tau, s_qcnt);
 
-  int32_t* sel_row = a.sel + (int64_t)row * a.m;
-  float* sh_row = a.s_high + (int64_t)row * a.m;
+  // 4. compaction: the selected tokens of this workgroup in token order, as
+  // offsets within the chunk in LDS (global list when they do not fit).
+  const int64_t cnt = max((int64_t)0, min((int64_t)count, a.m - (int64_t)offset));
+  const bool in_lds = cnt <= kListCap;
+  int32_t* sel_g = a.sel + (int64_t)row * a.m;        // workspace list (fallback)
+  float* sh_g = a.s_high + (int64_t)row * a.m;
+  int32_t* sel_dbg = a.sel_out ? a.sel_out + (int64_t)row * a.m : nullptr;
+  float* sh_dbg = a.s_high_out ? a.s_high_out + (int64_t)row * a.m : nullptr;
   ordered_ranks<SPT>(sel, sh, [&](int j, uint32_t r) {
     const int64_t pos = (int64_t)offset + r;
-    if (pos < a.m) sel_row[pos] = (int32_t)(t0 + (int64_t)j * SB + tid);
+    if (pos >= a.m) return;
+    const int32_t t = (int32_t)(t0 + (int64_t)j * SB + tid);
+    if (in_lds) s_lt[r] = (uint16_t)(j * SB + tid);
+    else sel_g[pos] = t;
+    if (sel_dbg) sel_dbg[pos] = t;
   });
-  const int64_t cnt = min((int64_t)count, a.m - (int64_t)offset);
-  __threadfence_block();
+  if (!in_lds) __threadfence_block();
   __syncthreads();
 
-  // 4. Khigh rescore of this workgroup's selected tokens (LPT lanes per token)
-  constexpr int TPW = 64 / LPT;  // tokens per wave per iteration
-  const int w = wave_id(), lane = lane_id();
-  const int jj = lane % LPT;
-  const int64_t step = (int64_t)SNW * TPW;
-  const int64_t my0 = (int64_t)w * TPW + lane / LPT;
-  const int64_t wave0 = (int64_t)w * TPW;
-  float lmax = -INFINITY;
+  // 5. Khigh rescore, one thread per selected token (entries i = tid + k*SB;
+  // the same thread handles the same entries in every later loop). Value
+  // records are fetched in the same pass; their |coefficient| sums bound the
+  // value weights for the fixed-point accumulation below.
   const uint32_t* kbase = a.kc + kv * a.T * a.K;
-  for (int64_t base = 0; base + wave0 < cnt; base += step) {
-    const int64_t i = base + my0;
-    const bool valid = i < cnt;
-    float v = 0.f;
-    if (valid && jj < a.khigh) {
-      const int64_t t = min(max((int64_t)sel_row[offset + i], (int64_t)0), a.T - 1);
-      const uint32_t wd = kbase[t * a.K + jj];
-      v = code_coef(wd) * s_u[code_idx(wd) & (kMaxAtomsDecode - 1)];
+  const uint32_t* vbase = a.vc + kv * a.T * a.K;
+  const bool one_batch = cnt <= (int64_t)SB * kTokBatch;
+  // (lmax, vb): running max of s_high and sum_t exp(s_t - lmax) sum_j |kappa^v_tj|
+  float lmax = -INFINITY, vb = 0.f;
+  uint32_t vw[kTokBatch][32];
+  for (int64_t base = 0; base < cnt; base += (int64_t)SB * kTokBatch) {
+    int64_t tt[kTokBatch];
+#pragma unroll
+    for (int r = 0; r < kTokBatch; ++r) {
+      const int64_t i = base + (int64_t)r * SB + tid;
+      int64_t t = t0;
+      if (i < cnt) t = in_lds ? t0 + s_lt[i] : (int64_t)sel_g[offset + i];
+      tt[r] = min(max(t, (int64_t)0), a.T - 1);
     }
-    v = group_sum<LPT>(v);
-    if (valid) {
-      if (jj == 0) sh_row[offset + i] = v;
-      lmax = fmaxf(lmax, v);
+    uint32_t kw[kTokBatch][32];
+#pragma unroll
+    for (int r = 0; r < kTokBatch; ++r) {
+      load_record<FAST>(kbase + tt[r] * a.K, a.K, a.khigh, kw[r]);
+      load_record<FAST>(vbase + tt[r] * a.K, a.K, a.K, vw[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < kTokBatch; ++r) {
+      const int64_t i = base + (int64_t)r * SB + tid;
+      float s = 0.f, va = 0.f;
+      if (FAST) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          if (q < a.khigh) s = fmaf(code_coef(kw[r][q]), s_u[code_idx(kw[r][q]) & AMASK], s);
+          va += fabsf(code_coef(vw[r][q]));
+        }
+      } else {
+        for (int q = 0; q < a.khigh; ++q)
+          s = fmaf(code_coef(kw[r][q]), s_u[code_idx(kw[r][q]) & AMASK], s);
+        for (int q = 0; q < a.K; ++q) va += fabsf(code_coef(vw[r][q]));
+      }
+      if (i < cnt) {
+        if (in_lds) s_ls[i] = s;
+        else sh_g[offset + i] = s;
+        if (sh_dbg) sh_dbg[offset + i] = s;
+        if (s > lmax) {
+          vb = vb * __expf(lmax - s) + va;
+          lmax = s;
+        } else {
+          vb += __expf(s - lmax) * va;
+        }
+      }
     }
   }
   const float M = block_max<SNW>(lmax, s_red);
+  // sum_t p_t sum_j |kappa^v_tj| over this workgroup's tokens (online-softmax
+  // rescaling of each thread's running sum to the workgroup max)
+  vb = (lmax > -INFINITY) ? vb * __expf(lmax - M) : 0.f;
+  const float vsum = block_sum<SNW>(vb, s_red) * 1.0001f;
 
-  // 5. softmax partial + per-atom value weights (LDS float atomics)
-  for (int i = tid; i < a.N; i += SB) s_u[i] = 0.f;
-  __threadfence_block();
+  // 6. softmax weights and per-atom value weights. LDS integer atomics are
+  // much faster than float ones on gfx950, so weights accumulate in int32
+  // fixed point with a power-of-two scale S such that S * sum|p kappa| <=
+  // 2^30: no bin can overflow, and each contribution is rounded to 2^-31
+  // of the workgroup's total weight mass.
+  const int sexp = (vsum > 0.f) ? 30 - ilogbf(vsum) - 1 : 0;
+  const float S = ldexpf(1.f, min(sexp, 100));
+  int32_t* s_w = (int32_t*)s_u;
+  for (int i = tid; i < a.N; i += SB) s_w[i] = 0;
+  if (!in_lds) __threadfence_block();
   __syncthreads();
   float lsum = 0.f;
-  const uint32_t* vbase = a.vc + kv * a.T * a.K;
-  for (int64_t base = 0; base + wave0 < cnt; base += step) {
-    const int64_t i = base + my0;
-    if (i < cnt) {
-      const int64_t t = min(max((int64_t)sel_row[offset + i], (int64_t)0), a.T - 1);
-      const float pt = __expf(sh_row[offset + i] - M);
-      if (jj < a.K) {
-        const uint32_t wd = vbase[t * a.K + jj];
-        atomicAdd(&s_u[code_idx(wd) & (kMaxAtomsDecode - 1)], pt * code_coef(wd));
+  for (int64_t base = 0; base < cnt; base += (int64_t)SB * kTokBatch) {
+    float pt[kTokBatch];
+    if (!one_batch) {
+      int64_t tt[kTokBatch];
+#pragma unroll
+      for (int r = 0; r < kTokBatch; ++r) {
+        const int64_t i = base + (int64_t)r * SB + tid;
+        int64_t t = t0;
+        if (i < cnt) t = in_lds ? t0 + s_lt[i] : (int64_t)sel_g[offset + i];
+        tt[r] = min(max(t, (int64_t)0), a.T - 1);
       }
-      if (jj == 0) lsum += pt;
+#pragma unroll
+      for (int r = 0; r < kTokBatch; ++r) load_record<FAST>(vbase + tt[r] * a.K, a.K, a.K, vw[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < kTokBatch; ++r) {
+      const int64_t i = base + (int64_t)r * SB + tid;
+      pt[r] = (i < cnt) ? (in_lds ? s_ls[i] : sh_g[offset + i]) : -INFINITY;
+    }
+#pragma unroll
+    for (int r = 0; r < kTokBatch; ++r) {
+      const int64_t i = base + (int64_t)r * SB + tid;
+      if (i < cnt) {
+        const float pr = __expf(pt[r] - M);
+        lsum += pr;
+        const float ps = pr * S;
+        if (FAST) {
+#pragma unroll
+          for (int q = 0; q < 16; ++q)
+            atomicAdd((uint32_t*)&s_w[code_idx(vw[r][q]) & AMASK],
+                      (uint32_t)(int32_t)rintf(ps * code_coef(vw[r][q])));
+        } else {
+          for (int q = 0; q < a.K; ++q)
+            atomicAdd((uint32_t*)&s_w[code_idx(vw[r][q]) & AMASK],
+                      (uint32_t)(int32_t)rintf(ps * code_coef(vw[r][q])));
+        }
+      }
     }
   }
   const float lsum_all = block_sum<SNW>(lsum, s_red);
   __syncthreads();
 
-  // 6. write the partial weights and the (max, sum) pair
-  {
-    float* dst = a.wpart + ((int64_t)row * a.P + p) * a.N;
-    const int n4 = a.N >> 2;
-    for (int i = tid; i < n4; i += SB) ((float4*)dst)[i] = ((const float4*)s_u)[i];
-    for (int i = (n4 << 2) + tid; i < a.N; i += SB) dst[i] = s_u[i];
-    if (tid == 0) a.stats[(int64_t)row * a.P + p] = make_float2(cnt > 0 ? M : -INFINITY, lsum_all);
+  // 7. this workgroup's unnormalised weights and its (max, sum of exp) pair;
+  // the W.Dv kernel merges the P partials of each row.
+  float* dst = a.wpart + ((int64_t)row * a.P + p) * a.N;
+  const float invS = 1.f / S;
+  const int n4 = a.N >> 2;
+  for (int i = tid; i < n4; i += SB) {
+    const int4 v = ((const int4*)s_w)[i];
+    ((float4*)dst)[i] = make_float4((float)v.x * invS, (float)v.y * invS, (float)v.z * invS,
+                                    (float)v.w * invS);
   }
+  for (int i = (n4 << 2) + tid; i < a.N; i += SB) dst[i] = (float)s_w[i] * invS;
+  if (tid == 0) a.stats[(int64_t)row * a.P + p] = make_float2(cnt > 0 ? M : -INFINITY, lsum_all);
 }
 
 // ---------------------------------------------------------------------------
-// W . Dv
+// out = W . Dv  (split-K over atom chunks, then a fixed-order sum)
 // ---------------------------------------------------------------------------
 struct WdvArgs {
-  const float* wpart;     // [rows, P, N]
-  const float2* stats;    // [rows, P]
+  const float* wpart;     // [rows, P, N] unnormalised per-workgroup weights
+  const float2* stats;    // [rows, P] (max, sum of exp) per partial
   const void* dv;         // [N, d]
   int N, d, P, rows, nrt, nsub, nchunks;
   float* opart;           // [nchunks, rows, d]
-  float* w_out;           // optional [rows, N]
+  float* w_out;           // optional [rows, N] normalised weights
 };
 
-constexpr int WPITCH = kWdvSub + 8;         // u16 elements per A row in LDS
-constexpr int BPITCH = kWdvSub / 2 + 4;     // u32 words (atom pairs) per B row
+constexpr int WSUB = 128;                 // atoms per MFMA sub-chunk
+constexpr int WRT = 32;                   // rows per workgroup tile
+constexpr int WPITCH = WSUB + 8;          // u16 per A row in LDS
+constexpr int BPITCH = WSUB / 2 + 4;      // u32 (atom pairs) per B row in LDS
 
-// Fills s_coef[r][p] = exp(M_p - M_r) / L_r for the 16 rows of the tile.
+// s_coef[r][q] = exp(M_q - max_q M_q) / sum_q exp(M_q - max M) l_q for the
+// tile's rows: the softmax merge of the row's P partial results.
 __device__ __forceinline__ void wdv_coefs(const WdvArgs& a, int r0, float* s_coef) {
-  const int tid = threadIdx.x;
-  if (tid < 16) {
-    const int row = r0 + tid;
-    if (row < a.rows) {
-      const float2* st = a.stats + (int64_t)row * a.P;
-      float M = -INFINITY;
-      for (int p = 0; p < a.P; ++p) M = fmaxf(M, st[p].x);
-      float Lr = 0.f;
-      for (int p = 0; p < a.P; ++p) {
-        const float c = (st[p].y > 0.f) ? __expf(st[p].x - M) : 0.f;
-        s_coef[tid * kMaxRowP + p] = c;
-        Lr += c * st[p].y;
-      }
-      const float inv = 1.f / Lr;
-      for (int p = 0; p < a.P; ++p) s_coef[tid * kMaxRowP + p] *= inv;
-    } else {
-      for (int p = 0; p < a.P; ++p) s_coef[tid * kMaxRowP + p] = 0.f;
+  const int w = wave_id(), l = lane_id();
+  for (int r = w; r < WRT; r += 4) {
+    const int row = r0 + r;
+    float Mq = -INFINITY, lq = 0.f;
+    if (row < a.rows && l < a.P) {
+      const float2 st = a.stats[(int64_t)row * a.P + l];
+      Mq = st.x;
+      lq = st.y;
     }
+    const float Mx = wave_max(Mq);
+    const float c = (lq > 0.f) ? __expf(Mq - Mx) : 0.f;
+    const float Lr = wave_sum(c * lq);
+    if (l < a.P) s_coef[r * kMaxRowP + l] = (Lr > 0.f) ? c / Lr : 0.f;
   }
 }
 
-// merged weight W[r][atom] for the tile's rows
-__device__ __forceinline__ float wdv_weight(const WdvArgs& a, const float* s_coef, int r0, int r,
-                                            int atom) {
-  const int row = r0 + r;
-  if (row >= a.rows || atom >= a.N) return 0.f;
-  const float* src = a.wpart + (int64_t)row * a.P * a.N + atom;
-  float acc = 0.f;
-  for (int p = 0; p < a.P; ++p) acc = fmaf(s_coef[r * kMaxRowP + p], src[(int64_t)p * a.N], acc);
-  return acc;
+// 16 merged weights W[row][a0 .. a0+16) (zero outside the matrix)
+__device__ __forceinline__ void wdv_merge16(const WdvArgs& a, const float* s_coef, int r, int row,
+                                            int a0, float (&v)[16]) {
+#pragma unroll
+  for (int e = 0; e < 16; ++e) v[e] = 0.f;
+  if (row >= a.rows) return;
+  const float* src = a.wpart + (int64_t)row * a.P * a.N + a0;
+  if (a0 + 16 <= a.N && (a.N & 3) == 0) {
+#pragma unroll 4
+    for (int q = 0; q < a.P; ++q) {
+      const float c = s_coef[r * kMaxRowP + q];
+      const float4* sp = (const float4*)(src + (int64_t)q * a.N);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float4 x = sp[k];
+        v[4 * k] = fmaf(c, x.x, v[4 * k]);
+        v[4 * k + 1] = fmaf(c, x.y, v[4 * k + 1]);
+        v[4 * k + 2] = fmaf(c, x.z, v[4 * k + 2]);
+        v[4 * k + 3] = fmaf(c, x.w, v[4 * k + 3]);
+      }
+    }
+  } else {
+    for (int q = 0; q < a.P; ++q) {
+      const float c = s_coef[r * kMaxRowP + q];
+      for (int e = 0; e < 16 && a0 + e < a.N; ++e)
+        v[e] = fmaf(c, src[(int64_t)q * a.N + e], v[e]);
+    }
+  }
+  if (a.w_out) {
+    float* wo = a.w_out + (int64_t)row * a.N + a0;
+    for (int e = 0; e < 16 && a0 + e < a.N; ++e) wo[e] = v[e];
+  }
 }
 
 __global__ __launch_bounds__(256) void k_wdv_bf16(WdvArgs a) {
-  __shared__ float s_coef[16 * kMaxRowP];
-  __shared__ __attribute__((aligned(16))) uint16_t s_ahi[16 * WPITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t s_alo[16 * WPITCH];
+  __shared__ float s_coef[WRT * kMaxRowP];
+  __shared__ __attribute__((aligned(16))) uint16_t s_ahi[WRT * WPITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t s_alo[WRT * WPITCH];
   __shared__ __attribute__((aligned(16))) uint32_t s_bt[128 * BPITCH];
 
   const int tid = threadIdx.x, w = wave_id(), l = lane_id();
   const int L = xcd_tile(blockIdx.x, a.nchunks * a.nrt);
   const int chunk = L / a.nrt, rt = L % a.nrt;
-  const int r0 = rt * 16;
+  const int r0 = rt * WRT;
   wdv_coefs(a, r0, s_coef);
   __syncthreads();
-
   const uint16_t* dv = (const uint16_t*)a.dv;
-  const int ncol = a.d >> 4;  // 16-wide output column tiles
-  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  const int ncol = a.d >> 4;
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
   for (int sub = 0; sub < a.nsub; ++sub) {
-    const int a0 = (chunk * a.nsub + sub) * kWdvSub;
+    const int a0 = (chunk * a.nsub + sub) * WSUB;
     if (a0 >= a.N) break;
-    // A: merged weights, split into bf16 hi + lo
+    // A: 32 rows x 128 atoms of merged W, split into bf16 hi + lo
     {
-      const int atom = a0 + tid;  // kWdvSub == blockDim
-      for (int r = 0; r < 16; ++r) {
-        const float wv = wdv_weight(a, s_coef, r0, r, atom);
-        if (a.w_out && r0 + r < a.rows && atom < a.N) a.w_out[(int64_t)(r0 + r) * a.N + atom] = wv;
-        const uint32_t hi = f32_to_bf16_rne(wv);
-        const uint32_t lo = f32_to_bf16_rne(wv - __uint_as_float(hi << 16));
-        s_ahi[r * WPITCH + tid] = (uint16_t)hi;
-        s_alo[r * WPITCH + tid] = (uint16_t)lo;
+      const int r = tid >> 3, c0 = (tid & 7) * 16;
+      float v[16];
+      wdv_merge16(a, s_coef, r, r0 + r, a0 + c0, v);
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        const uint32_t h0 = f32_to_bf16_rne(v[e]), h1 = f32_to_bf16_rne(v[e + 1]);
+        const uint32_t l0 = f32_to_bf16_rne(v[e] - __uint_as_float(h0 << 16));
+        const uint32_t l1 = f32_to_bf16_rne(v[e + 1] - __uint_as_float(h1 << 16));
+        *(uint32_t*)&s_ahi[r * WPITCH + c0 + e] = h0 | (h1 << 16);
+        *(uint32_t*)&s_alo[r * WPITCH + c0 + e] = l0 | (l1 << 16);
       }
     }
-    // B: Dv rows a0 .. a0+255, transposed to [dim][atom pair]
-    for (int it = tid; it < (kWdvSub / 2) * (a.d >> 3); it += 256) {
-      const int ap = it % (kWdvSub / 2), sg = it / (kWdvSub / 2);
+    // B: Dv rows a0..a0+127 transposed to [dim][atom pair]
+    for (int it = tid; it < (WSUB / 2) * (a.d >> 3); it += 256) {
+      const int ap = it % (WSUB / 2), sg = it / (WSUB / 2);
       const int atom = a0 + 2 * ap;
       u32x4 x0 = u32x4{0u, 0u, 0u, 0u}, x1 = u32x4{0u, 0u, 0u, 0u};
       if (atom < a.N) x0 = *(const u32x4*)(dv + (int64_t)atom * a.d + 8 * sg);
@@ -336,21 +493,22 @@ __global__ __launch_bounds__(256) void k_wdv_bf16(WdvArgs a) {
       }
     }
     __syncthreads();
-    // MFMA: wave w owns output columns [32w, 32w+32)
+    // MFMA: wave w owns output columns [32w, 32w+32), both 16-row tiles
     if (2 * w < ncol) {
 #pragma unroll
-      for (int ks = 0; ks < kWdvSub / 32; ++ks) {
+      for (int ks = 0; ks < WSUB / 32; ++ks) {
         const int kk = ks * 32 + 8 * (l >> 4);
-        const u32x4 ah = *(const u32x4*)(s_ahi + (l & 15) * WPITCH + kk);
-        const u32x4 al = *(const u32x4*)(s_alo + (l & 15) * WPITCH + kk);
         const int n0 = 32 * w + (l & 15);
         const u32x4 b0 = *(const u32x4*)(s_bt + n0 * BPITCH + (kk >> 1));
-        acc0 = mfma_bf16(ah, b0, acc0);
-        acc0 = mfma_bf16(al, b0, acc0);
-        if (2 * w + 1 < ncol) {
-          const u32x4 b1 = *(const u32x4*)(s_bt + (n0 + 16) * BPITCH + (kk >> 1));
-          acc1 = mfma_bf16(ah, b1, acc1);
-          acc1 = mfma_bf16(al, b1, acc1);
+        const u32x4 b1 = *(const u32x4*)(s_bt + (n0 + 16) * BPITCH + (kk >> 1));
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+          const u32x4 ah = *(const u32x4*)(s_ahi + (rr * 16 + (l & 15)) * WPITCH + kk);
+          const u32x4 al = *(const u32x4*)(s_alo + (rr * 16 + (l & 15)) * WPITCH + kk);
+          acc[rr][0] = mfma_bf16(ah, b0, acc[rr][0]);
+          acc[rr][0] = mfma_bf16(al, b0, acc[rr][0]);
+          acc[rr][1] = mfma_bf16(ah, b1, acc[rr][1]);
+          acc[rr][1] = mfma_bf16(al, b1, acc[rr][1]);
         }
       }
     }
@@ -359,48 +517,52 @@ __global__ __launch_bounds__(256) void k_wdv_bf16(WdvArgs a) {
   if (2 * w < ncol) {
     float* dst = a.opart + (int64_t)chunk * a.rows * a.d;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = r0 + 4 * (l >> 4) + i;
-      if (row < a.rows) {
-        dst[(int64_t)row * a.d + 32 * w + (l & 15)] = acc0[i];
-        if (2 * w + 1 < ncol) dst[(int64_t)row * a.d + 32 * w + 16 + (l & 15)] = acc1[i];
+    for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = r0 + rr * 16 + 4 * (l >> 4) + i;
+        if (row < a.rows) {
+          dst[(int64_t)row * a.d + 32 * w + (l & 15)] = acc[rr][0][i];
+          if (2 * w + 1 < ncol) dst[(int64_t)row * a.d + 32 * w + 16 + (l & 15)] = acc[rr][1][i];
+        }
       }
-    }
   }
 }
 
 // fp32 value dictionary (small configurations): plain fp32 FMAs.
 __global__ __launch_bounds__(256) void k_wdv_f32(WdvArgs a) {
-  __shared__ float s_coef[16 * kMaxRowP];
-  __shared__ float s_w[16 * kWdvSub];
+  __shared__ float s_coef[WRT * kMaxRowP];
+  __shared__ float s_w[WRT * WSUB];
   const int tid = threadIdx.x;
   const int L = xcd_tile(blockIdx.x, a.nchunks * a.nrt);
   const int chunk = L / a.nrt, rt = L % a.nrt;
-  const int r0 = rt * 16;
+  const int r0 = rt * WRT;
   wdv_coefs(a, r0, s_coef);
   __syncthreads();
   const float* dv = (const float*)a.dv;
-  const int r = tid >> 4;            // row within the tile
-  const int c0 = (tid & 15) * 8;     // 8 output columns per thread
-  float acc[8];
+  const int r = tid >> 3;            // row within the tile
+  const int c0 = (tid & 7) * 16;     // 16 output columns per thread
+  float acc[16];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
   for (int sub = 0; sub < a.nsub; ++sub) {
-    const int a0 = (chunk * a.nsub + sub) * kWdvSub;
+    const int a0 = (chunk * a.nsub + sub) * WSUB;
     if (a0 >= a.N) break;
-    for (int rr = 0; rr < 16; ++rr) {
-      const float wv = wdv_weight(a, s_coef, r0, rr, a0 + tid);
-      s_w[rr * kWdvSub + tid] = wv;
-      if (a.w_out && r0 + rr < a.rows && a0 + tid < a.N) a.w_out[(int64_t)(r0 + rr) * a.N + a0 + tid] = wv;
+    {
+      float v[16];
+      const int rr = tid >> 3, c1 = (tid & 7) * 16;
+      wdv_merge16(a, s_coef, rr, r0 + rr, a0 + c1, v);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s_w[rr * WSUB + c1 + e] = v[e];
     }
     __syncthreads();
-    const int na = min(kWdvSub, a.N - a0);
+    const int na = min(WSUB, a.N - a0);
     if (c0 < a.d) {
       for (int k = 0; k < na; ++k) {
-        const float wv = s_w[r * kWdvSub + k];
+        const float wv = s_w[r * WSUB + k];
         const float* drow = dv + (int64_t)(a0 + k) * a.d + c0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = fmaf(wv, drow[i], acc[i]);
+        for (int i = 0; i < 16; ++i) acc[i] = fmaf(wv, drow[i], acc[i]);
       }
     }
     __syncthreads();
@@ -409,17 +571,36 @@ __global__ __launch_bounds__(256) void k_wdv_f32(WdvArgs a) {
   if (row < a.rows && c0 < a.d) {
     float* dst = a.opart + ((int64_t)chunk * a.rows + row) * a.d + c0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dst[i] = acc[i];
+    for (int i = 0; i < 16; ++i) dst[i] = acc[i];
   }
 }
 
-__global__ __launch_bounds__(256) void k_reduce_out(const float* opart, int nchunks, int64_t n,
-                                                    float* out) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
+// out[o] = sum_c opart[c][o] in a fixed order: 16 threads per output each
+// sum every 16th chunk, then a fixed-order combine in LDS.
+constexpr int RED_OUT = 64;   // outputs per workgroup
+__global__ __launch_bounds__(1024) void k_reduce_out(const float* opart, int nchunks, int64_t n,
+                                                     float* out) {
+  __shared__ float s_p[16][RED_OUT + 1];
+  const int o = threadIdx.x % RED_OUT, q = threadIdx.x / RED_OUT;
+  const int64_t i = (int64_t)blockIdx.x * RED_OUT + o;
   float s = 0.f;
-  for (int c = 0; c < nchunks; ++c) s += opart[(int64_t)c * n + i];
-  out[i] = s;
+  if (i < n) {
+    int c = q;
+    for (; c + 48 < nchunks; c += 64) {
+      const float x0 = opart[(int64_t)c * n + i], x1 = opart[(int64_t)(c + 16) * n + i];
+      const float x2 = opart[(int64_t)(c + 32) * n + i], x3 = opart[(int64_t)(c + 48) * n + i];
+      s += x0; s += x1; s += x2; s += x3;
+    }
+    for (; c < nchunks; c += 16) s += opart[(int64_t)c * n + i];
+  }
+  s_p[q][o] = s;
+  __syncthreads();
+  if (q == 0 && i < n) {
+    float t = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) t += s_p[k][o];
+    out[i] = t;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -446,9 +627,9 @@ sdkv_status plan_decode(const sdkv_attn_args* a, DecodePlan* p) {
   q.chunk = (T + P - 1) / P;
   q.spt = spt_for(q.chunk);
   if (q.spt == 0) return SDKV_ERR_UNSUPPORTED;
-  q.lpt = a->K <= 16 ? 16 : 32;
-  q.nrt = (int)((q.rows + 15) / 16);
-  const int nsub_total = (a->n_atoms + kWdvSub - 1) / kWdvSub;
+  q.fast = (a->K == 16 && a->klow <= 4 && a->khigh <= 16) ? 1 : 0;
+  q.nrt = (int)((q.rows + WRT - 1) / WRT);
+  const int nsub_total = (a->n_atoms + WSUB - 1) / WSUB;
   const int target = std::max(1, 512 / q.nrt);
   q.nsub = std::max(1, (nsub_total + target - 1) / target);
   q.nchunks = (nsub_total + q.nsub - 1) / q.nsub;
@@ -462,26 +643,22 @@ sdkv_status plan_decode(const sdkv_attn_args* a, DecodePlan* p) {
   q.off_wpart = off;  off = align_up(off + (size_t)rows * q.P * N * 4, A);
   q.off_stats = off;  off = align_up(off + (size_t)rows * q.P * 8, A);
   q.off_zero = off;
-  q.off_ghist = off;  off += (q.P > 1) ? (size_t)rows * 3 * 2048 * 4 : 0;
+  q.off_ghist = off;  off += (q.P > 1) ? (size_t)rows * 2048 * 4 : 0;
   q.off_xchg = off;   off += (size_t)rows * q.P * 2 * 4;
   q.off_bar = off;    off += (size_t)rows * 4;
   q.off_err = off;    off += 4;
   off = align_up(off, A);
   q.zero_bytes = off - q.off_zero;
   q.off_opart = off;  off = align_up(off + (size_t)q.nchunks * rows * a->d * 4, A);
+  q.off_cand = off;   off = align_up(off + (q.P > 1 ? (size_t)rows * q.P * q.chunk * 4 : 0), A);
   q.total = off;
   *p = q;
   return SDKV_OK;
 }
 
-template <int SPT, int LPT>
-static const void* rows_kernel() {
-  return (const void*)&k_rows<SPT, LPT>;
-}
-
-static const void* pick_rows_kernel(int spt, int lpt) {
-#define SDKV_PICK(S)                                                   \
-  if (spt == S) return lpt == 16 ? rows_kernel<S, 16>() : rows_kernel<S, 32>();
+static const void* pick_rows_kernel(int spt, bool fast) {
+#define SDKV_PICK(S) \
+  if (spt == S) return fast ? (const void*)&k_rows<S, true> : (const void*)&k_rows<S, false>;
   SDKV_PICK(4)
   SDKV_PICK(8)
   SDKV_PICK(16)
@@ -496,8 +673,8 @@ sdkv_status launch_decode(const sdkv_attn_args* a, const DecodePlan& p, void* ws
   char* base = (char*)ws;
   const int64_t rows = p.rows;
   float* U = (float*)(base + p.off_u);
-  int32_t* sel = a->sel ? a->sel : (int32_t*)(base + p.off_sel);
-  float* shigh = a->s_high ? a->s_high : (float*)(base + p.off_shigh);
+  int32_t* sel = (int32_t*)(base + p.off_sel);
+  float* shigh = (float*)(base + p.off_shigh);
   float* wpart = (float*)(base + p.off_wpart);
   float2* stats = (float2*)(base + p.off_stats);
   uint32_t* ghist = (uint32_t*)(base + p.off_ghist);
@@ -505,6 +682,7 @@ sdkv_status launch_decode(const sdkv_attn_args* a, const DecodePlan& p, void* ws
   uint32_t* bar = (uint32_t*)(base + p.off_bar);
   uint32_t* err = (uint32_t*)(base + p.off_err);
   float* opart = (float*)(base + p.off_opart);
+  void* const* ev = a->stage_events;
 
   // 1. U table (+ clear the barrier / histogram region)
   UArgs ua;
@@ -518,7 +696,6 @@ sdkv_status launch_decode(const sdkv_attn_args* a, const DecodePlan& p, void* ws
   ua.u_dbg = a->u;
   ua.zero = (uint32_t*)(base + p.off_zero);
   ua.zero_words = (int64_t)(p.zero_bytes / 4);
-  void* const* ev = a->stage_events;
   if (!record_stage(ev, 0, stream)) return SDKV_ERR_DEVICE;
   if (a->dict_dtype == SDKV_BF16) {
     const int grid = (a->n_atoms + 63) / 64;
@@ -551,15 +728,18 @@ sdkv_status launch_decode(const sdkv_attn_args* a, const DecodePlan& p, void* ws
   ra.s_low_out = a->s_low;
   ra.sel = sel;
   ra.s_high = shigh;
+  ra.sel_out = a->sel;
+  ra.s_high_out = a->s_high;
   ra.wpart = wpart;
   ra.stats = stats;
   ra.ghist = ghist;
+  ra.cand = (uint32_t*)(base + p.off_cand);
   ra.xchg = xchg;
   ra.bar = bar;
   ra.err = err;
-  const void* kfn = pick_rows_kernel(p.spt, p.lpt);
+  const bool aligned = (((uintptr_t)a->key_codes | (uintptr_t)a->val_codes) & 15u) == 0;
+  const void* kfn = pick_rows_kernel(p.spt, p.fast && aligned);
   if (!kfn) return SDKV_ERR_UNSUPPORTED;
-  if (!record_stage(ev, 1, stream)) return SDKV_ERR_DEVICE;
   int64_t batch = rows;
   if (p.P > 1) {
     int cap = 0;
@@ -568,6 +748,7 @@ sdkv_status launch_decode(const sdkv_attn_args* a, const DecodePlan& p, void* ws
     batch = std::min<int64_t>(rows, cap / p.P);
     if (batch < 1) return SDKV_ERR_UNSUPPORTED;
   }
+  if (!record_stage(ev, 1, stream)) return SDKV_ERR_DEVICE;
   for (int64_t r0 = 0; r0 < rows; r0 += batch) {
     ra.row0 = (int)r0;
     ra.nrows = (int)std::min<int64_t>(batch, rows - r0);
@@ -581,20 +762,20 @@ sdkv_status launch_decode(const sdkv_attn_args* a, const DecodePlan& p, void* ws
     if (e != hipSuccess) return SDKV_ERR_DEVICE;
   }
 
-  // 3. merge partials and contract with Dv
+  // 3. contract the value weights with Dv
   WdvArgs wa;
   wa.wpart = wpart;
   wa.stats = stats;
+  wa.P = p.P;
+  wa.w_out = a->w;
   wa.dv = a->dv;
   wa.N = a->n_atoms;
   wa.d = a->d;
-  wa.P = p.P;
   wa.rows = (int)rows;
   wa.nrt = p.nrt;
   wa.nsub = p.nsub;
   wa.nchunks = p.nchunks;
   wa.opart = opart;
-  wa.w_out = a->w;
   const dim3 wgrid((unsigned)(p.nchunks * p.nrt));
   if (!record_stage(ev, 2, stream)) return SDKV_ERR_DEVICE;
   if (a->dict_dtype == SDKV_BF16)
@@ -605,8 +786,8 @@ sdkv_status launch_decode(const sdkv_attn_args* a, const DecodePlan& p, void* ws
 
   const int64_t nout = rows * a->d;
   if (!record_stage(ev, 3, stream)) return SDKV_ERR_DEVICE;
-  hipLaunchKernelGGL(k_reduce_out, dim3((unsigned)((nout + 255) / 256)), dim3(256), 0, stream,
-                     (const float*)opart, p.nchunks, nout, a->out);
+  hipLaunchKernelGGL(k_reduce_out, dim3((unsigned)((nout + RED_OUT - 1) / RED_OUT)), dim3(1024), 0,
+                     stream, (const float*)opart, p.nchunks, nout, a->out);
   if (hipGetLastError() != hipSuccess) return SDKV_ERR_DEVICE;
   if (!record_stage(ev, 4, stream)) return SDKV_ERR_DEVICE;
   return SDKV_OK;

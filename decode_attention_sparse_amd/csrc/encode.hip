@@ -120,9 +120,9 @@ __global__ __launch_bounds__(EB) void k_encode(EncArgs a) {
     }
     s_rnorm[tid] = sqrtf(nrm);
   }
-  __threadfence();
+  // residual rows are exchanged between waves of this workgroup through
+  // global memory: workgroup-scope ordering (part of __syncthreads) suffices
   __syncthreads();
-  __threadfence();
 
   const int nchunks = a.npad / ECH;
   for (int step = 0; step < a.K; ++step) {
@@ -261,9 +261,7 @@ __global__ __launch_bounds__(EB) void k_encode(EncArgs a) {
         if (a.coef_f32) a.coef_f32[rowg * a.K + step] = bc;
       }
     }
-    __threadfence();
     __syncthreads();
-    __threadfence();
   }
 
   // --- final outputs ------------------------------------------------------------

@@ -20,7 +20,6 @@ constexpr int kMaxSPT = 64;                                // keys per thread
 constexpr int64_t kMaxChunk = (int64_t)kRowThreads * kMaxSPT;  // 32768 tokens
 constexpr int kMaxRowP = 64;   // workgroups per decode row
 constexpr int kMaxAtomsDecode = 32768;
-constexpr int kWdvSub = 256;   // atoms per MFMA sub-chunk in the W.Dv kernel
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -30,14 +29,15 @@ struct DecodePlan {
   int P = 1;             // workgroups per row
   int64_t chunk = 0;     // tokens per workgroup
   int spt = 0;           // keys per thread (template instance)
-  int lpt = 16;          // lanes per token in the rescore/value loops
-  int nrt = 0;           // 16-row tiles in the W.Dv kernel
-  int nsub = 1;          // 256-atom sub-chunks per W.Dv workgroup
+  int fast = 0;          // K == 16, klow <= 4, khigh <= 16: vector code loads
+  int nrt = 0;           // 32-row tiles in the W.Dv kernel
+  int nsub = 1;          // 128-atom sub-chunks per W.Dv workgroup
   int nchunks = 0;       // atom chunks in the W.Dv kernel
   // workspace byte offsets
   size_t off_u = 0, off_sel = 0, off_shigh = 0, off_wpart = 0, off_stats = 0;
   size_t off_zero = 0, zero_bytes = 0;  // [ghist | xchg | bar | err], cleared per call
   size_t off_ghist = 0, off_xchg = 0, off_bar = 0, off_err = 0, off_opart = 0;
+  size_t off_cand = 0;
   size_t total = 0;
 };
 
@@ -51,6 +51,7 @@ struct TopkPlan {
   int64_t chunk = 0;
   int spt = 0;
   size_t off_ghist = 0, off_xchg = 0, off_bar = 0, off_err = 0, zero_bytes = 0;
+  size_t off_cand = 0;
   size_t total = 0;
 };
 sdkv_status plan_topk(int64_t rows, int64_t n, int64_t k, TopkPlan* p);

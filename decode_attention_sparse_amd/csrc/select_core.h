@@ -9,11 +9,12 @@
 //
 // Selection = the m largest keys, ties broken toward the lower element index
 // (the "top 10%" of the review page's Summary, with the tie rule read as
-// lowest index first). Found by a 3-round MSD radix select over 11/11/10-bit
-// digits; with P > 1 the per-workgroup digit histograms are merged through
-// global atomics between cooperative barriers, and a final exchange of
-// per-workgroup counts gives every workgroup its output offset and its share
-// of the keys equal to the threshold.
+// lowest index first). Found by an MSD radix select over 11/11/10-bit digits.
+// One workgroup per row: three local rounds. P > 1 workgroups per row: one
+// global 11-bit histogram round, then an exchange of the keys in the
+// threshold bin, after which every workgroup finishes the select and the
+// per-workgroup counts locally (radix_select_coop) -- two cross-workgroup
+// synchronisations in all.
 #pragma once
 #include "sdkv_device.h"
 
@@ -32,11 +33,15 @@ struct SelShared {
 struct SelGroup {
   int P;              // workgroups sharing the row
   int p;              // this workgroup's position (element order)
-  uint32_t* ghist;    // [3][2048] zeroed before launch (P > 1)
+  uint32_t* ghist;    // [2048] zeroed before launch (P > 1)
   uint32_t* xchg;     // [P][2]
   uint32_t* bar;      // barrier counter, zeroed before launch
   uint32_t* err;      // set to 1 if a barrier wait gave up
+  uint32_t* cand;     // [P][cap] candidate keys of each workgroup (P > 1)
+  int64_t cap;        // candidate slots per workgroup (>= keys per workgroup)
 };
+
+constexpr int kCandPT = 32;  // candidates per thread kept in registers
 
 // Calls f(j, rank) for every set bit j of `bits`, where rank is the position
 // of slot j among all set slots of the block in element order.
@@ -65,12 +70,251 @@ __device__ __forceinline__ void ordered_ranks(uint64_t bits, SelShared& sh, F&& 
   __syncthreads();
 }
 
+// Finds digit v of an nbins-bin histogram in sh.hist with
+// #(digit > v) < need <= #(digit >= v). Returns v; *above = #(digit > v).
+// Uniform across the block. (If fewer than `need` keys exist, v = 0.)
+__device__ __forceinline__ uint32_t find_digit(SelShared& sh, int nbins, uint32_t need,
+                                               uint32_t* above_out) {
+  const int tid = threadIdx.x;
+  const int bpt = nbins / SB;
+  uint32_t loc = 0;
+  for (int i = 0; i < bpt; ++i) loc += sh.hist[tid * bpt + i];
+  sh.scan[SB - 1 - tid] = loc;  // reversed order: a prefix scan gives suffix sums
+  if (tid == 0) { sh.bcast[0] = 0u; sh.bcast[1] = 0u; }
+  __syncthreads();
+  const uint32_t rv = sh.scan[tid];
+  uint32_t tot;
+  const uint32_t above = block_excl_scan<SNW>(rv, sh.tmp, &tot);
+  const int o = SB - 1 - tid;
+  if (above < need && above + rv >= need) {
+    uint32_t run = above;
+    for (int i = bpt - 1; i >= 0; --i) {
+      const uint32_t c = sh.hist[o * bpt + i];
+      if (run + c >= need) {
+        sh.bcast[0] = (uint32_t)(o * bpt + i);
+        sh.bcast[1] = run;
+        break;
+      }
+      run += c;
+    }
+  }
+  __syncthreads();
+  const uint32_t v = sh.bcast[0];
+  *above_out = sh.bcast[1];
+  __syncthreads();
+  return v;
+}
+
+// Multi-workgroup select with two cross-workgroup synchronisations:
+//  1. a global histogram of the top 11 key bits gives the threshold bin v1;
+//  2. each workgroup publishes the keys of its chunk that fall in bin v1
+//     (a few percent of them) and its count of keys above the bin; every
+//     workgroup then reads all candidates of the row and finishes the
+//     remaining 21 bits of the radix select, and the per-workgroup counts
+//     of keys above / equal to the threshold, locally.
+template <int SPT>
+__device__ __forceinline__ uint64_t radix_select_coop(const uint32_t (&key)[SPT], uint32_t m, SelShared& sh,
+                                      const SelGroup& g, uint32_t* offset, uint32_t* count,
+                                      uint32_t* tau_out, uint32_t* s_qcnt) {
+  const int tid = threadIdx.x;
+  // --- round 1: global histogram of the top 11 bits ----------------------------
+  for (int i = tid; i < 2048; i += SB) sh.hist[i] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < SPT; ++j)
+    if (key[j] != 0u) atomicAdd(&sh.hist[key[j] >> 21], 1u);
+  __syncthreads();
+  for (int i = tid; i < 2048; i += SB) {
+    const uint32_t c = sh.hist[i];
+    if (c) atomicAdd(&g.ghist[i], c);
+  }
+  group_barrier(g.bar, (uint32_t)g.P, g.err);
+  for (int i = tid; i < 2048; i += SB) sh.hist[i] = ld_agent(&g.ghist[i]);
+  __syncthreads();
+  uint32_t gt1;
+  const uint32_t v1 = find_digit(sh, 2048, m, &gt1);
+  const uint32_t need1 = m - min(m, gt1);
+
+  // --- round 2: publish this workgroup's candidates (keys in bin v1) ----------
+  uint64_t cbits = 0;
+  uint32_t na = 0, nc = 0;
+#pragma unroll
+  for (int j = 0; j < SPT; ++j) {
+    const uint32_t k = key[j];
+    const uint32_t dg = k >> 21;
+    if (k != 0u && dg > v1) ++na;
+    if (k != 0u && dg == v1) { cbits |= 1ull << j; ++nc; }
+  }
+  uint32_t tna, tnc;
+  (void)block_excl_scan<SNW>(na, sh.tmp, &tna);
+  (void)block_excl_scan<SNW>(nc, sh.tmp, &tnc);
+  uint32_t* mycand = g.cand + (int64_t)g.p * g.cap;
+  ordered_ranks<SPT>(cbits, sh, [&](int j, uint32_t r) {
+    if (r < g.cap) st_agent(&mycand[r], key[j]);
+  });
+  if (tid == 0) {
+    st_agent(&g.xchg[2 * g.p], tna);
+    st_agent(&g.xchg[2 * g.p + 1], tnc);
+  }
+  group_barrier(g.bar, (uint32_t)g.P * 2u, g.err);
+
+  // --- every workgroup: counts per workgroup, then all candidates ------------
+  // s_qcnt layout: [0,P) above-bin counts A_q, [P,2P) candidate counts c_q,
+  // [2P,3P+1) candidate prefix, [3P+1,4P+1) #cand > tau, [4P+1,5P+1) #cand == tau
+  const int P = g.P;
+  if (tid < P) {
+    s_qcnt[tid] = ld_agent(&g.xchg[2 * tid]);
+    s_qcnt[P + tid] = min((uint32_t)g.cap, ld_agent(&g.xchg[2 * tid + 1]));
+    s_qcnt[3 * P + 1 + tid] = 0u;
+    s_qcnt[4 * P + 1 + tid] = 0u;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t run = 0;
+    for (int q = 0; q < P; ++q) { s_qcnt[2 * P + q] = run; run += s_qcnt[P + q]; }
+    s_qcnt[3 * P] = run;
+  }
+  __syncthreads();
+  const uint32_t C = s_qcnt[3 * P];
+  const uint32_t* cpre = s_qcnt + 2 * P;
+  // candidate g_idx -> (workgroup q, slot) by binary search on the prefix
+  auto cand_at = [&](uint32_t gi, int* qo) -> uint32_t {
+    int lo = 0, hi = P - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (cpre[mid] <= gi) lo = mid; else hi = mid - 1;
+    }
+    *qo = lo;
+    return ld_agent(&g.cand[(int64_t)lo * g.cap + (gi - cpre[lo])]);
+  };
+  const bool in_regs = C <= (uint32_t)SB * kCandPT;
+  uint32_t ck[kCandPT];
+  if (in_regs) {
+#pragma unroll
+    for (int k = 0; k < kCandPT; ++k) {
+      const uint32_t gi = (uint32_t)(tid + k * SB);
+      int q;
+      ck[k] = 0u;
+      if ((uint32_t)(k * SB) < C && gi < C) ck[k] = cand_at(gi, &q);
+    }
+  }
+  // local rounds 2 and 3 over the candidates
+  uint32_t prefix = v1 << 21, pmask = 0xFFE00000u, need = need1;
+  for (int round = 1; round < 3; ++round) {
+    const int shift = round == 1 ? 10 : 0;
+    const int nbins = round == 1 ? 2048 : 1024;
+    for (int i = tid; i < 2048; i += SB) sh.hist[i] = 0u;
+    __syncthreads();
+    if (in_regs) {
+#pragma unroll
+      for (int k = 0; k < kCandPT; ++k) {
+        const uint32_t c = ck[k];
+        if (c != 0u && (c & pmask) == prefix)
+          atomicAdd(&sh.hist[(c >> shift) & (uint32_t)(nbins - 1)], 1u);
+      }
+    } else {
+      for (uint32_t gi = tid; gi < C; gi += SB) {
+        int q;
+        const uint32_t c = cand_at(gi, &q);
+        if (c != 0u && (c & pmask) == prefix)
+          atomicAdd(&sh.hist[(c >> shift) & (uint32_t)(nbins - 1)], 1u);
+      }
+    }
+    __syncthreads();
+    uint32_t gt;
+    const uint32_t v = find_digit(sh, nbins, need, &gt);
+    need -= min(need, gt);
+    prefix |= v << shift;
+    pmask |= (uint32_t)(nbins - 1) << shift;
+  }
+  const uint32_t tau = prefix;
+  *tau_out = tau;
+  // Per-workgroup counts of candidates above / equal to tau. Candidates are
+  // laid out in workgroup order, so the lanes of a wave see one or two
+  // workgroups: aggregate with ballots, one LDS atomic per workgroup seen.
+  auto tally = [&](uint32_t gi, uint32_t c, bool valid) {
+    const bool isgt = valid && c > tau, iseq = valid && c == tau;
+    int q = 0;
+    if (isgt || iseq) {
+      int lo = 0, hi = P - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cpre[mid] <= gi) lo = mid; else hi = mid - 1;
+      }
+      q = lo;
+    }
+    uint64_t pend = __ballot(isgt || iseq);
+    while (pend) {
+      const int leader = __builtin_ctzll(pend);
+      const int qq = __shfl(q, leader, 64);
+      const uint64_t same = __ballot((isgt || iseq) && q == qq);
+      const uint32_t ngt = (uint32_t)__popcll(__ballot(isgt && q == qq));
+      const uint32_t neq = (uint32_t)__popcll(__ballot(iseq && q == qq));
+      if (lane_id() == leader) {
+        if (ngt) atomicAdd(&s_qcnt[3 * P + 1 + qq], ngt);
+        if (neq) atomicAdd(&s_qcnt[4 * P + 1 + qq], neq);
+      }
+      pend &= ~same;
+    }
+  };
+  if (in_regs) {
+#pragma unroll
+    for (int k = 0; k < kCandPT; ++k) {
+      const uint32_t gi = (uint32_t)(tid + k * SB);
+      if ((uint32_t)(k * SB) < C) tally(gi, ck[k], gi < C && ck[k] >= tau);
+    }
+  } else {
+    for (uint32_t base = 0; base < C; base += SB) {
+      const uint32_t gi = base + tid;
+      int q;
+      const uint32_t c = (gi < C) ? cand_at(gi, &q) : 0u;
+      tally(gi, c, gi < C && c >= tau);
+    }
+  }
+  __syncthreads();
+  uint32_t off_gt = 0, off_eq = 0;
+  for (int q = 0; q < g.p; ++q) {
+    off_gt += s_qcnt[q] + s_qcnt[3 * P + 1 + q];
+    off_eq += s_qcnt[4 * P + 1 + q];
+  }
+  const uint32_t tg = tna + s_qcnt[3 * P + 1 + g.p];
+  const uint32_t te = s_qcnt[4 * P + 1 + g.p];
+  __syncthreads();
+
+  uint64_t gt_bits = 0, eq_bits = 0;
+#pragma unroll
+  for (int j = 0; j < SPT; ++j) {
+    const uint32_t k = key[j];
+    if (k > tau) gt_bits |= 1ull << j;
+    else if (k == tau && k != 0u) eq_bits |= 1ull << j;
+  }
+  // see radix_select for why this is written without a guarded subtraction
+  const uint32_t eq_before = min(need, off_eq);
+  const uint32_t rem = need - eq_before;
+  const uint32_t take = min(rem, te);
+  *offset = off_gt + eq_before;
+  *count = tg + take;
+  uint64_t sel = gt_bits;
+  if (take == te) {
+    sel |= eq_bits;
+  } else if (take > 0) {
+    uint64_t keep = 0;
+    ordered_ranks<SPT>(eq_bits, sh, [&](int j, uint32_t r) {
+      if (r < take) keep |= 1ull << j;
+    });
+    sel |= keep;
+  }
+  return sel;
+}
+
 // Returns this thread's selection bitmask; *offset / *count give the block's
 // output range in the row's ascending selection list, *tau the threshold key.
+// With P > 1 this is radix_select_coop; s_qcnt is LDS scratch of >= 5P+1 words.
 template <int SPT>
-__device__ uint64_t radix_select(const uint32_t (&key)[SPT], uint32_t m, SelShared& sh,
+__device__ __forceinline__ uint64_t radix_select(const uint32_t (&key)[SPT], uint32_t m, SelShared& sh,
                                  const SelGroup& g, uint32_t* offset, uint32_t* count,
-                                 uint32_t* tau_out) {
+                                 uint32_t* tau_out, uint32_t* s_qcnt) {
+  if (g.P > 1) return radix_select_coop<SPT>(key, m, sh, g, offset, count, tau_out, s_qcnt);
   const int tid = threadIdx.x;
   uint32_t prefix = 0, pmask = 0, need = m;
   for (int round = 0; round < 3; ++round) {
@@ -84,43 +328,8 @@ __device__ uint64_t radix_select(const uint32_t (&key)[SPT], uint32_t m, SelShar
       if (k != 0u && (k & pmask) == prefix) atomicAdd(&sh.hist[(k >> shift) & (uint32_t)(nbins - 1)], 1u);
     }
     __syncthreads();
-    if (g.P > 1) {
-      uint32_t* gh = g.ghist + round * 2048;
-      for (int i = tid; i < nbins; i += SB) {
-        const uint32_t c = sh.hist[i];
-        if (c) atomicAdd(&gh[i], c);
-      }
-      group_barrier(g.bar, (uint32_t)g.P * (round + 1), g.err);
-      for (int i = tid; i < nbins; i += SB) sh.hist[i] = ld_agent(&gh[i]);
-      __syncthreads();
-    }
-    // Find digit v with  #(digit > v) < need <= #(digit >= v).
-    const int bpt = nbins / SB;
-    uint32_t loc = 0;
-    for (int i = 0; i < bpt; ++i) loc += sh.hist[tid * bpt + i];
-    sh.scan[SB - 1 - tid] = loc;  // reversed order: a prefix scan gives suffix sums
-    if (tid == 0) { sh.bcast[0] = 0u; sh.bcast[1] = 0u; sh.bcast[2] = 0u; }
-    __syncthreads();
-    const uint32_t rv = sh.scan[tid];
-    uint32_t tot;
-    const uint32_t above = block_excl_scan<SNW>(rv, sh.tmp, &tot);
-    const int o = SB - 1 - tid;
-    if (above < need && above + rv >= need) {
-      uint32_t run = above;
-      for (int i = bpt - 1; i >= 0; --i) {
-        const uint32_t c = sh.hist[o * bpt + i];
-        if (run + c >= need) {
-          sh.bcast[0] = (uint32_t)(o * bpt + i);
-          sh.bcast[1] = run;
-          sh.bcast[2] = c;
-          break;
-        }
-        run += c;
-      }
-    }
-    __syncthreads();
-    const uint32_t v = sh.bcast[0], gt = sh.bcast[1];
-    __syncthreads();
+    uint32_t gt;
+    const uint32_t v = find_digit(sh, nbins, need, &gt);
     need -= min(need, gt);
     prefix |= v << shift;
     pmask |= (uint32_t)(nbins - 1) << shift;
@@ -139,28 +348,7 @@ __device__ uint64_t radix_select(const uint32_t (&key)[SPT], uint32_t m, SelShar
   uint32_t tg, te;
   (void)block_excl_scan<SNW>(cg, sh.tmp, &tg);
   (void)block_excl_scan<SNW>(ce, sh.tmp, &te);
-  uint32_t off_gt = 0, off_eq = 0;
-  if (g.P > 1) {
-    if (tid == 0) {
-      st_agent(&g.xchg[2 * g.p], tg);
-      st_agent(&g.xchg[2 * g.p + 1], te);
-    }
-    group_barrier(g.bar, (uint32_t)g.P * 4u, g.err);
-    if (tid < 64) {
-      uint32_t a = 0, b = 0;
-      for (int q = tid; q < g.p; q += 64) {
-        a += ld_agent(&g.xchg[2 * q]);
-        b += ld_agent(&g.xchg[2 * q + 1]);
-      }
-      a = wave_sum_u32(a);
-      b = wave_sum_u32(b);
-      if (tid == 0) { sh.bcast[4] = a; sh.bcast[5] = b; }
-    }
-    __syncthreads();
-    off_gt = sh.bcast[4];
-    off_eq = sh.bcast[5];
-    __syncthreads();
-  }
+  const uint32_t off_gt = 0, off_eq = 0;  // a single workgroup owns the row
   // Equal keys are handed out in element order: the blocks before this one
   // take min(need, off_eq) of them, this one takes the next min(rem, te).
   // Written without a subtraction guarded by a comparison: clang/LLVM tags

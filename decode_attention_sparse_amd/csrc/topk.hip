@@ -15,7 +15,8 @@ struct TopkArgs {
   int P, row0, nrows;
   int32_t* idx;
   float* thr;
-  uint32_t* ghist;  // [rows, 3, 2048]
+  uint32_t* ghist;  // [rows, 2048]
+  uint32_t* cand;   // [rows, P, chunk]
   uint32_t* xchg;   // [rows, P, 2]
   uint32_t* bar;    // [rows]
   uint32_t* err;
@@ -29,6 +30,7 @@ __global__ __launch_bounds__(256) void k_fill_zero(uint32_t* p, int64_t n) {
 template <int SPT>
 __global__ __launch_bounds__(SB) void k_topk(TopkArgs a) {
   __shared__ SelShared sh;
+  __shared__ uint32_t s_qcnt[5 * kTopkMaxP + 1];
   const int tid = threadIdx.x;
   const int L = xcd_tile(blockIdx.x, a.nrows * a.P);
   const int p = L % a.P;
@@ -45,12 +47,14 @@ __global__ __launch_bounds__(SB) void k_topk(TopkArgs a) {
   SelGroup grp;
   grp.P = a.P;
   grp.p = p;
-  grp.ghist = a.ghist + row * 3 * 2048;
+  grp.ghist = a.ghist + row * 2048;
   grp.xchg = a.xchg + row * a.P * 2;
   grp.bar = a.bar + row;
   grp.err = a.err;
+  grp.cand = a.cand + row * a.P * a.chunk;
+  grp.cap = a.chunk;
   uint32_t offset, count, tau;
-  const uint64_t sel = radix_select<SPT>(key, (uint32_t)a.k, sh, grp, &offset, &count, &tau);
+  const uint64_t sel = radix_select<SPT>(key, (uint32_t)a.k, sh, grp, &offset, &count, &tau, s_qcnt);
   int32_t* out = a.idx + row * a.k;
   ordered_ranks<SPT>(sel, sh, [&](int j, uint32_t r) {
     const int64_t pos = (int64_t)offset + r;
@@ -81,12 +85,13 @@ sdkv_status plan_topk(int64_t rows, int64_t n, int64_t k, TopkPlan* p) {
   q.spt = topk_spt(q.chunk);
   if (q.spt == 0) return SDKV_ERR_UNSUPPORTED;
   size_t off = 0;
-  q.off_ghist = off;  off += (q.P > 1) ? (size_t)rows * 3 * 2048 * 4 : 0;
+  q.off_ghist = off;  off += (q.P > 1) ? (size_t)rows * 2048 * 4 : 0;
   q.off_xchg = off;   off += (size_t)rows * q.P * 2 * 4;
   q.off_bar = off;    off += (size_t)rows * 4;
   q.off_err = off;    off += 4;
   q.zero_bytes = align_up(off, 256);
-  q.total = q.zero_bytes;
+  q.off_cand = q.zero_bytes;
+  q.total = q.off_cand + align_up(q.P > 1 ? (size_t)rows * q.P * q.chunk * 4 : 0, 256);
   *p = q;
   return SDKV_OK;
 }
@@ -118,6 +123,7 @@ sdkv_status launch_topk(const float* scores, int64_t ld, int32_t* idx, float* th
   a.xchg = (uint32_t*)(base + p.off_xchg);
   a.bar = (uint32_t*)(base + p.off_bar);
   a.err = (uint32_t*)(base + p.off_err);
+  a.cand = (uint32_t*)(base + p.off_cand);
   const void* kfn = pick_topk_kernel(p.spt);
   if (!kfn) return SDKV_ERR_UNSUPPORTED;
   int64_t batch = p.rows;
