@@ -279,6 +279,82 @@ def sdkv_decode_attn(q, dk, dv, key_codes, val_codes, *, klow: int, khigh: int,
     return out
 
 
+class DecodeCall:
+    """A decode-attention call whose arguments and workspace are marshalled
+    once; launch() then costs one C call. Keeps references to every tensor it
+    points at. Same arguments as sdkv_decode_attn (without debug outputs)."""
+
+    def __init__(self, q, dk, dv, key_codes, val_codes, *, klow: int, khigh: int,
+                 top_num: int = 1, top_den: int = 10, scale: Optional[float] = None,
+                 key_low=None, out=None, workspace: Optional[Workspace] = None, stream=None):
+        torch = _torch()
+        B, Hq, d = q.shape
+        if scale is None:
+            scale = 1.0 / math.sqrt(d)
+        if out is None:
+            out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+        self.out = out
+        self._keep = (q, dk, dv, key_codes, val_codes, key_low, out)
+        self.args = attn_args(q, dk, dv, key_codes, val_codes, klow, khigh, top_num, top_den,
+                              scale, out, key_low=key_low)
+        self.ws = workspace if workspace is not None else Workspace()
+        wp, wn = _ws(self.ws, decode_attn_workspace_bytes(self.args))
+        self._wsp, self._wsn = ctypes.c_void_p(wp), wn
+        self._stream = _stream(stream)
+        self._argp = ctypes.byref(self.args)
+        self._fn = _lib().sdkv_decode_attn
+        self._ev = None
+
+    def launch(self, stage_events=None):
+        if stage_events is not None:
+            self._ev, self.args.stage_events = _events(stage_events)
+        else:
+            self.args.stage_events = None
+        st = self._fn(self._argp, self._wsp, self._wsn, self._stream)
+        if st != SDKV_OK:
+            raise SdkvError(st, "sdkv_decode_attn")
+        return self.out
+
+
+class EncodeCall:
+    """An encode call marshalled once (see DecodeCall); codes int32 [n, K]."""
+
+    def __init__(self, x, dictionary, K: int, *, codes=None, resid_norm=None,
+                 workspace: Optional[Workspace] = None, stream=None):
+        torch = _torch()
+        n, d = x.shape
+        if codes is None:
+            codes = torch.empty((n, K), dtype=torch.int32, device=x.device)
+        self.codes, self.resid_norm = codes, resid_norm
+        self._keep = (x, dictionary, codes, resid_norm)
+        self.args = EncodeArgs(x=_dev(x, "x"), x_dtype=_dtype_code(x),
+                               dict=_dev(dictionary, "dictionary"),
+                               dict_dtype=_dtype_code(dictionary), n=n, d=d,
+                               n_atoms=dictionary.shape[0], K=K, codes=_dev(codes, "codes"),
+                               coef_f32=None, resid_norm=_dev(resid_norm, "resid_norm"),
+                               low_plane=None, klow=0)
+        nb = c_size_t(0)
+        _check(_lib().sdkv_encode_workspace(ctypes.byref(self.args), ctypes.byref(nb)),
+               "sdkv_encode_workspace")
+        self.ws = workspace if workspace is not None else Workspace()
+        wp, wn = _ws(self.ws, nb.value)
+        self._wsp, self._wsn = ctypes.c_void_p(wp), wn
+        self._stream = _stream(stream)
+        self._argp = ctypes.byref(self.args)
+        self._fn = _lib().sdkv_encode
+        self._ev = None
+
+    def launch(self, stage_events=None):
+        if stage_events is not None:
+            self._ev, self.args.stage_events = _events(stage_events)
+        else:
+            self.args.stage_events = None
+        st = self._fn(self._argp, self._wsp, self._wsn, self._stream)
+        if st != SDKV_OK:
+            raise SdkvError(st, "sdkv_encode")
+        return self.codes
+
+
 def sdkv_select_topk(scores, k: int, *, idx_out=None, thr_out=None,
                      workspace: Optional[Workspace] = None, stream=None):
     """Indices (int32, ascending) of the k largest entries of each row of the
@@ -309,4 +385,4 @@ def sdkv_select_topk(scores, k: int, *, idx_out=None, thr_out=None,
 
 __all__ = ["sdkv_encode", "sdkv_decode_attn", "sdkv_select_topk", "selected_count",
            "Workspace", "SdkvError", "lib", "LIB_PATH", "HEADER", "EncodeArgs", "AttnArgs",
-           "attn_args", "decode_attn_workspace_bytes"]
+           "attn_args", "decode_attn_workspace_bytes", "DecodeCall", "EncodeCall"]

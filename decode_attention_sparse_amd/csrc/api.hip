@@ -5,6 +5,8 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
+#include <vector>
 
 #include "sdkv_internal.h"
 
@@ -12,14 +14,39 @@ using namespace sdkv;
 
 namespace sdkv {
 
+// The co-residency capacity of a (kernel, block size, device) never changes,
+// so it is computed once and cached. This small mutex-guarded cache is the
+// library's only process-wide state.
+namespace {
+struct CapEntry {
+  const void* kernel;
+  int dev, threads, cap;
+};
+std::mutex g_cap_mu;
+std::vector<CapEntry> g_cap;
+}  // namespace
+
 sdkv_status coresident_blocks(const void* kernel, int threads, size_t dyn_lds, int* out) {
-  int dev = 0, cus = 0, per_cu = 0;
+  int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return SDKV_ERR_DEVICE;
+  if (dyn_lds == 0) {
+    std::lock_guard<std::mutex> lk(g_cap_mu);
+    for (const CapEntry& e : g_cap)
+      if (e.kernel == kernel && e.dev == dev && e.threads == threads) {
+        *out = e.cap;
+        return SDKV_OK;
+      }
+  }
+  int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return SDKV_ERR_DEVICE;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, dyn_lds) != hipSuccess)
     return SDKV_ERR_DEVICE;
   *out = cus * per_cu;
+  if (dyn_lds == 0) {
+    std::lock_guard<std::mutex> lk(g_cap_mu);
+    g_cap.push_back(CapEntry{kernel, dev, threads, *out});
+  }
   return SDKV_OK;
 }
 

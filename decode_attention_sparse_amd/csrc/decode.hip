@@ -120,6 +120,8 @@ struct RowsArgs {
   uint32_t* xchg;           // [rows, P, 2]
   uint32_t* bar;            // [rows]
   uint32_t* err;
+  uint32_t* ticket;         // workgroup start-order counter, zeroed per call
+  int xcd_map;              // map tickets to rows XCD-locally
 };
 
 constexpr int kTokBatch = 4;   // selected tokens per thread per load batch
@@ -150,7 +152,16 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   __shared__ uint32_t s_qcnt[5 * kMaxRowP + 1];
 
   const int tid = threadIdx.x;
-  const int L = xcd_tile(blockIdx.x, a.nrows * a.P);
+  // Work is assigned in workgroup start order (a ticket), not by block id:
+  // every workgroup of a row then holds a ticket within a window of 8P, so
+  // the earliest unfinished row always has all its workgroups resident once
+  // earlier rows retire -- the row barriers cannot deadlock without a
+  // cooperative launch (the host checks that the window fits the device).
+  __shared__ uint32_t s_ticket;
+  if (tid == 0) s_ticket = atomicAdd(a.ticket, 1u);
+  __syncthreads();
+  const int nb = a.nrows * a.P;
+  const int L = a.xcd_map ? xcd_tile((int)s_ticket, nb) : (int)s_ticket;
   const int p = L % a.P;
   const int row = a.row0 + L / a.P;
   const int b = row / a.Hq, h = row % a.Hq, g = h / a.G;
@@ -442,7 +453,51 @@ __device__ __forceinline__ void wdv_merge16(const WdvArgs& a, const float* s_coe
   }
 }
 
-__global__ __launch_bounds__(256) void k_wdv_bf16(WdvArgs a) {
+// 8 merged weights W[row][a0 .. a0+8) (zero outside the matrix); all loads of
+// up to 8 partials are issued before the multiply-adds.
+__device__ __forceinline__ void wdv_merge8(const WdvArgs& a, const float* s_coef, int r, int row,
+                                           int a0, float (&v)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = 0.f;
+  if (row >= a.rows) return;
+  const float* src = a.wpart + (int64_t)row * a.P * a.N + a0;
+  if (a0 + 8 <= a.N && (a.N & 3) == 0) {
+    for (int q0 = 0; q0 < a.P; q0 += 8) {
+      float4 x[8][2];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (q0 + q < a.P) {
+          const float4* sp = (const float4*)(src + (int64_t)(q0 + q) * a.N);
+          x[q][0] = sp[0];
+          x[q][1] = sp[1];
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (q0 + q < a.P) {
+          const float c = s_coef[r * kMaxRowP + q0 + q];
+          v[0] = fmaf(c, x[q][0].x, v[0]); v[1] = fmaf(c, x[q][0].y, v[1]);
+          v[2] = fmaf(c, x[q][0].z, v[2]); v[3] = fmaf(c, x[q][0].w, v[3]);
+          v[4] = fmaf(c, x[q][1].x, v[4]); v[5] = fmaf(c, x[q][1].y, v[5]);
+          v[6] = fmaf(c, x[q][1].z, v[6]); v[7] = fmaf(c, x[q][1].w, v[7]);
+        }
+      }
+    }
+  } else {
+    for (int q = 0; q < a.P; ++q) {
+      const float c = s_coef[r * kMaxRowP + q];
+      for (int e = 0; e < 8 && a0 + e < a.N; ++e) v[e] = fmaf(c, src[(int64_t)q * a.N + e], v[e]);
+    }
+  }
+  if (a.w_out) {
+    float* wo = a.w_out + (int64_t)row * a.N + a0;
+    for (int e = 0; e < 8 && a0 + e < a.N; ++e) wo[e] = v[e];
+  }
+}
+
+// 512 threads: the A tile (32 rows x 128 atoms) is merged 8 atoms per thread;
+// wave w computes output columns [16w, 16w+16) for both 16-row tiles.
+__global__ __launch_bounds__(512) void k_wdv_bf16(WdvArgs a) {
   __shared__ float s_coef[WRT * kMaxRowP];
   __shared__ __attribute__((aligned(16))) uint16_t s_ahi[WRT * WPITCH];
   __shared__ __attribute__((aligned(16))) uint16_t s_alo[WRT * WPITCH];
@@ -452,26 +507,34 @@ __global__ __launch_bounds__(256) void k_wdv_bf16(WdvArgs a) {
   const int L = xcd_tile(blockIdx.x, a.nchunks * a.nrt);
   const int chunk = L / a.nrt, rt = L % a.nrt;
   const int r0 = rt * WRT;
-  wdv_coefs(a, r0, s_coef);
+  for (int r = w; r < WRT; r += 8) {
+    const int row = r0 + r;
+    float Mq = -INFINITY, lq = 0.f;
+    if (row < a.rows && l < a.P) {
+      const float2 st = a.stats[(int64_t)row * a.P + l];
+      Mq = st.x;
+      lq = st.y;
+    }
+    const float Mx = wave_max(Mq);
+    const float c = (lq > 0.f) ? __expf(Mq - Mx) : 0.f;
+    const float Lr = wave_sum(c * lq);
+    if (l < a.P) s_coef[r * kMaxRowP + l] = (Lr > 0.f) ? c / Lr : 0.f;
+  }
   __syncthreads();
   const uint16_t* dv = (const uint16_t*)a.dv;
   const int ncol = a.d >> 4;
-  f32x4 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 
   for (int sub = 0; sub < a.nsub; ++sub) {
     const int a0 = (chunk * a.nsub + sub) * WSUB;
     if (a0 >= a.N) break;
-    // A: 32 rows x 128 atoms of merged W, split into bf16 hi + lo
+    // A: merged weights, split into bf16 hi + lo
     {
-      const int r = tid >> 3, c0 = (tid & 7) * 16;
-      float v[16];
-      wdv_merge16(a, s_coef, r, r0 + r, a0 + c0, v);
+      const int r = tid >> 4, c0 = (tid & 15) * 8;
+      float v[8];
+      wdv_merge8(a, s_coef, r, r0 + r, a0 + c0, v);
 #pragma unroll
-      for (int e = 0; e < 16; e += 2) {
+      for (int e = 0; e < 8; e += 2) {
         const uint32_t h0 = f32_to_bf16_rne(v[e]), h1 = f32_to_bf16_rne(v[e + 1]);
         const uint32_t l0 = f32_to_bf16_rne(v[e] - __uint_as_float(h0 << 16));
         const uint32_t l1 = f32_to_bf16_rne(v[e + 1] - __uint_as_float(h1 << 16));
@@ -480,7 +543,7 @@ __global__ __launch_bounds__(256) void k_wdv_bf16(WdvArgs a) {
       }
     }
     // B: Dv rows a0..a0+127 transposed to [dim][atom pair]
-    for (int it = tid; it < (WSUB / 2) * (a.d >> 3); it += 256) {
+    for (int it = tid; it < (WSUB / 2) * (a.d >> 3); it += 512) {
       const int ap = it % (WSUB / 2), sg = it / (WSUB / 2);
       const int atom = a0 + 2 * ap;
       u32x4 x0 = u32x4{0u, 0u, 0u, 0u}, x1 = u32x4{0u, 0u, 0u, 0u};
@@ -493,38 +556,30 @@ __global__ __launch_bounds__(256) void k_wdv_bf16(WdvArgs a) {
       }
     }
     __syncthreads();
-    // MFMA: wave w owns output columns [32w, 32w+32), both 16-row tiles
-    if (2 * w < ncol) {
+    if (w < ncol) {
 #pragma unroll
       for (int ks = 0; ks < WSUB / 32; ++ks) {
         const int kk = ks * 32 + 8 * (l >> 4);
-        const int n0 = 32 * w + (l & 15);
-        const u32x4 b0 = *(const u32x4*)(s_bt + n0 * BPITCH + (kk >> 1));
-        const u32x4 b1 = *(const u32x4*)(s_bt + (n0 + 16) * BPITCH + (kk >> 1));
+        const u32x4 b0 = *(const u32x4*)(s_bt + (16 * w + (l & 15)) * BPITCH + (kk >> 1));
 #pragma unroll
         for (int rr = 0; rr < 2; ++rr) {
           const u32x4 ah = *(const u32x4*)(s_ahi + (rr * 16 + (l & 15)) * WPITCH + kk);
           const u32x4 al = *(const u32x4*)(s_alo + (rr * 16 + (l & 15)) * WPITCH + kk);
-          acc[rr][0] = mfma_bf16(ah, b0, acc[rr][0]);
-          acc[rr][0] = mfma_bf16(al, b0, acc[rr][0]);
-          acc[rr][1] = mfma_bf16(ah, b1, acc[rr][1]);
-          acc[rr][1] = mfma_bf16(al, b1, acc[rr][1]);
+          acc[rr] = mfma_bf16(ah, b0, acc[rr]);
+          acc[rr] = mfma_bf16(al, b0, acc[rr]);
         }
       }
     }
     __syncthreads();
   }
-  if (2 * w < ncol) {
+  if (w < ncol) {
     float* dst = a.opart + (int64_t)chunk * a.rows * a.d;
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = r0 + rr * 16 + 4 * (l >> 4) + i;
-        if (row < a.rows) {
-          dst[(int64_t)row * a.d + 32 * w + (l & 15)] = acc[rr][0][i];
-          if (2 * w + 1 < ncol) dst[(int64_t)row * a.d + 32 * w + 16 + (l & 15)] = acc[rr][1][i];
-        }
+        if (row < a.rows) dst[(int64_t)row * a.d + 16 * w + (l & 15)] = acc[rr][i];
       }
   }
 }
@@ -647,6 +702,7 @@ sdkv_status plan_decode(const sdkv_attn_args* a, DecodePlan* p) {
   q.off_xchg = off;   off += (size_t)rows * q.P * 2 * 4;
   q.off_bar = off;    off += (size_t)rows * 4;
   q.off_err = off;    off += 4;
+  q.off_ticket = off; off += 4;
   off = align_up(off, A);
   q.zero_bytes = off - q.off_zero;
   q.off_opart = off;  off = align_up(off + (size_t)q.nchunks * rows * a->d * 4, A);
@@ -740,26 +796,24 @@ sdkv_status launch_decode(const sdkv_attn_args* a, const DecodePlan& p, void* ws
   const bool aligned = (((uintptr_t)a->key_codes | (uintptr_t)a->val_codes) & 15u) == 0;
   const void* kfn = pick_rows_kernel(p.spt, p.fast && aligned);
   if (!kfn) return SDKV_ERR_UNSUPPORTED;
-  int64_t batch = rows;
+  ra.ticket = (uint32_t*)(base + p.off_ticket);
+  ra.xcd_map = 0;
   if (p.P > 1) {
+    // a row's workgroups hold tickets within a window of 8P (XCD-local
+    // mapping) or P; that window must fit the co-resident capacity
     int cap = 0;
     sdkv_status st = coresident_blocks(kfn, SB, 0, &cap);
     if (st != SDKV_OK) return st;
-    batch = std::min<int64_t>(rows, cap / p.P);
-    if (batch < 1) return SDKV_ERR_UNSUPPORTED;
+    if (cap < p.P) return SDKV_ERR_UNSUPPORTED;
+    ra.xcd_map = (16 * p.P <= cap) ? 1 : 0;
   }
   if (!record_stage(ev, 1, stream)) return SDKV_ERR_DEVICE;
-  for (int64_t r0 = 0; r0 < rows; r0 += batch) {
-    ra.row0 = (int)r0;
-    ra.nrows = (int)std::min<int64_t>(batch, rows - r0);
-    const dim3 grid((unsigned)(ra.nrows * p.P)), block(SB);
+  {
+    ra.row0 = 0;
+    ra.nrows = (int)rows;
+    const dim3 grid((unsigned)(rows * p.P)), block(SB);
     void* args[] = {&ra};
-    hipError_t e;
-    if (p.P > 1)
-      e = hipLaunchCooperativeKernel(kfn, grid, block, args, 0, stream);
-    else
-      e = hipLaunchKernel(kfn, grid, block, args, 0, stream);
-    if (e != hipSuccess) return SDKV_ERR_DEVICE;
+    if (hipLaunchKernel(kfn, grid, block, args, 0, stream) != hipSuccess) return SDKV_ERR_DEVICE;
   }
 
   // 3. contract the value weights with Dv
@@ -779,7 +833,7 @@ sdkv_status launch_decode(const sdkv_attn_args* a, const DecodePlan& p, void* ws
   const dim3 wgrid((unsigned)(p.nchunks * p.nrt));
   if (!record_stage(ev, 2, stream)) return SDKV_ERR_DEVICE;
   if (a->dict_dtype == SDKV_BF16)
-    hipLaunchKernelGGL(k_wdv_bf16, wgrid, dim3(256), 0, stream, wa);
+    hipLaunchKernelGGL(k_wdv_bf16, wgrid, dim3(512), 0, stream, wa);
   else
     hipLaunchKernelGGL(k_wdv_f32, wgrid, dim3(256), 0, stream, wa);
   if (hipGetLastError() != hipSuccess) return SDKV_ERR_DEVICE;

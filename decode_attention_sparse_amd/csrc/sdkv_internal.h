@@ -11,9 +11,7 @@
 namespace sdkv {
 
 // Planning assumes an MI355X: 256 compute units. The same plan (and so the
-// same workspace size) is used on any device; the launch code splits a
-// cooperative grid into smaller row batches if the device holds fewer
-// co-resident workgroups.
+// same workspace size) is used on any device.
 constexpr int kPlanCUs = 256;
 constexpr int kRowThreads = 512;
 constexpr int kMaxSPT = 64;                                // keys per thread
@@ -37,7 +35,7 @@ struct DecodePlan {
   size_t off_u = 0, off_sel = 0, off_shigh = 0, off_wpart = 0, off_stats = 0;
   size_t off_zero = 0, zero_bytes = 0;  // [ghist | xchg | bar | err], cleared per call
   size_t off_ghist = 0, off_xchg = 0, off_bar = 0, off_err = 0, off_opart = 0;
-  size_t off_cand = 0;
+  size_t off_cand = 0, off_ticket = 0;
   size_t total = 0;
 };
 
@@ -51,7 +49,7 @@ struct TopkPlan {
   int64_t chunk = 0;
   int spt = 0;
   size_t off_ghist = 0, off_xchg = 0, off_bar = 0, off_err = 0, zero_bytes = 0;
-  size_t off_cand = 0;
+  size_t off_cand = 0, off_ticket = 0;
   size_t total = 0;
 };
 sdkv_status plan_topk(int64_t rows, int64_t n, int64_t k, TopkPlan* p);

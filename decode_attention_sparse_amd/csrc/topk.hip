@@ -20,6 +20,8 @@ struct TopkArgs {
   uint32_t* xchg;   // [rows, P, 2]
   uint32_t* bar;    // [rows]
   uint32_t* err;
+  uint32_t* ticket; // workgroup start-order counter (see k_rows)
+  int xcd_map;
 };
 
 __global__ __launch_bounds__(256) void k_fill_zero(uint32_t* p, int64_t n) {
@@ -32,7 +34,12 @@ __global__ __launch_bounds__(SB) void k_topk(TopkArgs a) {
   __shared__ SelShared sh;
   __shared__ uint32_t s_qcnt[5 * kTopkMaxP + 1];
   const int tid = threadIdx.x;
-  const int L = xcd_tile(blockIdx.x, a.nrows * a.P);
+  // rows are assigned in workgroup start order, as in the decode row kernel
+  __shared__ uint32_t s_ticket;
+  if (tid == 0) s_ticket = atomicAdd(a.ticket, 1u);
+  __syncthreads();
+  const int nb = a.nrows * a.P;
+  const int L = a.xcd_map ? xcd_tile((int)s_ticket, nb) : (int)s_ticket;
   const int p = L % a.P;
   const int64_t row = a.row0 + L / a.P;
   const int64_t t0 = (int64_t)p * a.chunk;
@@ -89,6 +96,7 @@ sdkv_status plan_topk(int64_t rows, int64_t n, int64_t k, TopkPlan* p) {
   q.off_xchg = off;   off += (size_t)rows * q.P * 2 * 4;
   q.off_bar = off;    off += (size_t)rows * 4;
   q.off_err = off;    off += 4;
+  q.off_ticket = off; off += 4;
   q.zero_bytes = align_up(off, 256);
   q.off_cand = q.zero_bytes;
   q.total = q.off_cand + align_up(q.P > 1 ? (size_t)rows * q.P * q.chunk * 4 : 0, 256);
@@ -126,24 +134,28 @@ sdkv_status launch_topk(const float* scores, int64_t ld, int32_t* idx, float* th
   a.cand = (uint32_t*)(base + p.off_cand);
   const void* kfn = pick_topk_kernel(p.spt);
   if (!kfn) return SDKV_ERR_UNSUPPORTED;
-  int64_t batch = p.rows;
+  a.xcd_map = 0;
   if (p.P > 1) {
     int cap = 0;
     sdkv_status st = coresident_blocks(kfn, SB, 0, &cap);
     if (st != SDKV_OK) return st;
-    batch = std::min<int64_t>(p.rows, cap / p.P);
-    if (batch < 1) return SDKV_ERR_UNSUPPORTED;
+    if (cap < p.P) return SDKV_ERR_UNSUPPORTED;
+    a.xcd_map = (16 * p.P <= cap) ? 1 : 0;
   }
-  // rows per launch also bounded so the grid size fits an int
-  batch = std::min<int64_t>(batch, (int64_t)1 << 20);
+  a.ticket = (uint32_t*)(base + p.off_ticket);
+  // rows per launch bounded so the grid size fits an int; every launch gets
+  // a fresh ticket range, so the ticket is cleared before each one
+  const int64_t batch = std::max<int64_t>(1, std::min<int64_t>(p.rows, ((int64_t)1 << 30) / p.P));
   for (int64_t r0 = 0; r0 < p.rows; r0 += batch) {
+    if (r0 > 0) {
+      hipLaunchKernelGGL(k_fill_zero, dim3(1), dim3(64), 0, stream, a.ticket, (int64_t)1);
+      if (hipGetLastError() != hipSuccess) return SDKV_ERR_DEVICE;
+    }
     a.row0 = (int)r0;
     a.nrows = (int)std::min<int64_t>(batch, p.rows - r0);
     void* args[] = {&a};
     const dim3 grid((unsigned)(a.nrows * p.P)), block(SB);
-    hipError_t e = (p.P > 1) ? hipLaunchCooperativeKernel(kfn, grid, block, args, 0, stream)
-                             : hipLaunchKernel(kfn, grid, block, args, 0, stream);
-    if (e != hipSuccess) return SDKV_ERR_DEVICE;
+    if (hipLaunchKernel(kfn, grid, block, args, 0, stream) != hipSuccess) return SDKV_ERR_DEVICE;
   }
   return SDKV_OK;
 }

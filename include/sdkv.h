@@ -23,8 +23,9 @@
  *    is written. Kernel launch failures are reported as SDKV_ERR_DEVICE
  *    (faults inside an already-enqueued kernel surface at the caller's next
  *    synchronisation, as for any HIP kernel). No C++ exception crosses the
- *    ABI. The library keeps no mutable global state (calls are reentrant);
- *    two calls that share a workspace must not overlap in time.
+ *    ABI. Calls are reentrant and thread-safe (the only process-wide state
+ *    is a mutex-guarded cache of per-device kernel occupancy); two calls
+ *    that share a workspace must not overlap in time.
  *  - Inputs must be finite. Code indices must be < n_atoms; other indices
  *    give unspecified (but in-bounds) results.
  */
