@@ -11,8 +11,9 @@
 //   k_utable_*   U = scale * Q Dk^T for every (batch, query head)   [MFMA bf16]
 //   k_rows       per (batch, query head) and token chunk: U row staged in
 //                LDS; s_low for every token of the chunk kept in registers;
-//                exact top-m radix select (cooperative across the row's
-//                chunks); Khigh rescore of the selected tokens; softmax
+//                exact top-m select (one synchronisation of the row's
+//                chunks around a shared sample's quantile window, or a
+//                two-synchronisation radix select); Khigh rescore of the selected tokens; softmax
 //                partials and per-atom value weights accumulated in LDS.
 //   k_wdv_*      merge the per-chunk softmax partials and contract the value
 //                weights with Dv: out = W Dv                       [MFMA bf16]
@@ -124,8 +125,12 @@ struct RowsArgs {
   int xcd_map;              // map tickets to rows XCD-locally
 };
 
-constexpr int kTokBatch = 4;   // selected tokens per thread per load batch
-constexpr int kListCap = 3456; // selected tokens per workgroup kept in LDS
+struct Words3 {
+  uint32_t x, y, z;
+};
+
+constexpr int kTokBatch = 2;   // selected tokens per thread per load batch
+constexpr int kListCap = 3072; // selected tokens per workgroup kept in LDS
 
 // Loads the first `nw` words of a code record (record length K words).
 // FAST: K == 16, the record is 64-byte aligned and read as 4 x 16 bytes.
@@ -142,11 +147,78 @@ __device__ __forceinline__ void load_record(const uint32_t* rec, int K, int nw, 
   }
 }
 
+// U row of `row` into LDS. All loads are issued before the first store
+// (stores go to clamped indices: a duplicate store writes the same value).
+__device__ __forceinline__ void stage_u(const RowsArgs& a, int row, float* s_u) {
+  const int tid = threadIdx.x;
+  const float4* src4 = (const float4*)(a.U + (int64_t)row * a.N);
+  const int n4 = a.N >> 2;
+  constexpr int UPT = kMaxAtomsDecode / 4 / SB;
+  if (n4 > 0) {
+    float4 ub[UPT];
+#pragma unroll
+    for (int k = 0; k < UPT; ++k) ub[k] = src4[min(tid + k * SB, n4 - 1)];
+#pragma unroll
+    for (int k = 0; k < UPT; ++k) ((float4*)s_u)[min(tid + k * SB, n4 - 1)] = ub[k];
+  }
+  for (int i = (n4 << 2) + tid; i < a.N; i += SB) s_u[i] = a.U[(int64_t)row * a.N + i];
+}
+
+// U row staging and low scores of a chunk for records of 16 words whose
+// first min(klow, 4) words score the token (klow <= 4). The U loads are
+// issued with the first token batch; token batches are double-buffered (the
+// next batch is requested before the current one is scored). LOW3: klow == 3,
+// each token's three words are one 12-byte load.
+template <int SPT, bool LOW3>
+__device__ __forceinline__ void score_chunk(const RowsArgs& a, int row, const uint32_t* lo,
+                                            int64_t t0, int64_t t1, float* s_u,
+                                            uint32_t (&key)[SPT]) {
+  const int tid = threadIdx.x;
+  const int lw = a.low_words;
+  constexpr int AMASK = kMaxAtomsDecode - 1;
+  constexpr int JB = SPT < 8 ? SPT : 8;
+  constexpr int NBATCH = SPT / JB;
+  static_assert(SPT % JB == 0, "token batches must tile the chunk");
+  uint32_t wb[2][JB][4];
+  auto load_batch = [&](int jb, uint32_t (&w)[JB][4]) {
+#pragma unroll
+    for (int jj = 0; jj < JB; ++jj) {
+      const int64_t t = min(t0 + (int64_t)(jb + jj) * SB + tid, a.T - 1);
+      const uint32_t* wp = lo + t * lw;
+      if (LOW3) {
+        const Words3 v = *(const Words3*)wp;
+        w[jj][0] = v.x; w[jj][1] = v.y; w[jj][2] = v.z; w[jj][3] = 0u;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[jj][i] = wp[min(i, a.klow - 1)];
+      }
+    }
+  };
+  load_batch(0, wb[0]);
+  stage_u(a, row, s_u);
+  __syncthreads();
+  const int nk = LOW3 ? 3 : a.klow;
+#pragma unroll
+  for (int bt = 0; bt < NBATCH; ++bt) {
+    if (bt + 1 < NBATCH) load_batch((bt + 1) * JB, wb[(bt + 1) & 1]);
+#pragma unroll
+    for (int jj = 0; jj < JB; ++jj) {
+      const uint32_t (&wd)[4] = wb[bt & 1][jj];
+      const int64_t t = t0 + (int64_t)(bt * JB + jj) * SB + tid;
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i < nk) s = fmaf(code_coef(wd[i]), s_u[code_idx(wd[i]) & AMASK], s);
+      key[bt * JB + jj] = (t < t1) ? float_key(s) : 0u;
+    }
+  }
+}
+
 template <int SPT, bool FAST>
 __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   __shared__ float s_u[kMaxAtomsDecode];
   __shared__ SelShared sh;
-  __shared__ float s_red[16];
+  __shared__ float s_red[SNW];
   __shared__ uint16_t s_lt[kListCap];
   __shared__ float s_ls[kListCap];
   __shared__ uint32_t s_qcnt[5 * kMaxRowP + 1];
@@ -170,57 +242,36 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   const int64_t t1 = min(a.T, t0 + a.chunk);
   constexpr int AMASK = kMaxAtomsDecode - 1;
 
-  // 1. stage this query head's U row in LDS
-  {
-    const float* src = a.U + (int64_t)row * a.N;
-    const int n4 = a.N >> 2;
-    for (int i = tid; i < n4; i += SB) ((float4*)s_u)[i] = ((const float4*)src)[i];
-    for (int i = (n4 << 2) + tid; i < a.N; i += SB) s_u[i] = src[i];
-  }
-  __syncthreads();
-
-  // 2. s_low of every token in the chunk -> order-preserving keys. Loads are
-  // issued for 8 tokens at a time from clamped (always valid) addresses.
+  // 1. this query head's U row into LDS and 2. s_low of every token of the
+  // chunk as order-preserving keys
+  const uint32_t* lo = a.low + kv * a.T * a.low_words;
+  const int lw = a.low_words;
+  const bool low3 = FAST && a.klow == 3;
   uint32_t key[SPT];
-  {
-    const uint32_t* lo = a.low + kv * a.T * a.low_words;
-    const int lw = a.low_words;
+  if (FAST) {
+    if (low3) score_chunk<SPT, true>(a, row, lo, t0, t1, s_u, key);
+    else score_chunk<SPT, false>(a, row, lo, t0, t1, s_u, key);
+  } else {
+    stage_u(a, row, s_u);
+    __syncthreads();
 #pragma unroll
-    for (int jb = 0; jb < SPT; jb += 8) {
-      if (FAST) {
-        uint32_t wd[8][4];
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const int64_t t = min(t0 + (int64_t)(jb + jj) * SB + tid, a.T - 1);
-          const uint32_t* wp = lo + t * lw;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) wd[jj][i] = wp[min(i, a.klow - 1)];
-        }
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const int64_t t = t0 + (int64_t)(jb + jj) * SB + tid;
-          float s = 0.f;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (i < a.klow) s = fmaf(code_coef(wd[jj][i]), s_u[code_idx(wd[jj][i]) & AMASK], s);
-          key[jb + jj] = (t < t1) ? float_key(s) : 0u;
-          if (a.s_low_out && t < t1) a.s_low_out[(int64_t)row * a.T + t] = s;
-        }
-      } else {
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const int64_t t = t0 + (int64_t)(jb + jj) * SB + tid;
-          key[jb + jj] = 0u;
-          if (t < t1) {
-            const uint32_t* wp = lo + t * lw;
-            float s = 0.f;
-            for (int i = 0; i < a.klow; ++i)
-              s = fmaf(code_coef(wp[i]), s_u[code_idx(wp[i]) & AMASK], s);
-            key[jb + jj] = float_key(s);
-            if (a.s_low_out) a.s_low_out[(int64_t)row * a.T + t] = s;
-          }
-        }
+    for (int j = 0; j < SPT; ++j) {
+      const int64_t t = t0 + (int64_t)j * SB + tid;
+      key[j] = 0u;
+      if (t < t1) {
+        const uint32_t* wp = lo + t * lw;
+        float s = 0.f;
+        for (int i = 0; i < a.klow; ++i)
+          s = fmaf(code_coef(wp[i]), s_u[code_idx(wp[i]) & AMASK], s);
+        key[j] = float_key(s);
       }
+    }
+  }
+  if (a.s_low_out) {
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) {
+      const int64_t t = t0 + (int64_t)j * SB + tid;
+      if (t < t1) a.s_low_out[(int64_t)row * a.T + t] = key_float(key[j]);
     }
   }
 
@@ -235,7 +286,48 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   grp.cand = a.cand + (int64_t)row * a.P * a.chunk;
   grp.cap = a.chunk;
   uint32_t offset, count, tau;
-  const uint64_t sel = radix_select<SPT>(key, (uint32_t)a.m, sh, grp, &offset, &count, &tau, s_qcnt);
+  uint64_t sel = 0;
+  if (a.P == 1) {
+    sel = radix_select<SPT>(key, (uint32_t)a.m, sh, grp, &offset, &count, &tau, s_qcnt);
+  } else {
+    // s_low of a fixed sample of the row's tokens (the same in every
+    // workgroup of the row): all tokens if T <= kSampleN, else 256 runs of
+    // 16 consecutive tokens, run g starting at floor(g T / 256)
+    const int64_t ns = min((int64_t)kSampleN, a.T);
+    const bool all = a.T <= kSampleN;
+    uint32_t skey[kSamplePT];
+    {
+      uint32_t wd[kSamplePT][4];
+      const uint32_t* wps[kSamplePT];
+#pragma unroll
+      for (int j = 0; j < kSamplePT; ++j) {
+        const int64_t i = min((int64_t)(tid + j * SB), ns - 1);
+        const int64_t t = all ? i : (((i >> 4) * a.T) >> 8) + (i & 15);
+        wps[j] = lo + t * lw;
+        if (low3) {
+          const Words3 v = *(const Words3*)wps[j];
+          wd[j][0] = v.x; wd[j][1] = v.y; wd[j][2] = v.z; wd[j][3] = v.z;
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) wd[j][c] = wps[j][min(c, a.klow - 1)];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kSamplePT; ++j) {
+        const uint32_t* wp = wps[j];
+        float s = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (c < a.klow) s = fmaf(code_coef(wd[j][c]), s_u[code_idx(wd[j][c]) & AMASK], s);
+        for (int c = 4; c < a.klow; ++c)
+          s = fmaf(code_coef(wp[c]), s_u[code_idx(wp[c]) & AMASK], s);
+        skey[j] = (tid + j * SB < ns) ? float_key(s) : 0u;
+      }
+    }
+    if (!sample_window_select<SPT>(key, skey, (uint32_t)ns, (uint32_t)a.m, (uint32_t)a.T, sh, grp,
+                                   &offset, &count, &tau, &sel, s_qcnt))
+      sel = radix_select_coop<SPT>(key, (uint32_t)a.m, sh, grp, &offset, &count, &tau, s_qcnt, 1u);
+  }
 
   // 4. compaction: the selected tokens of this workgroup in token order, as
   // offsets within the chunk in LDS (global list when they do not fit).
@@ -663,7 +755,7 @@ __global__ __launch_bounds__(1024) void k_reduce_out(const float* opart, int nch
 // ---------------------------------------------------------------------------
 static int spt_for(int64_t chunk) {
   const int64_t need = (chunk + SB - 1) / SB;
-  for (int s : {4, 8, 16, 32, 64})
+  for (int s : {4, 8, 16, 32})
     if (need <= s) return s;
   return 0;
 }
@@ -719,7 +811,6 @@ static const void* pick_rows_kernel(int spt, bool fast) {
   SDKV_PICK(8)
   SDKV_PICK(16)
   SDKV_PICK(32)
-  SDKV_PICK(64)
 #undef SDKV_PICK
   return nullptr;
 }

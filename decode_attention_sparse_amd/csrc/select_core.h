@@ -20,13 +20,13 @@
 
 namespace sdkv {
 
-constexpr int SB = 512;        // threads per block in select-bearing kernels
+constexpr int SB = 1024;       // threads per block in select-bearing kernels
 constexpr int SNW = SB / 64;   // waves per block
 
 struct SelShared {
   uint32_t hist[2048];
   uint32_t scan[SB];
-  uint32_t tmp[16];
+  uint32_t tmp[2 * SB / 64];
   uint32_t bcast[8];
 };
 
@@ -41,7 +41,7 @@ struct SelGroup {
   int64_t cap;        // candidate slots per workgroup (>= keys per workgroup)
 };
 
-constexpr int kCandPT = 32;  // candidates per thread kept in registers
+constexpr int kCandPT = 16;  // candidates per thread kept in registers
 
 // Calls f(j, rank) for every set bit j of `bits`, where rank is the position
 // of slot j among all set slots of the block in element order.
@@ -115,7 +115,7 @@ __device__ __forceinline__ uint32_t find_digit(SelShared& sh, int nbins, uint32_
 template <int SPT>
 __device__ __forceinline__ uint64_t radix_select_coop(const uint32_t (&key)[SPT], uint32_t m, SelShared& sh,
                                       const SelGroup& g, uint32_t* offset, uint32_t* count,
-                                      uint32_t* tau_out, uint32_t* s_qcnt) {
+                                      uint32_t* tau_out, uint32_t* s_qcnt, uint32_t bar_base) {
   const int tid = threadIdx.x;
   // --- round 1: global histogram of the top 11 bits ----------------------------
   for (int i = tid; i < 2048; i += SB) sh.hist[i] = 0u;
@@ -128,7 +128,7 @@ __device__ __forceinline__ uint64_t radix_select_coop(const uint32_t (&key)[SPT]
     const uint32_t c = sh.hist[i];
     if (c) atomicAdd(&g.ghist[i], c);
   }
-  group_barrier(g.bar, (uint32_t)g.P, g.err);
+  group_barrier(g.bar, (uint32_t)g.P * (bar_base + 1u), g.err);
   for (int i = tid; i < 2048; i += SB) sh.hist[i] = ld_agent(&g.ghist[i]);
   __syncthreads();
   uint32_t gt1;
@@ -156,7 +156,7 @@ __device__ __forceinline__ uint64_t radix_select_coop(const uint32_t (&key)[SPT]
     st_agent(&g.xchg[2 * g.p], tna);
     st_agent(&g.xchg[2 * g.p + 1], tnc);
   }
-  group_barrier(g.bar, (uint32_t)g.P * 2u, g.err);
+  group_barrier(g.bar, (uint32_t)g.P * (bar_base + 2u), g.err);
 
   // --- every workgroup: counts per workgroup, then all candidates ------------
   // s_qcnt layout: [0,P) above-bin counts A_q, [P,2P) candidate counts c_q,
@@ -189,13 +189,21 @@ __device__ __forceinline__ uint64_t radix_select_coop(const uint32_t (&key)[SPT]
   };
   const bool in_regs = C <= (uint32_t)SB * kCandPT;
   uint32_t ck[kCandPT];
+  uint32_t cq[kCandPT / 4];  // owning workgroup of each candidate, 8 bits each
   if (in_regs) {
+    // this thread's candidates gi = tid + k*SB increase with k, so their
+    // owning workgroup is found by advancing monotonically
+    int q = 0;
 #pragma unroll
     for (int k = 0; k < kCandPT; ++k) {
       const uint32_t gi = (uint32_t)(tid + k * SB);
-      int q;
       ck[k] = 0u;
-      if ((uint32_t)(k * SB) < C && gi < C) ck[k] = cand_at(gi, &q);
+      if (k % 4 == 0) cq[k / 4] = 0u;
+      if ((uint32_t)(k * SB) < C && gi < C) {
+        while (q + 1 < P && cpre[q + 1] <= gi) ++q;
+        ck[k] = ld_agent(&g.cand[(int64_t)q * g.cap + (gi - cpre[q])]);
+        cq[k / 4] |= (uint32_t)q << (8 * (k % 4));
+      }
     }
   }
   // local rounds 2 and 3 over the candidates
@@ -232,17 +240,8 @@ __device__ __forceinline__ uint64_t radix_select_coop(const uint32_t (&key)[SPT]
   // Per-workgroup counts of candidates above / equal to tau. Candidates are
   // laid out in workgroup order, so the lanes of a wave see one or two
   // workgroups: aggregate with ballots, one LDS atomic per workgroup seen.
-  auto tally = [&](uint32_t gi, uint32_t c, bool valid) {
+  auto tally = [&](int q, uint32_t c, bool valid) {
     const bool isgt = valid && c > tau, iseq = valid && c == tau;
-    int q = 0;
-    if (isgt || iseq) {
-      int lo = 0, hi = P - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (cpre[mid] <= gi) lo = mid; else hi = mid - 1;
-      }
-      q = lo;
-    }
     uint64_t pend = __ballot(isgt || iseq);
     while (pend) {
       const int leader = __builtin_ctzll(pend);
@@ -261,14 +260,15 @@ __device__ __forceinline__ uint64_t radix_select_coop(const uint32_t (&key)[SPT]
 #pragma unroll
     for (int k = 0; k < kCandPT; ++k) {
       const uint32_t gi = (uint32_t)(tid + k * SB);
-      if ((uint32_t)(k * SB) < C) tally(gi, ck[k], gi < C && ck[k] >= tau);
+      const int q = (int)((cq[k / 4] >> (8 * (k % 4))) & 0xFFu);
+      if ((uint32_t)(k * SB) < C) tally(q, ck[k], gi < C && ck[k] >= tau);
     }
   } else {
     for (uint32_t base = 0; base < C; base += SB) {
       const uint32_t gi = base + tid;
-      int q;
+      int q = 0;
       const uint32_t c = (gi < C) ? cand_at(gi, &q) : 0u;
-      tally(gi, c, gi < C && c >= tau);
+      tally(q, c, gi < C && c >= tau);
     }
   }
   __syncthreads();
@@ -309,12 +309,287 @@ __device__ __forceinline__ uint64_t radix_select_coop(const uint32_t (&key)[SPT]
 
 // Returns this thread's selection bitmask; *offset / *count give the block's
 // output range in the row's ascending selection list, *tau the threshold key.
+// k-th largest (k >= 1) of the non-zero keys held by the block (N per
+// thread) by an LDS radix select over 11/11/10-bit digits, starting at
+// `round0` with every key known to carry the digits of `prefix` above it.
+// Returns 0 if there are fewer than k keys.
+template <int N>
+__device__ __forceinline__ uint32_t local_kth(const uint32_t (&keys)[N], uint32_t k, SelShared& sh,
+                                              int round0, uint32_t prefix) {
+  const int tid = threadIdx.x;
+  uint32_t pmask = round0 == 0 ? 0u : (round0 == 1 ? 0xFFE00000u : 0xFFFFFC00u);
+  prefix &= pmask;
+  uint32_t need = k;
+  for (int round = round0; round < 3; ++round) {
+    const int shift = round == 0 ? 21 : (round == 1 ? 10 : 0);
+    const int nbins = round == 2 ? 1024 : 2048;
+    for (int i = tid; i < 2048; i += SB) sh.hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const uint32_t c = keys[j];
+      if (c != 0u && (c & pmask) == prefix)
+        atomicAdd(&sh.hist[(c >> shift) & (uint32_t)(nbins - 1)], 1u);
+    }
+    __syncthreads();
+    uint32_t gt;
+    const uint32_t v = find_digit(sh, nbins, need, &gt);
+    need -= min(need, gt);
+    prefix |= v << shift;
+    pmask |= (uint32_t)(nbins - 1) << shift;
+  }
+  return prefix;
+}
+
+// Bin in [0, 2048) of a key's value on the linear scale (v - base) * inv,
+// clamped. Monotone non-decreasing in the key for any base and any inv >= 0
+// (IEEE rounding is monotone), so keys in a higher bin are always larger;
+// identical wherever it is evaluated with the same base and inv.
+__device__ __forceinline__ int value_bin(uint32_t k, float base, float inv) {
+  const float x = (key_float(k) - base) * inv;
+  return (int)fminf(fmaxf(x, 0.f), 2047.f);
+}
+
+constexpr int kSampleN = 4096;             // shared sample size (tokens)
+constexpr int kSamplePT = kSampleN / SB;
+constexpr int kWinPT = 16;                 // window keys per thread in registers
+
+// Sample-window select with one cross-workgroup synchronisation. Every
+// workgroup of the row holds the keys `skey` of the same fixed sample of ns
+// of the row's T elements, so all derive the same window of value bins
+// around the sample's estimate of the m-th largest key (the bins of sample
+// ranks m ns / T -/+ (5 standard deviations + 4), on a linear scale between
+// the sample's smallest and largest value). Each workgroup publishes its
+// count of keys above the window and its keys inside it; after one barrier
+// every workgroup reads them all and finishes the select locally (a fine
+// linear histogram of the window keys, then exact ranks inside one bin).
+// That the window holds the m-th largest key is checked exactly (fewer than
+// m keys above it, at least m at or above its bottom); if that fails, or a
+// workgroup's window keys exceed its slots, the function returns false
+// having used one barrier and changed nothing else, and the caller runs
+// the two-synchronisation select. The result is exact either way.
+template <int SPT>
+__device__ __forceinline__ bool sample_window_select(const uint32_t (&key)[SPT],
+                                                     const uint32_t (&skey)[kSamplePT],
+                                                     uint32_t ns, uint32_t m, uint32_t T,
+                                                     SelShared& sh, const SelGroup& g,
+                                                     uint32_t* offset, uint32_t* count,
+                                                     uint32_t* tau_out, uint64_t* sel_out,
+                                                     uint32_t* s_qcnt) {
+  const int tid = threadIdx.x, w = wave_id(), lane = lane_id();
+  const int P = g.P;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  // --- sample value range ------------------------------------------------------
+  uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+#pragma unroll
+  for (int j = 0; j < kSamplePT; ++j)
+    if (skey[j] != 0u) { kmn = min(kmn, skey[j]); kmx = max(kmx, skey[j]); }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    kmn = min(kmn, (uint32_t)__shfl_xor((int)kmn, o, 64));
+    kmx = max(kmx, (uint32_t)__shfl_xor((int)kmx, o, 64));
+  }
+  if (lane == 0) { sh.tmp[w] = kmn; sh.tmp[SNW + w] = kmx; }
+  if (tid == 0) { sh.bcast[4] = 0u; sh.bcast[5] = 0u; sh.bcast[6] = 0u; }
+  for (int i = tid; i < 2048; i += SB) sh.hist[i] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < SNW; ++i) { kmn = min(kmn, sh.tmp[i]); kmx = max(kmx, sh.tmp[SNW + i]); }
+  const float base = key_float(kmn);
+  const float span = key_float(kmx) - base;
+  const float inv = (kmx > kmn && span > 0.f && span < INFINITY) ? 2048.f / span : 0.f;
+  // --- window bins from the sample's rank estimates ---------------------------
+  const float rho = (ns >= T) ? (float)m : (float)((double)m * ns / T);
+  const float sd = sqrtf(fmaxf(rho * (1.f - rho / (float)ns), 0.f));
+  const float wd = (ns >= T) ? 0.f : 5.f * sd + 4.f;
+  const uint32_t r_hi = (uint32_t)fmaxf(1.f, floorf(rho - wd));
+  const uint32_t r_lo = (uint32_t)fminf((float)ns, fmaxf((float)r_hi, ceilf(rho + wd)));
+#pragma unroll
+  for (int j = 0; j < kSamplePT; ++j)
+    if (skey[j] != 0u) atomicAdd(&sh.hist[value_bin(skey[j], base, inv)], 1u);
+  __syncthreads();  // also: every thread has read sh.tmp
+  uint32_t gtx;
+  const int b_hi = (int)find_digit(sh, 2048, r_hi, &gtx);
+  const int b_lo = (int)find_digit(sh, 2048, r_lo, &gtx);
+  // --- publish: count above the window; window keys in wave-reserved slots ----
+  const int wcap = (int)min(g.cap, (int64_t)(SB * kWinPT / P));
+  uint64_t wbits = 0;
+  uint32_t na = 0;
+#pragma unroll
+  for (int j = 0; j < SPT; ++j) {
+    const uint32_t k = key[j];
+    const int bk = value_bin(k, base, inv);
+    na += (k != 0u && bk > b_hi) ? 1u : 0u;
+    if (k != 0u && bk >= b_lo && bk <= b_hi) wbits |= 1ull << j;
+  }
+  uint32_t wn = 0;
+#pragma unroll
+  for (int j = 0; j < SPT; ++j) wn += (uint32_t)__popcll(__ballot((wbits >> j) & 1ull));
+  const uint32_t na_w = wave_sum_u32(na);
+  uint32_t wbase = 0;
+  if (lane == 0) {
+    wbase = atomicAdd(&sh.bcast[4], wn);
+    atomicAdd(&sh.bcast[5], na_w);
+  }
+  wbase = (uint32_t)__shfl((int)wbase, 0, 64);
+  uint32_t* mywin = g.cand + (int64_t)g.p * g.cap;
+#pragma unroll
+  for (int j = 0; j < SPT; ++j) {
+    const uint64_t bj = __ballot((wbits >> j) & 1ull);
+    const uint32_t r = wbase + (uint32_t)__popcll(bj & lt);
+    if (((wbits >> j) & 1ull) && r < (uint32_t)wcap) st_agent(&mywin[r], key[j]);
+    wbase += (uint32_t)__popcll(bj);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    st_agent(&g.xchg[2 * g.p], sh.bcast[5]);
+    st_agent(&g.xchg[2 * g.p + 1], sh.bcast[4]);
+  }
+  group_barrier(g.bar, (uint32_t)P, g.err);
+  // --- read every workgroup's counts and window keys --------------------------
+  // slot u = q * wcap + r belongs to workgroup q; loads are branch-free (the
+  // index is clamped, unused slots are masked after)
+  const uint32_t nslots = (uint32_t)(P * wcap);
+  uint32_t ck[kWinPT];
+#pragma unroll
+  for (int k = 0; k < kWinPT; ++k) {
+    const uint32_t u = min((uint32_t)(tid + k * SB), nslots - 1u);
+    ck[k] = ld_agent(&g.cand[(int64_t)(u / wcap) * g.cap + (u % wcap)]);
+  }
+  if (tid < P) {
+    s_qcnt[tid] = ld_agent(&g.xchg[2 * tid]);
+    s_qcnt[P + tid] = ld_agent(&g.xchg[2 * tid + 1]);
+  }
+  if (tid < 5) s_qcnt[2 * P + tid] = 0u;
+  __syncthreads();
+  uint32_t A = 0, total = 0, a_before = 0;
+  bool overflow = false;
+  for (int q = 0; q < P; ++q) {
+    A += s_qcnt[q];
+    a_before += (q < g.p) ? s_qcnt[q] : 0u;
+    total += s_qcnt[P + q];
+    overflow |= s_qcnt[P + q] > (uint32_t)wcap;
+  }
+  if (overflow || A >= m || m - A > total) {
+    __syncthreads();
+    return false;
+  }
+#pragma unroll
+  for (int k = 0; k < kWinPT; ++k) {
+    const uint32_t u = (uint32_t)(tid + k * SB);
+    const uint32_t uc = min(u, nslots - 1u);
+    const bool live = u < nslots && (uc % wcap) < s_qcnt[P + uc / wcap];
+    ck[k] = live ? ck[k] : 0u;
+  }
+  // --- the threshold: the need1-th largest window key -------------------------
+  const uint32_t need1 = m - A;
+  float base2 = base, inv2 = 0.f;
+  if (inv > 0.f) {
+    base2 = base + (float)b_lo / inv;
+    inv2 = inv * (2048.f / (float)(b_hi - b_lo + 1));
+  }
+  for (int i = tid; i < 2048; i += SB) sh.hist[i] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kWinPT; ++k)
+    if (ck[k] != 0u) atomicAdd(&sh.hist[value_bin(ck[k], base2, inv2)], 1u);
+  __syncthreads();
+  uint32_t gt2;
+  const int bstar = (int)find_digit(sh, 2048, need1, &gt2);
+  const uint32_t need2 = need1 - min(need1, gt2);
+  const uint32_t nc = sh.hist[bstar];
+  uint32_t tau;
+  if (nc <= (uint32_t)SB) {
+    // gather the bin's keys (wave-aggregated slots), then exact ranks
+#pragma unroll
+    for (int k = 0; k < kWinPT; ++k) {
+      const bool in = ck[k] != 0u && value_bin(ck[k], base2, inv2) == bstar;
+      const uint64_t bk = __ballot(in);
+      if (bk) {
+        uint32_t b0 = 0;
+        if (lane == 0) b0 = atomicAdd(&sh.bcast[6], (uint32_t)__popcll(bk));
+        b0 = (uint32_t)__shfl((int)b0, 0, 64);
+        if (in) sh.scan[b0 + (uint32_t)__popcll(bk & lt)] = ck[k];
+      }
+    }
+    __syncthreads();
+    if ((uint32_t)tid < nc) {
+      const uint32_t x = sh.scan[tid];
+      uint32_t ngt = 0, nge = 0;
+      for (uint32_t i = 0; i < nc; ++i) {
+        const uint32_t y = sh.scan[i];
+        ngt += y > x ? 1u : 0u;
+        nge += y >= x ? 1u : 0u;
+      }
+      if (ngt < need2 && need2 <= nge) sh.bcast[7] = x;
+    }
+    __syncthreads();
+    tau = sh.bcast[7];
+    __syncthreads();
+  } else {
+    tau = local_kth<kWinPT>(ck, need1, sh, 0, 0u);
+  }
+  *tau_out = tau;
+  // --- counts around tau: window keys of earlier workgroups, all window keys
+  // above tau, and this workgroup's own keys above / equal to tau ------------
+  const uint32_t ulim = (uint32_t)(g.p * wcap);
+  uint32_t c_gtb = 0, c_eqb = 0, c_gta = 0;
+#pragma unroll
+  for (int k = 0; k < kWinPT; ++k) {
+    const uint32_t u = (uint32_t)(tid + k * SB);
+    const uint32_t x = ck[k];
+    const bool isgt = x != 0u && x > tau, iseq = x != 0u && x == tau;
+    c_gtb += (uint32_t)__popcll(__ballot(isgt && u < ulim));
+    c_eqb += (uint32_t)__popcll(__ballot(iseq && u < ulim));
+    c_gta += (uint32_t)__popcll(__ballot(isgt));
+  }
+  uint64_t gt_bits = 0, eq_bits = 0;
+#pragma unroll
+  for (int j = 0; j < SPT; ++j) {
+    const uint32_t k = key[j];
+    if (k > tau) gt_bits |= 1ull << j;
+    else if (k == tau && k != 0u) eq_bits |= 1ull << j;
+  }
+  const uint32_t own_gt = wave_sum_u32((uint32_t)__popcll(gt_bits));
+  const uint32_t own_eq = wave_sum_u32((uint32_t)__popcll(eq_bits));
+  if (lane == 0) {
+    atomicAdd(&s_qcnt[2 * P + 0], c_gtb);
+    atomicAdd(&s_qcnt[2 * P + 1], c_eqb);
+    atomicAdd(&s_qcnt[2 * P + 2], c_gta);
+    atomicAdd(&s_qcnt[2 * P + 3], own_gt);
+    atomicAdd(&s_qcnt[2 * P + 4], own_eq);
+  }
+  __syncthreads();
+  const uint32_t gtb = s_qcnt[2 * P + 0], eqb = s_qcnt[2 * P + 1], gt_all = s_qcnt[2 * P + 2];
+  const uint32_t tg = s_qcnt[2 * P + 3], te = s_qcnt[2 * P + 4];
+  __syncthreads();
+  const uint32_t need = need1 - min(need1, gt_all);  // keys equal to tau to take
+  // see radix_select for why this is written without a guarded subtraction
+  const uint32_t eq_before = min(need, eqb);
+  const uint32_t rem = need - eq_before;
+  const uint32_t take = min(rem, te);
+  *offset = a_before + gtb + eq_before;
+  *count = tg + take;
+  uint64_t sel = gt_bits;
+  if (take == te) {
+    sel |= eq_bits;
+  } else if (take > 0) {
+    uint64_t keep = 0;
+    ordered_ranks<SPT>(eq_bits, sh, [&](int j, uint32_t r) {
+      if (r < take) keep |= 1ull << j;
+    });
+    sel |= keep;
+  }
+  *sel_out = sel;
+  return true;
+}
+
 // With P > 1 this is radix_select_coop; s_qcnt is LDS scratch of >= 5P+1 words.
 template <int SPT>
 __device__ __forceinline__ uint64_t radix_select(const uint32_t (&key)[SPT], uint32_t m, SelShared& sh,
                                  const SelGroup& g, uint32_t* offset, uint32_t* count,
                                  uint32_t* tau_out, uint32_t* s_qcnt) {
-  if (g.P > 1) return radix_select_coop<SPT>(key, m, sh, g, offset, count, tau_out, s_qcnt);
+  if (g.P > 1) return radix_select_coop<SPT>(key, m, sh, g, offset, count, tau_out, s_qcnt, 0u);
   const int tid = threadIdx.x;
   uint32_t prefix = 0, pmask = 0, need = m;
   for (int round = 0; round < 3; ++round) {

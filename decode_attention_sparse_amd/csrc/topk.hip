@@ -72,7 +72,7 @@ __global__ __launch_bounds__(SB) void k_topk(TopkArgs a) {
 
 static int topk_spt(int64_t chunk) {
   const int64_t need = (chunk + SB - 1) / SB;
-  for (int s : {4, 16, 64})
+  for (int s : {4, 16, 32})
     if (need <= s) return s;
   return 0;
 }
@@ -107,7 +107,7 @@ sdkv_status plan_topk(int64_t rows, int64_t n, int64_t k, TopkPlan* p) {
 static const void* pick_topk_kernel(int spt) {
   if (spt == 4) return (const void*)&k_topk<4>;
   if (spt == 16) return (const void*)&k_topk<16>;
-  if (spt == 64) return (const void*)&k_topk<64>;
+  if (spt == 32) return (const void*)&k_topk<32>;
   return nullptr;
 }
 
