@@ -82,11 +82,20 @@ class HipEvents:
         self.made = []
 
 
+def sources_digest(paths):
+    """sha256 over the concatenated contents of the given repo-relative files."""
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def read_traffic(kernel: str, workload: str):
     """HBM bytes per launch measured with rocprofv3 counters, from the
-    committed summary profiles/traffic_<kernel>_<workload>.md, if its recorded
-    source digest still matches the kernel source; else None."""
-    import hashlib
+    committed summary profiles/traffic_<kernel>_<workload>.md, if the digest it
+    records of the kernel's sources still matches them; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.md")
     if not os.path.exists(path):
         return None
@@ -94,18 +103,34 @@ def read_traffic(kernel: str, workload: str):
     for line in open(path):
         if ":" in line and line.strip().startswith("- "):
             k, v = line.strip()[2:].split(":", 1)
-            vals[k.strip()] = v.strip()
-    src = vals.get("source")
-    digest = vals.get("source_sha256")
-    if not src or not digest:
+            vals[k.strip()] = v.strip().strip("`")
+    srcs = [s.strip() for s in vals.get("sources", "").split(",") if s.strip()]
+    if not srcs or not vals.get("sources_sha256"):
         return None
-    with open(os.path.join(ROOT, src), "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != digest:
-            return None
     try:
+        if sources_digest(srcs) != vals["sources_sha256"]:
+            return None
         return float(vals["hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
+    except (OSError, KeyError, ValueError):
         return None
+
+
+def calibrate_copy(torch, mib: int, reps: int = 5):
+    """A plain device-to-device copy of a known number of bytes: the reference
+    against which the rocprofv3 FETCH_SIZE / WRITE_SIZE counters are scaled,
+    and the achievable stream-copy bandwidth."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    el = (time.perf_counter() - t) / reps
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "reps": reps + 1,
+                      "copy_GBs": round(2 * n * 4 / el / 1e9, 1)}), flush=True)
 
 
 # ---------------------------------------------------------------------------
@@ -287,6 +312,10 @@ def main():
     ap.add_argument("--enc-warmup", type=int, default=1)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-encode", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="encode only (profiling runs); prints no benchmark line")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -302,8 +331,18 @@ def main():
     import synth
     if not torch.cuda.is_available():
         raise SystemExit("no GPU visible")
+    if args.calibrate_copy:
+        calibrate_copy(torch, args.calibrate_copy)
+        return
     sd.lib()
     ev = HipEvents()
+    if args.no_decode:
+        log("encode benchmark (524,288 vectors)")
+        enc = bench_encode(args, torch, sd, synth, ev)
+        log(f"  {enc['ms']:.2f} ms/step, kernel {enc['kernel_ms']:.2f} ms, "
+            f"{enc['value'] / 1e6:.2f} M vectors/s, {enc['roofline']['achieved']} TFLOP/s")
+        ev.close()
+        return
     log("decode benchmark (128K context)")
     dec = bench_decode(args, torch, sd, synth, ev)
     log(f"  {dec['ms'] * 1e3:.1f} us/step, stages (us): "

@@ -121,9 +121,11 @@ struct RowsArgs {
   uint32_t* xchg;           // [rows, P, 2]
   uint32_t* bar;            // [rows]
   uint32_t* err;
-  uint32_t* ticket;         // workgroup start-order counter, zeroed per call
-  int xcd_map;              // map tickets to rows XCD-locally
+  uint32_t* ticket;         // [8] workgroup start-order counters, zeroed per call
+  int xcd_map;              // per-XCD ticket classes (rows stay on one XCD)
 };
+
+static_assert(kRowThreads == SB && kMaxRowSPT == kMaxSPT, "planner and kernels disagree");
 
 struct Words3 {
   uint32_t x, y, z;
@@ -224,16 +226,13 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   __shared__ uint32_t s_qcnt[5 * kMaxRowP + 1];
 
   const int tid = threadIdx.x;
-  // Work is assigned in workgroup start order (a ticket), not by block id:
-  // every workgroup of a row then holds a ticket within a window of 8P, so
-  // the earliest unfinished row always has all its workgroups resident once
-  // earlier rows retire -- the row barriers cannot deadlock without a
-  // cooperative launch (the host checks that the window fits the device).
-  __shared__ uint32_t s_ticket;
-  if (tid == 0) s_ticket = atomicAdd(a.ticket, 1u);
+  // Work is assigned in workgroup start order (tickets), not by block id, so
+  // a row's P workgroups can wait on each other without a cooperative
+  // launch (the host checks that the co-resident capacity covers a row).
+  __shared__ int s_tile;
+  if (tid == 0) s_tile = ticket_tile(a.ticket, a.nrows * a.P, a.xcd_map != 0);
   __syncthreads();
-  const int nb = a.nrows * a.P;
-  const int L = a.xcd_map ? xcd_tile((int)s_ticket, nb) : (int)s_ticket;
+  const int L = s_tile;
   const int p = L % a.P;
   const int row = a.row0 + L / a.P;
   const int b = row / a.Hq, h = row % a.Hq, g = h / a.G;
@@ -286,9 +285,10 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   grp.cand = a.cand + (int64_t)row * a.P * a.chunk;
   grp.cap = a.chunk;
   uint32_t offset, count, tau;
-  uint64_t sel = 0;
-  if (a.P == 1) {
-    sel = radix_select<SPT>(key, (uint32_t)a.m, sh, grp, &offset, &count, &tau, s_qcnt);
+  Mask sel = 0;
+  if (SPT > kMaxCoopSPT || a.P == 1) {
+    // single-workgroup rows (the only ones the host plans at SPT > kMaxCoopSPT)
+    sel = radix_select_local<SPT>(key, (uint32_t)a.m, sh, &offset, &count, &tau);
   } else {
     // s_low of a fixed sample of the row's tokens (the same in every
     // workgroup of the row): all tokens if T <= kSampleN, else 256 runs of
@@ -768,7 +768,10 @@ sdkv_status plan_decode(const sdkv_attn_args* a, DecodePlan* p) {
   const int64_t p_min = (T + kMaxChunk - 1) / kMaxChunk;
   const int64_t p_par = std::max<int64_t>(1, kPlanCUs / std::max<int64_t>(1, q.rows));
   const int64_t p_cap = std::max<int64_t>(1, (T + 2047) / 2048);
-  const int64_t P = std::max(p_min, std::min(p_par, p_cap));
+  int64_t P = std::max(p_min, std::min(p_par, p_cap));
+  // rows split over several workgroups hold at most kMaxCoopSPT keys per
+  // thread (the 32-key row kernel is built for single-workgroup rows only)
+  if (P > 1) P = std::max(P, (T + kMaxCoopChunk - 1) / kMaxCoopChunk);
   if (P > kMaxRowP) return SDKV_ERR_UNSUPPORTED;
   q.P = (int)P;
   q.chunk = (T + P - 1) / P;
@@ -794,7 +797,7 @@ sdkv_status plan_decode(const sdkv_attn_args* a, DecodePlan* p) {
   q.off_xchg = off;   off += (size_t)rows * q.P * 2 * 4;
   q.off_bar = off;    off += (size_t)rows * 4;
   q.off_err = off;    off += 4;
-  q.off_ticket = off; off += 4;
+  q.off_ticket = off; off += 8 * 4;
   off = align_up(off, A);
   q.zero_bytes = off - q.off_zero;
   q.off_opart = off;  off = align_up(off + (size_t)q.nchunks * rows * a->d * 4, A);
@@ -888,16 +891,18 @@ sdkv_status launch_decode(const sdkv_attn_args* a, const DecodePlan& p, void* ws
   const void* kfn = pick_rows_kernel(p.spt, p.fast && aligned);
   if (!kfn) return SDKV_ERR_UNSUPPORTED;
   ra.ticket = (uint32_t*)(base + p.off_ticket);
-  ra.xcd_map = 0;
+  // Per-XCD ticket classes need whole rows per class; with P > 1 every
+  // class must also hold two rows' workgroups co-resident.
+  const int64_t nb = rows * p.P;
+  bool xcd = nb % 8 == 0 && (nb / 8) % p.P == 0;
   if (p.P > 1) {
-    // a row's workgroups hold tickets within a window of 8P (XCD-local
-    // mapping) or P; that window must fit the co-resident capacity
     int cap = 0;
     sdkv_status st = coresident_blocks(kfn, SB, 0, &cap);
     if (st != SDKV_OK) return st;
     if (cap < p.P) return SDKV_ERR_UNSUPPORTED;
-    ra.xcd_map = (16 * p.P <= cap) ? 1 : 0;
+    xcd = xcd && 16 * p.P <= cap;
   }
+  ra.xcd_map = xcd ? 1 : 0;
   if (!record_stage(ev, 1, stream)) return SDKV_ERR_DEVICE;
   {
     ra.row0 = 0;

@@ -133,19 +133,25 @@ __device__ __forceinline__ float block_sum(float v, float* tmp) {
 }
 
 // --- cross-workgroup barrier among the workgroups sharing `ctr` ---------------
-// Only used in cooperative launches (all workgroups co-resident). Data that
-// crosses workgroups inside a kernel is written and read only with relaxed
-// agent-scope atomics (device-coherent sc1 accesses on gfx950), so the barrier
-// needs no cache-flushing fence: every thread waits for its own memory
-// operations to complete (s_waitcnt), then one thread arrives and polls.
-// (An agent-scope __threadfence() per thread writes back and invalidates the
-// L2 and measured ~65 us per barrier on MI355X; this form measured ~2 us.)
+// The workgroups must be co-resident (the callers assign work by start-order
+// tickets and check the capacity). MI355X has one L2 per XCD and the L2s are
+// not coherent with each other, so data that one workgroup writes and another
+// reads inside a kernel needs an agent-scope release / acquire pair: every
+// thread first completes its own memory operations (s_waitcnt) and meets the
+// others at the workgroup barrier; then one thread releases (write-back of
+// this XCD's L2, buffer_wbl2), arrives with an atomic add (performed
+// coherently), polls the counter, and acquires (invalidation of this XCD's L2,
+// buffer_inv) before the workgroup barrier lets the other threads read. The
+// cross-workgroup data itself is accessed with agent-scope atomic loads and
+// stores, which bypass the per-CU L1. One fence pair per workgroup, not one
+// per thread: per-thread fences measured ~65 us per barrier.
 // The spin is bounded: after ~2^24 polls the workgroup records the failure in
 // *err and continues, so no wave can wait forever.
 __device__ __forceinline__ void group_barrier(uint32_t* ctr, uint32_t target, uint32_t* err) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     uint32_t spins = 0;
     while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
@@ -155,6 +161,7 @@ __device__ __forceinline__ void group_barrier(uint32_t* ctr, uint32_t target, ui
         break;
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
 }
@@ -166,12 +173,29 @@ __device__ __forceinline__ void st_agent(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Workgroup -> logical tile mapping that keeps consecutive logical tiles on
+// Workgroup id -> logical tile mapping that keeps consecutive logical tiles on
 // one XCD: the dispatcher hands workgroup ids to the 8 XCDs round-robin, so
 // id i runs on XCD i % 8. When nb is a multiple of 8, XCD x gets the
 // contiguous logical range [x*nb/8, (x+1)*nb/8). A bijection either way.
 __device__ __forceinline__ int xcd_tile(int bid, int nb) {
   return (nb % 8 == 0) ? (bid % 8) * (nb / 8) + bid / 8 : bid;
+}
+
+// Logical tile of this workgroup, handed out in start order by `tickets`
+// (call from one thread). A workgroup holds a ticket only once it runs, so
+// the holders of the lowest unfinished tickets are always resident: tiles
+// that wait on each other (a row's workgroups) cannot deadlock as long as
+// the co-resident capacity covers a row. With `xcd`, workgroup ids are split
+// into 8 classes by id % 8 -- the XCD the dispatcher sends each id to -- and
+// class c hands out the contiguous tiles [c nb/8, (c+1) nb/8) from its own
+// counter, so tiles that share data stay on one XCD and share its L2. The
+// caller guarantees nb % 8 == 0 for `xcd`.
+__device__ __forceinline__ int ticket_tile(uint32_t* tickets, int nb, bool xcd) {
+  if (xcd) {
+    const int c = (int)(blockIdx.x & 7u);
+    return c * (nb >> 3) + (int)atomicAdd(&tickets[c], 1u);
+  }
+  return (int)atomicAdd(&tickets[0], 1u);
 }
 
 }  // namespace sdkv

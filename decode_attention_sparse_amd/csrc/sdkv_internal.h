@@ -13,9 +13,15 @@ namespace sdkv {
 // Planning assumes an MI355X: 256 compute units. The same plan (and so the
 // same workspace size) is used on any device.
 constexpr int kPlanCUs = 256;
-constexpr int kRowThreads = 512;
-constexpr int kMaxSPT = 64;                                // keys per thread
-constexpr int64_t kMaxChunk = (int64_t)kRowThreads * kMaxSPT;  // 32768 tokens
+constexpr int kRowThreads = 1024;                             // select-bearing workgroups
+constexpr int kMaxRowSPT = 32;                                // keys per thread
+constexpr int64_t kMaxChunk = (int64_t)kRowThreads * kMaxRowSPT;  // 32768 tokens
+// Rows split over several workgroups: at most 16 keys per thread. The row
+// kernel with 32 keys per thread and the cross-workgroup select returned
+// wrong selections on gfx950 (every row; correct at 16 keys per thread and
+// with the single-workgroup select at 32), so it is not built.
+constexpr int kMaxCoopSPT = 16;
+constexpr int64_t kMaxCoopChunk = (int64_t)kRowThreads * kMaxCoopSPT;  // 16384 tokens
 constexpr int kMaxRowP = 64;   // workgroups per decode row
 constexpr int kMaxAtomsDecode = 32768;
 

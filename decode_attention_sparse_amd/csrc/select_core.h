@@ -43,15 +43,20 @@ struct SelGroup {
 
 constexpr int kCandPT = 16;  // candidates per thread kept in registers
 
+// Per-thread element masks: bit j is element j of the thread's SPT <= 32.
+using Mask = uint32_t;
+constexpr int kMaxSPT = 32;
+
 // Calls f(j, rank) for every set bit j of `bits`, where rank is the position
 // of slot j among all set slots of the block in element order.
 template <int SPT, class F>
-__device__ __forceinline__ void ordered_ranks(uint64_t bits, SelShared& sh, F&& f) {
+__device__ __forceinline__ void ordered_ranks(Mask bits, SelShared& sh, F&& f) {
   static_assert(SPT * SNW <= SB, "rank table exceeds block");
+  static_assert(SPT <= kMaxSPT, "element masks are 32 bits");
   const int w = wave_id(), lane = lane_id();
 #pragma unroll
   for (int j = 0; j < SPT; ++j) {
-    const uint64_t b = __ballot((bits >> j) & 1ull);
+    const uint64_t b = __ballot((bits >> j) & 1u);
     if (lane == 0) sh.scan[j * SNW + w] = (uint32_t)__popcll(b);
   }
   __syncthreads();
@@ -64,8 +69,8 @@ __device__ __forceinline__ void ordered_ranks(uint64_t bits, SelShared& sh, F&& 
   const uint64_t lt = (1ull << lane) - 1ull;
 #pragma unroll
   for (int j = 0; j < SPT; ++j) {
-    const uint64_t b = __ballot((bits >> j) & 1ull);
-    if ((bits >> j) & 1ull) f(j, sh.scan[j * SNW + w] + (uint32_t)__popcll(b & lt));
+    const uint64_t b = __ballot((bits >> j) & 1u);
+    if ((bits >> j) & 1u) f(j, sh.scan[j * SNW + w] + (uint32_t)__popcll(b & lt));
   }
   __syncthreads();
 }
@@ -113,7 +118,7 @@ __device__ __forceinline__ uint32_t find_digit(SelShared& sh, int nbins, uint32_
 //     remaining 21 bits of the radix select, and the per-workgroup counts
 //     of keys above / equal to the threshold, locally.
 template <int SPT>
-__device__ __forceinline__ uint64_t radix_select_coop(const uint32_t (&key)[SPT], uint32_t m, SelShared& sh,
+__device__ __forceinline__ Mask radix_select_coop(const uint32_t (&key)[SPT], uint32_t m, SelShared& sh,
                                       const SelGroup& g, uint32_t* offset, uint32_t* count,
                                       uint32_t* tau_out, uint32_t* s_qcnt, uint32_t bar_base) {
   const int tid = threadIdx.x;
@@ -136,14 +141,14 @@ __device__ __forceinline__ uint64_t radix_select_coop(const uint32_t (&key)[SPT]
   const uint32_t need1 = m - min(m, gt1);
 
   // --- round 2: publish this workgroup's candidates (keys in bin v1) ----------
-  uint64_t cbits = 0;
+  Mask cbits = 0;
   uint32_t na = 0, nc = 0;
 #pragma unroll
   for (int j = 0; j < SPT; ++j) {
     const uint32_t k = key[j];
     const uint32_t dg = k >> 21;
     if (k != 0u && dg > v1) ++na;
-    if (k != 0u && dg == v1) { cbits |= 1ull << j; ++nc; }
+    if (k != 0u && dg == v1) { cbits |= 1u << j; ++nc; }
   }
   uint32_t tna, tnc;
   (void)block_excl_scan<SNW>(na, sh.tmp, &tna);
@@ -281,12 +286,12 @@ __device__ __forceinline__ uint64_t radix_select_coop(const uint32_t (&key)[SPT]
   const uint32_t te = s_qcnt[4 * P + 1 + g.p];
   __syncthreads();
 
-  uint64_t gt_bits = 0, eq_bits = 0;
+  Mask gt_bits = 0, eq_bits = 0;
 #pragma unroll
   for (int j = 0; j < SPT; ++j) {
     const uint32_t k = key[j];
-    if (k > tau) gt_bits |= 1ull << j;
-    else if (k == tau && k != 0u) eq_bits |= 1ull << j;
+    if (k > tau) gt_bits |= 1u << j;
+    else if (k == tau && k != 0u) eq_bits |= 1u << j;
   }
   // see radix_select for why this is written without a guarded subtraction
   const uint32_t eq_before = min(need, off_eq);
@@ -294,13 +299,13 @@ __device__ __forceinline__ uint64_t radix_select_coop(const uint32_t (&key)[SPT]
   const uint32_t take = min(rem, te);
   *offset = off_gt + eq_before;
   *count = tg + take;
-  uint64_t sel = gt_bits;
+  Mask sel = gt_bits;
   if (take == te) {
     sel |= eq_bits;
   } else if (take > 0) {
-    uint64_t keep = 0;
+    Mask keep = 0;
     ordered_ranks<SPT>(eq_bits, sh, [&](int j, uint32_t r) {
-      if (r < take) keep |= 1ull << j;
+      if (r < take) keep |= 1u << j;
     });
     sel |= keep;
   }
@@ -374,7 +379,7 @@ __device__ __forceinline__ bool sample_window_select(const uint32_t (&key)[SPT],
                                                      uint32_t ns, uint32_t m, uint32_t T,
                                                      SelShared& sh, const SelGroup& g,
                                                      uint32_t* offset, uint32_t* count,
-                                                     uint32_t* tau_out, uint64_t* sel_out,
+                                                     uint32_t* tau_out, Mask* sel_out,
                                                      uint32_t* s_qcnt) {
   const int tid = threadIdx.x, w = wave_id(), lane = lane_id();
   const int P = g.P;
@@ -413,18 +418,18 @@ __device__ __forceinline__ bool sample_window_select(const uint32_t (&key)[SPT],
   const int b_lo = (int)find_digit(sh, 2048, r_lo, &gtx);
   // --- publish: count above the window; window keys in wave-reserved slots ----
   const int wcap = (int)min(g.cap, (int64_t)(SB * kWinPT / P));
-  uint64_t wbits = 0;
+  Mask wbits = 0;
   uint32_t na = 0;
 #pragma unroll
   for (int j = 0; j < SPT; ++j) {
     const uint32_t k = key[j];
     const int bk = value_bin(k, base, inv);
     na += (k != 0u && bk > b_hi) ? 1u : 0u;
-    if (k != 0u && bk >= b_lo && bk <= b_hi) wbits |= 1ull << j;
+    if (k != 0u && bk >= b_lo && bk <= b_hi) wbits |= 1u << j;
   }
   uint32_t wn = 0;
 #pragma unroll
-  for (int j = 0; j < SPT; ++j) wn += (uint32_t)__popcll(__ballot((wbits >> j) & 1ull));
+  for (int j = 0; j < SPT; ++j) wn += (uint32_t)__popcll(__ballot((wbits >> j) & 1u));
   const uint32_t na_w = wave_sum_u32(na);
   uint32_t wbase = 0;
   if (lane == 0) {
@@ -435,9 +440,9 @@ __device__ __forceinline__ bool sample_window_select(const uint32_t (&key)[SPT],
   uint32_t* mywin = g.cand + (int64_t)g.p * g.cap;
 #pragma unroll
   for (int j = 0; j < SPT; ++j) {
-    const uint64_t bj = __ballot((wbits >> j) & 1ull);
+    const uint64_t bj = __ballot((wbits >> j) & 1u);
     const uint32_t r = wbase + (uint32_t)__popcll(bj & lt);
-    if (((wbits >> j) & 1ull) && r < (uint32_t)wcap) st_agent(&mywin[r], key[j]);
+    if (((wbits >> j) & 1u) && r < (uint32_t)wcap) st_agent(&mywin[r], key[j]);
     wbase += (uint32_t)__popcll(bj);
   }
   __syncthreads();
@@ -543,12 +548,12 @@ __device__ __forceinline__ bool sample_window_select(const uint32_t (&key)[SPT],
     c_eqb += (uint32_t)__popcll(__ballot(iseq && u < ulim));
     c_gta += (uint32_t)__popcll(__ballot(isgt));
   }
-  uint64_t gt_bits = 0, eq_bits = 0;
+  Mask gt_bits = 0, eq_bits = 0;
 #pragma unroll
   for (int j = 0; j < SPT; ++j) {
     const uint32_t k = key[j];
-    if (k > tau) gt_bits |= 1ull << j;
-    else if (k == tau && k != 0u) eq_bits |= 1ull << j;
+    if (k > tau) gt_bits |= 1u << j;
+    else if (k == tau && k != 0u) eq_bits |= 1u << j;
   }
   const uint32_t own_gt = wave_sum_u32((uint32_t)__popcll(gt_bits));
   const uint32_t own_eq = wave_sum_u32((uint32_t)__popcll(eq_bits));
@@ -570,13 +575,13 @@ __device__ __forceinline__ bool sample_window_select(const uint32_t (&key)[SPT],
   const uint32_t take = min(rem, te);
   *offset = a_before + gtb + eq_before;
   *count = tg + take;
-  uint64_t sel = gt_bits;
+  Mask sel = gt_bits;
   if (take == te) {
     sel |= eq_bits;
   } else if (take > 0) {
-    uint64_t keep = 0;
+    Mask keep = 0;
     ordered_ranks<SPT>(eq_bits, sh, [&](int j, uint32_t r) {
-      if (r < take) keep |= 1ull << j;
+      if (r < take) keep |= 1u << j;
     });
     sel |= keep;
   }
@@ -584,12 +589,12 @@ __device__ __forceinline__ bool sample_window_select(const uint32_t (&key)[SPT],
   return true;
 }
 
-// With P > 1 this is radix_select_coop; s_qcnt is LDS scratch of >= 5P+1 words.
+// Exact top-m of the keys of one workgroup (the row is not split): three
+// local radix rounds, then ties to the lowest element index.
 template <int SPT>
-__device__ __forceinline__ uint64_t radix_select(const uint32_t (&key)[SPT], uint32_t m, SelShared& sh,
-                                 const SelGroup& g, uint32_t* offset, uint32_t* count,
-                                 uint32_t* tau_out, uint32_t* s_qcnt) {
-  if (g.P > 1) return radix_select_coop<SPT>(key, m, sh, g, offset, count, tau_out, s_qcnt, 0u);
+__device__ __forceinline__ Mask radix_select_local(const uint32_t (&key)[SPT], uint32_t m,
+                                                   SelShared& sh, uint32_t* offset,
+                                                   uint32_t* count, uint32_t* tau_out) {
   const int tid = threadIdx.x;
   uint32_t prefix = 0, pmask = 0, need = m;
   for (int round = 0; round < 3; ++round) {
@@ -612,13 +617,13 @@ __device__ __forceinline__ uint64_t radix_select(const uint32_t (&key)[SPT], uin
   const uint32_t tau = prefix;
   *tau_out = tau;
 
-  uint64_t gt_bits = 0, eq_bits = 0;
+  Mask gt_bits = 0, eq_bits = 0;
   uint32_t cg = 0, ce = 0;
 #pragma unroll
   for (int j = 0; j < SPT; ++j) {
     const uint32_t k = key[j];
-    if (k > tau) { gt_bits |= 1ull << j; ++cg; }
-    else if (k == tau && k != 0u) { eq_bits |= 1ull << j; ++ce; }
+    if (k > tau) { gt_bits |= 1u << j; ++cg; }
+    else if (k == tau && k != 0u) { eq_bits |= 1u << j; ++ce; }
   }
   uint32_t tg, te;
   (void)block_excl_scan<SNW>(cg, sh.tmp, &tg);
@@ -634,17 +639,27 @@ __device__ __forceinline__ uint64_t radix_select(const uint32_t (&key)[SPT], uin
   const uint32_t take = min(rem, te);
   *offset = off_gt + eq_before;
   *count = tg + take;
-  uint64_t sel = gt_bits;
+  Mask sel = gt_bits;
   if (take == te) {
     sel |= eq_bits;
   } else if (take > 0) {
-    uint64_t keep = 0;
+    Mask keep = 0;
     ordered_ranks<SPT>(eq_bits, sh, [&](int j, uint32_t r) {
-      if (r < take) keep |= 1ull << j;
+      if (r < take) keep |= 1u << j;
     });
     sel |= keep;
   }
   return sel;
+}
+
+// Single- or multi-workgroup select (P > 1: radix_select_coop); s_qcnt is LDS
+// scratch of >= 5P+1 words.
+template <int SPT>
+__device__ __forceinline__ Mask radix_select(const uint32_t (&key)[SPT], uint32_t m, SelShared& sh,
+                                             const SelGroup& g, uint32_t* offset, uint32_t* count,
+                                             uint32_t* tau_out, uint32_t* s_qcnt) {
+  if (g.P > 1) return radix_select_coop<SPT>(key, m, sh, g, offset, count, tau_out, s_qcnt, 0u);
+  return radix_select_local<SPT>(key, m, sh, offset, count, tau_out);
 }
 
 }  // namespace sdkv

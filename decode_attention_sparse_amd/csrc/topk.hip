@@ -20,7 +20,7 @@ struct TopkArgs {
   uint32_t* xchg;   // [rows, P, 2]
   uint32_t* bar;    // [rows]
   uint32_t* err;
-  uint32_t* ticket; // workgroup start-order counter (see k_rows)
+  uint32_t* ticket; // [8] workgroup start-order counters (see k_rows)
   int xcd_map;
 };
 
@@ -35,11 +35,10 @@ __global__ __launch_bounds__(SB) void k_topk(TopkArgs a) {
   __shared__ uint32_t s_qcnt[5 * kTopkMaxP + 1];
   const int tid = threadIdx.x;
   // rows are assigned in workgroup start order, as in the decode row kernel
-  __shared__ uint32_t s_ticket;
-  if (tid == 0) s_ticket = atomicAdd(a.ticket, 1u);
+  __shared__ int s_tile;
+  if (tid == 0) s_tile = ticket_tile(a.ticket, a.nrows * a.P, a.xcd_map != 0);
   __syncthreads();
-  const int nb = a.nrows * a.P;
-  const int L = a.xcd_map ? xcd_tile((int)s_ticket, nb) : (int)s_ticket;
+  const int L = s_tile;
   const int p = L % a.P;
   const int64_t row = a.row0 + L / a.P;
   const int64_t t0 = (int64_t)p * a.chunk;
@@ -61,7 +60,7 @@ __global__ __launch_bounds__(SB) void k_topk(TopkArgs a) {
   grp.cand = a.cand + row * a.P * a.chunk;
   grp.cap = a.chunk;
   uint32_t offset, count, tau;
-  const uint64_t sel = radix_select<SPT>(key, (uint32_t)a.k, sh, grp, &offset, &count, &tau, s_qcnt);
+  const Mask sel = radix_select<SPT>(key, (uint32_t)a.k, sh, grp, &offset, &count, &tau, s_qcnt);
   int32_t* out = a.idx + row * a.k;
   ordered_ranks<SPT>(sel, sh, [&](int j, uint32_t r) {
     const int64_t pos = (int64_t)offset + r;
@@ -96,7 +95,7 @@ sdkv_status plan_topk(int64_t rows, int64_t n, int64_t k, TopkPlan* p) {
   q.off_xchg = off;   off += (size_t)rows * q.P * 2 * 4;
   q.off_bar = off;    off += (size_t)rows * 4;
   q.off_err = off;    off += 4;
-  q.off_ticket = off; off += 4;
+  q.off_ticket = off; off += 8 * 4;
   q.zero_bytes = align_up(off, 256);
   q.off_cand = q.zero_bytes;
   q.total = q.off_cand + align_up(q.P > 1 ? (size_t)rows * q.P * q.chunk * 4 : 0, 256);
@@ -134,13 +133,16 @@ sdkv_status launch_topk(const float* scores, int64_t ld, int32_t* idx, float* th
   a.cand = (uint32_t*)(base + p.off_cand);
   const void* kfn = pick_topk_kernel(p.spt);
   if (!kfn) return SDKV_ERR_UNSUPPORTED;
-  a.xcd_map = 0;
+  // per-XCD ticket classes (see k_rows): with P > 1 every class must hold
+  // two rows' workgroups co-resident; each launch also needs whole rows per
+  // class
+  bool xcd_ok = true;
   if (p.P > 1) {
     int cap = 0;
     sdkv_status st = coresident_blocks(kfn, SB, 0, &cap);
     if (st != SDKV_OK) return st;
     if (cap < p.P) return SDKV_ERR_UNSUPPORTED;
-    a.xcd_map = (16 * p.P <= cap) ? 1 : 0;
+    xcd_ok = 16 * p.P <= cap;
   }
   a.ticket = (uint32_t*)(base + p.off_ticket);
   // rows per launch bounded so the grid size fits an int; every launch gets
@@ -148,11 +150,13 @@ sdkv_status launch_topk(const float* scores, int64_t ld, int32_t* idx, float* th
   const int64_t batch = std::max<int64_t>(1, std::min<int64_t>(p.rows, ((int64_t)1 << 30) / p.P));
   for (int64_t r0 = 0; r0 < p.rows; r0 += batch) {
     if (r0 > 0) {
-      hipLaunchKernelGGL(k_fill_zero, dim3(1), dim3(64), 0, stream, a.ticket, (int64_t)1);
+      hipLaunchKernelGGL(k_fill_zero, dim3(1), dim3(64), 0, stream, a.ticket, (int64_t)8);
       if (hipGetLastError() != hipSuccess) return SDKV_ERR_DEVICE;
     }
     a.row0 = (int)r0;
     a.nrows = (int)std::min<int64_t>(batch, p.rows - r0);
+    const int64_t nb = (int64_t)a.nrows * p.P;
+    a.xcd_map = (xcd_ok && nb % 8 == 0 && (nb / 8) % p.P == 0) ? 1 : 0;
     void* args[] = {&a};
     const dim3 grid((unsigned)(a.nrows * p.P)), block(SB);
     if (hipLaunchKernel(kfn, grid, block, args, 0, stream) != hipSuccess) return SDKV_ERR_DEVICE;

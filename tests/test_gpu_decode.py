@@ -170,3 +170,13 @@ def test_qwen_full_model_layers(layer):
     H.log(f"decode qwen layer {layer} (T=262144)")
     case = synth.qwen_layer_case(layer)
     compare(case, run_gpu(case))
+
+
+def test_long_rows_many_workgroups():
+    """262,144 tokens on the 32/8-head layer shape: each row is split over 16
+    workgroups of 16 keys per thread, 512 workgroups in all (more than fit on
+    the device at once), selection across workgroups with the one-barrier
+    window select."""
+    H.log("decode B=1 Hq=32 Hkv=8 T=262144")
+    case = synth.decode_case(B=1, Hq=32, Hkv=8, T=262144, seed=12)
+    compare(case, run_gpu(case))
