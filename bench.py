@@ -292,10 +292,18 @@ def cpu_baseline_decode(case, budget_s):
                       f"{el:.1f} s, fp64 NumPy"}
 
 
-def cpu_baseline_encode(ecase, n_sample, budget_s):
+def cpu_baseline_encode(ecase, budget_s):
+    """The oracle encoder on seeded vectors of the key stream: a 256-vector
+    probe sizes a sample that takes about budget_s seconds."""
     import oracle
     rng = np.random.default_rng(5)
-    pick = np.sort(rng.choice(ecase.x.shape[0], n_sample, replace=False))
+    n = ecase.x.shape[0]
+    probe = np.sort(rng.choice(n, 256, replace=False))
+    t = time.perf_counter()
+    oracle.mp_encode(ecase.x[probe], ecase.dictionary, 16)
+    per = (time.perf_counter() - t) / 256
+    n_sample = int(min(n, max(256, budget_s / max(per, 1e-9))))
+    pick = np.sort(rng.choice(n, n_sample, replace=False))
     t = time.perf_counter()
     oracle.mp_encode(ecase.x[pick], ecase.dictionary, 16)
     el = time.perf_counter() - t
@@ -358,8 +366,7 @@ def main():
         log("cpu baseline (fp64 oracle on host cores)")
         cpu = cpu_baseline_decode(dec["case"], args.cpu_budget)
         if enc is not None:
-            enc["cpu_baseline"] = cpu_baseline_encode(enc["streams"][0]["case"], 1024,
-                                                      args.cpu_budget)
+            enc["cpu_baseline"] = cpu_baseline_encode(enc["streams"][0]["case"], args.cpu_budget)
     ev.close()
     line = {
         "metric": METRIC, "value": round(dec["value"], 1), "unit": "context-tokens/s",
