@@ -112,11 +112,13 @@ struct RowsArgs {
   float* s_low_out;         // optional [rows, T]
   int32_t* sel_out;         // optional [rows, m]
   float* s_high_out;        // optional [rows, m]
-  int32_t* sel;             // [rows, m] workspace list (used when LDS is short)
-  float* s_high;            // [rows, m] workspace
+  int32_t* sel;             // [rows, P, chunk] per-workgroup lists (when LDS is short)
+  float* s_high;            // [rows, P, chunk]
   float* wpart;             // [rows, P, N] per-workgroup unnormalised weights
   float2* stats;            // [rows, P] (local max, local sum of exp)
   uint32_t* ghist;          // [rows, 2048]
+  uint32_t* fhist;          // [rows, 2048] window fine histograms (zeroed per call)
+  uint64_t* bucket;         // [rows, 2048, kBucket] window keys with owner tags
   uint32_t* cand;           // [rows, P, chunk] threshold-bin candidates
   uint32_t* xchg;           // [rows, P, 2]
   uint32_t* bar;            // [rows]
@@ -284,7 +286,11 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   grp.err = a.err;
   grp.cand = a.cand + (int64_t)row * a.P * a.chunk;
   grp.cap = a.chunk;
-  uint32_t offset, count, tau;
+  // offset: this workgroup's first position in the row's selection (token
+  // order); known from the radix selects, exchanged below when needed after
+  // the window select. nbar: cross-workgroup barriers used so far.
+  uint32_t offset = 0, count = 0, tau = 0, nbar = 0;
+  bool need_offset = false;
   Mask sel = 0;
   if (SPT > kMaxCoopSPT || a.P == 1) {
     // single-workgroup rows (the only ones the host plans at SPT > kMaxCoopSPT)
@@ -324,28 +330,51 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
         skey[j] = (tid + j * SB < ns) ? float_key(s) : 0u;
       }
     }
-    if (!sample_window_select<SPT>(key, skey, (uint32_t)ns, (uint32_t)a.m, (uint32_t)a.T, sh, grp,
-                                   &offset, &count, &tau, &sel, s_qcnt))
+    nbar = 1;
+    if (sample_window_select<SPT>(key, skey, (uint32_t)ns, (uint32_t)a.m, (uint32_t)a.T, sh, grp,
+                                  a.fhist + (int64_t)row * 2048,
+                                  a.bucket + (int64_t)row * 2048 * kBucket, &tau, &sel, s_qcnt)) {
+      need_offset = a.sel_out != nullptr || a.s_high_out != nullptr;
+    } else {
       sel = radix_select_coop<SPT>(key, (uint32_t)a.m, sh, grp, &offset, &count, &tau, s_qcnt, 1u);
+      nbar = 3;
+    }
   }
 
   // 4. compaction: the selected tokens of this workgroup in token order, as
-  // offsets within the chunk in LDS (global list when they do not fit).
-  const int64_t cnt = max((int64_t)0, min((int64_t)count, a.m - (int64_t)offset));
+  // offsets within the chunk in LDS (this workgroup's region of the global
+  // list when they do not fit).
+  int32_t* sel_g = a.sel + ((int64_t)row * a.P + p) * a.chunk;
+  float* sh_g = a.s_high + ((int64_t)row * a.P + p) * a.chunk;
+  const uint32_t nsel = ordered_ranks<SPT>(sel, sh, [&](int j, uint32_t r) {
+    if (r < (uint32_t)kListCap) s_lt[r] = (uint16_t)(j * SB + tid);
+    else sel_g[r] = (int32_t)(t0 + (int64_t)j * SB + tid);
+  });
+  const int64_t cnt = nsel;
   const bool in_lds = cnt <= kListCap;
-  int32_t* sel_g = a.sel + (int64_t)row * a.m;        // workspace list (fallback)
-  float* sh_g = a.s_high + (int64_t)row * a.m;
+  if (!in_lds) {
+    // the whole list goes to the global region (entries below kListCap too)
+    for (int64_t i = tid; i < min(cnt, (int64_t)kListCap); i += SB) sel_g[i] = (int32_t)(t0 + s_lt[i]);
+    __threadfence_block();
+  }
+  // debug outputs need the row-global position of this workgroup's entries
+  if (need_offset) {
+    if (tid == 0) st_agent(&grp.xchg[2 * p + 1], nsel);
+    group_barrier(grp.bar, (uint32_t)a.P * (nbar + 1u), grp.err);
+    if (tid == 0) {
+      uint32_t off = 0;
+      for (int q = 0; q < p; ++q) off += ld_agent(&grp.xchg[2 * q + 1]);
+      sh.bcast[6] = off;
+    }
+    __syncthreads();
+    offset = sh.bcast[6];
+    __syncthreads();
+  }
   int32_t* sel_dbg = a.sel_out ? a.sel_out + (int64_t)row * a.m : nullptr;
   float* sh_dbg = a.s_high_out ? a.s_high_out + (int64_t)row * a.m : nullptr;
-  ordered_ranks<SPT>(sel, sh, [&](int j, uint32_t r) {
-    const int64_t pos = (int64_t)offset + r;
-    if (pos >= a.m) return;
-    const int32_t t = (int32_t)(t0 + (int64_t)j * SB + tid);
-    if (in_lds) s_lt[r] = (uint16_t)(j * SB + tid);
-    else sel_g[pos] = t;
-    if (sel_dbg) sel_dbg[pos] = t;
-  });
-  if (!in_lds) __threadfence_block();
+  if (sel_dbg)
+    for (int64_t i = tid; i < cnt; i += SB)
+      if ((int64_t)offset + i < a.m) sel_dbg[offset + i] = in_lds ? (int32_t)(t0 + s_lt[i]) : sel_g[i];
   __syncthreads();
 
   // 5. Khigh rescore, one thread per selected token (entries i = tid + k*SB;
@@ -364,7 +393,7 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
     for (int r = 0; r < kTokBatch; ++r) {
       const int64_t i = base + (int64_t)r * SB + tid;
       int64_t t = t0;
-      if (i < cnt) t = in_lds ? t0 + s_lt[i] : (int64_t)sel_g[offset + i];
+      if (i < cnt) t = in_lds ? t0 + s_lt[i] : (int64_t)sel_g[i];
       tt[r] = min(max(t, (int64_t)0), a.T - 1);
     }
     uint32_t kw[kTokBatch][32];
@@ -390,8 +419,8 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
       }
       if (i < cnt) {
         if (in_lds) s_ls[i] = s;
-        else sh_g[offset + i] = s;
-        if (sh_dbg) sh_dbg[offset + i] = s;
+        else sh_g[i] = s;
+        if (sh_dbg && (int64_t)offset + i < a.m) sh_dbg[offset + i] = s;
         if (s > lmax) {
           vb = vb * __expf(lmax - s) + va;
           lmax = s;
@@ -427,7 +456,7 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
       for (int r = 0; r < kTokBatch; ++r) {
         const int64_t i = base + (int64_t)r * SB + tid;
         int64_t t = t0;
-        if (i < cnt) t = in_lds ? t0 + s_lt[i] : (int64_t)sel_g[offset + i];
+        if (i < cnt) t = in_lds ? t0 + s_lt[i] : (int64_t)sel_g[i];
         tt[r] = min(max(t, (int64_t)0), a.T - 1);
       }
 #pragma unroll
@@ -436,7 +465,7 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
 #pragma unroll
     for (int r = 0; r < kTokBatch; ++r) {
       const int64_t i = base + (int64_t)r * SB + tid;
-      pt[r] = (i < cnt) ? (in_lds ? s_ls[i] : sh_g[offset + i]) : -INFINITY;
+      pt[r] = (i < cnt) ? (in_lds ? s_ls[i] : sh_g[i]) : -INFINITY;
     }
 #pragma unroll
     for (int r = 0; r < kTokBatch; ++r) {
@@ -788,12 +817,14 @@ sdkv_status plan_decode(const sdkv_attn_args* a, DecodePlan* p) {
   const int64_t N = a->n_atoms, rows = q.rows;
   size_t off = 0;
   q.off_u = off;      off = align_up(off + (size_t)rows * N * 4, A);
-  q.off_sel = off;    off = align_up(off + (size_t)rows * q.m * 4, A);
-  q.off_shigh = off;  off = align_up(off + (size_t)rows * q.m * 4, A);
+  const size_t list = (size_t)rows * q.P * q.chunk * 4;  // per-workgroup regions
+  q.off_sel = off;    off = align_up(off + list, A);
+  q.off_shigh = off;  off = align_up(off + list, A);
   q.off_wpart = off;  off = align_up(off + (size_t)rows * q.P * N * 4, A);
   q.off_stats = off;  off = align_up(off + (size_t)rows * q.P * 8, A);
   q.off_zero = off;
   q.off_ghist = off;  off += (q.P > 1) ? (size_t)rows * 2048 * 4 : 0;
+  q.off_fhist = off;  off += (q.P > 1) ? (size_t)rows * 2048 * 4 : 0;
   q.off_xchg = off;   off += (size_t)rows * q.P * 2 * 4;
   q.off_bar = off;    off += (size_t)rows * 4;
   q.off_err = off;    off += 4;
@@ -802,6 +833,7 @@ sdkv_status plan_decode(const sdkv_attn_args* a, DecodePlan* p) {
   q.zero_bytes = off - q.off_zero;
   q.off_opart = off;  off = align_up(off + (size_t)q.nchunks * rows * a->d * 4, A);
   q.off_cand = off;   off = align_up(off + (q.P > 1 ? (size_t)rows * q.P * q.chunk * 4 : 0), A);
+  q.off_bucket = off; off = align_up(off + (q.P > 1 ? (size_t)rows * 2048 * kBucket * 8 : 0), A);
   q.total = off;
   *p = q;
   return SDKV_OK;
@@ -883,6 +915,8 @@ sdkv_status launch_decode(const sdkv_attn_args* a, const DecodePlan& p, void* ws
   ra.wpart = wpart;
   ra.stats = stats;
   ra.ghist = ghist;
+  ra.fhist = (uint32_t*)(base + p.off_fhist);
+  ra.bucket = (uint64_t*)(base + p.off_bucket);
   ra.cand = (uint32_t*)(base + p.off_cand);
   ra.xchg = xchg;
   ra.bar = bar;

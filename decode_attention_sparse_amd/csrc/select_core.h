@@ -48,9 +48,10 @@ using Mask = uint32_t;
 constexpr int kMaxSPT = 32;
 
 // Calls f(j, rank) for every set bit j of `bits`, where rank is the position
-// of slot j among all set slots of the block in element order.
+// of slot j among all set slots of the block in element order. Returns the
+// number of set slots in the block.
 template <int SPT, class F>
-__device__ __forceinline__ void ordered_ranks(Mask bits, SelShared& sh, F&& f) {
+__device__ __forceinline__ uint32_t ordered_ranks(Mask bits, SelShared& sh, F&& f) {
   static_assert(SPT * SNW <= SB, "rank table exceeds block");
   static_assert(SPT <= kMaxSPT, "element masks are 32 bits");
   const int w = wave_id(), lane = lane_id();
@@ -73,13 +74,15 @@ __device__ __forceinline__ void ordered_ranks(Mask bits, SelShared& sh, F&& f) {
     if ((bits >> j) & 1u) f(j, sh.scan[j * SNW + w] + (uint32_t)__popcll(b & lt));
   }
   __syncthreads();
+  return tot;
 }
 
 // Finds digit v of an nbins-bin histogram in sh.hist with
-// #(digit > v) < need <= #(digit >= v). Returns v; *above = #(digit > v).
-// Uniform across the block. (If fewer than `need` keys exist, v = 0.)
+// #(digit > v) < need <= #(digit >= v). Returns v; *above = #(digit > v);
+// *total (optional) = the histogram's total. Uniform across the block. (If
+// fewer than `need` keys exist, v = 0 and *above = 0.)
 __device__ __forceinline__ uint32_t find_digit(SelShared& sh, int nbins, uint32_t need,
-                                               uint32_t* above_out) {
+                                               uint32_t* above_out, uint32_t* total = nullptr) {
   const int tid = threadIdx.x;
   const int bpt = nbins / SB;
   uint32_t loc = 0;
@@ -106,6 +109,7 @@ __device__ __forceinline__ uint32_t find_digit(SelShared& sh, int nbins, uint32_
   __syncthreads();
   const uint32_t v = sh.bcast[0];
   *above_out = sh.bcast[1];
+  if (total) *total = tot;
   __syncthreads();
   return v;
 }
@@ -357,33 +361,42 @@ __device__ __forceinline__ int value_bin(uint32_t k, float base, float inv) {
 
 constexpr int kSampleN = 4096;             // shared sample size (tokens)
 constexpr int kSamplePT = kSampleN / SB;
-constexpr int kWinPT = 16;                 // window keys per thread in registers
 
-// Sample-window select with one cross-workgroup synchronisation. Every
-// workgroup of the row holds the keys `skey` of the same fixed sample of ns
-// of the row's T elements, so all derive the same window of value bins
-// around the sample's estimate of the m-th largest key (the bins of sample
-// ranks m ns / T -/+ (5 standard deviations + 4), on a linear scale between
-// the sample's smallest and largest value). Each workgroup publishes its
-// count of keys above the window and its keys inside it; after one barrier
-// every workgroup reads them all and finishes the select locally (a fine
-// linear histogram of the window keys, then exact ranks inside one bin).
-// That the window holds the m-th largest key is checked exactly (fewer than
-// m keys above it, at least m at or above its bottom); if that fails, or a
-// workgroup's window keys exceed its slots, the function returns false
-// having used one barrier and changed nothing else, and the caller runs
-// the two-synchronisation select. The result is exact either way.
+constexpr int kBucket = 16;  // keys kept per fine bin of a row's window
+
+// Sample-window select with one cross-workgroup synchronisation.
+//
+// Every workgroup of the row holds the keys `skey` of the same fixed sample
+// of ns of the row's T elements, so all derive the same window: the value
+// range between the sample's order statistics of rank m ns / T -/+ (5
+// standard deviations + 4), found with a linear 2048-bin histogram between
+// the sample's smallest and largest value. The window is divided into 2048
+// fine bins on a linear value scale (all bin functions are monotone in the
+// key, see value_bin). Each workgroup then
+//   * counts its keys above the window (published in xchg[2p]), and
+//   * adds each of its keys inside the window to the row's fine histogram
+//     `fh` (a global atomic), whose return value gives the key a slot in its
+//     bin's bucket `bkt` (kBucket keys per bin, tagged with the workgroup).
+// After the one barrier every workgroup reads the P counts and the 2048-bin
+// histogram, finds the bin holding the threshold, and reads only that bin's
+// bucket: the threshold is its need-th largest key, and the bucket's owner
+// tags give every workgroup's count of keys equal to it (for the tie quota,
+// lowest element index first). Keys above the threshold need no exchange:
+// each workgroup selects its own. If the window misses the threshold, or
+// the threshold's bin overflowed its bucket, the function returns false
+// having used one barrier, and the caller runs the two-barrier radix select;
+// the result is exact either way. The selection's global output offset is
+// not computed here (callers that need it exchange counts).
 template <int SPT>
 __device__ __forceinline__ bool sample_window_select(const uint32_t (&key)[SPT],
                                                      const uint32_t (&skey)[kSamplePT],
                                                      uint32_t ns, uint32_t m, uint32_t T,
                                                      SelShared& sh, const SelGroup& g,
-                                                     uint32_t* offset, uint32_t* count,
+                                                     uint32_t* fh, uint64_t* bkt,
                                                      uint32_t* tau_out, Mask* sel_out,
                                                      uint32_t* s_qcnt) {
   const int tid = threadIdx.x, w = wave_id(), lane = lane_id();
   const int P = g.P;
-  const uint64_t lt = (1ull << lane) - 1ull;
   // --- sample value range ------------------------------------------------------
   uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
 #pragma unroll
@@ -395,7 +408,7 @@ __device__ __forceinline__ bool sample_window_select(const uint32_t (&key)[SPT],
     kmx = max(kmx, (uint32_t)__shfl_xor((int)kmx, o, 64));
   }
   if (lane == 0) { sh.tmp[w] = kmn; sh.tmp[SNW + w] = kmx; }
-  if (tid == 0) { sh.bcast[4] = 0u; sh.bcast[5] = 0u; sh.bcast[6] = 0u; }
+  if (tid == 0) { sh.bcast[5] = 0u; sh.bcast[7] = 0u; }
   for (int i = tid; i < 2048; i += SB) sh.hist[i] = 0u;
   __syncthreads();
 #pragma unroll
@@ -416,138 +429,98 @@ __device__ __forceinline__ bool sample_window_select(const uint32_t (&key)[SPT],
   uint32_t gtx;
   const int b_hi = (int)find_digit(sh, 2048, r_hi, &gtx);
   const int b_lo = (int)find_digit(sh, 2048, r_lo, &gtx);
-  // --- publish: count above the window; window keys in wave-reserved slots ----
-  const int wcap = (int)min(g.cap, (int64_t)(SB * kWinPT / P));
-  Mask wbits = 0;
-  uint32_t na = 0;
-#pragma unroll
-  for (int j = 0; j < SPT; ++j) {
-    const uint32_t k = key[j];
-    const int bk = value_bin(k, base, inv);
-    na += (k != 0u && bk > b_hi) ? 1u : 0u;
-    if (k != 0u && bk >= b_lo && bk <= b_hi) wbits |= 1u << j;
-  }
-  uint32_t wn = 0;
-#pragma unroll
-  for (int j = 0; j < SPT; ++j) wn += (uint32_t)__popcll(__ballot((wbits >> j) & 1u));
-  const uint32_t na_w = wave_sum_u32(na);
-  uint32_t wbase = 0;
-  if (lane == 0) {
-    wbase = atomicAdd(&sh.bcast[4], wn);
-    atomicAdd(&sh.bcast[5], na_w);
-  }
-  wbase = (uint32_t)__shfl((int)wbase, 0, 64);
-  uint32_t* mywin = g.cand + (int64_t)g.p * g.cap;
-#pragma unroll
-  for (int j = 0; j < SPT; ++j) {
-    const uint64_t bj = __ballot((wbits >> j) & 1u);
-    const uint32_t r = wbase + (uint32_t)__popcll(bj & lt);
-    if (((wbits >> j) & 1u) && r < (uint32_t)wcap) st_agent(&mywin[r], key[j]);
-    wbase += (uint32_t)__popcll(bj);
-  }
-  __syncthreads();
-  if (tid == 0) {
-    st_agent(&g.xchg[2 * g.p], sh.bcast[5]);
-    st_agent(&g.xchg[2 * g.p + 1], sh.bcast[4]);
-  }
-  group_barrier(g.bar, (uint32_t)P, g.err);
-  // --- read every workgroup's counts and window keys --------------------------
-  // slot u = q * wcap + r belongs to workgroup q; loads are branch-free (the
-  // index is clamped, unused slots are masked after)
-  const uint32_t nslots = (uint32_t)(P * wcap);
-  uint32_t ck[kWinPT];
-#pragma unroll
-  for (int k = 0; k < kWinPT; ++k) {
-    const uint32_t u = min((uint32_t)(tid + k * SB), nslots - 1u);
-    ck[k] = ld_agent(&g.cand[(int64_t)(u / wcap) * g.cap + (u % wcap)]);
-  }
-  if (tid < P) {
-    s_qcnt[tid] = ld_agent(&g.xchg[2 * tid]);
-    s_qcnt[P + tid] = ld_agent(&g.xchg[2 * tid + 1]);
-  }
-  if (tid < 5) s_qcnt[2 * P + tid] = 0u;
-  __syncthreads();
-  uint32_t A = 0, total = 0, a_before = 0;
-  bool overflow = false;
-  for (int q = 0; q < P; ++q) {
-    A += s_qcnt[q];
-    a_before += (q < g.p) ? s_qcnt[q] : 0u;
-    total += s_qcnt[P + q];
-    overflow |= s_qcnt[P + q] > (uint32_t)wcap;
-  }
-  if (overflow || A >= m || m - A > total) {
-    __syncthreads();
-    return false;
-  }
-#pragma unroll
-  for (int k = 0; k < kWinPT; ++k) {
-    const uint32_t u = (uint32_t)(tid + k * SB);
-    const uint32_t uc = min(u, nslots - 1u);
-    const bool live = u < nslots && (uc % wcap) < s_qcnt[P + uc / wcap];
-    ck[k] = live ? ck[k] : 0u;
-  }
-  // --- the threshold: the need1-th largest window key -------------------------
-  const uint32_t need1 = m - A;
   float base2 = base, inv2 = 0.f;
   if (inv > 0.f) {
     base2 = base + (float)b_lo / inv;
     inv2 = inv * (2048.f / (float)(b_hi - b_lo + 1));
   }
-  for (int i = tid; i < 2048; i += SB) sh.hist[i] = 0u;
-  __syncthreads();
+  // --- publish: count above the window; window keys into the fine histogram ---
+  // in batches of 8 keys: all fine bins, then all histogram atomics (their
+  // returned slots are not waited for until the batch's stores)
+  uint32_t na = 0;
+  constexpr int PB = SPT < 8 ? SPT : 8;
 #pragma unroll
-  for (int k = 0; k < kWinPT; ++k)
-    if (ck[k] != 0u) atomicAdd(&sh.hist[value_bin(ck[k], base2, inv2)], 1u);
+  for (int j0 = 0; j0 < SPT; j0 += PB) {
+    int fbv[PB];
+#pragma unroll
+    for (int jj = 0; jj < PB; ++jj) {
+      const uint32_t k = key[j0 + jj];
+      const int bk = value_bin(k, base, inv);
+      na += (k != 0u && bk > b_hi) ? 1u : 0u;
+      fbv[jj] = (k != 0u && bk >= b_lo && bk <= b_hi) ? value_bin(k, base2, inv2) : -1;
+    }
+    uint32_t slot[PB];
+#pragma unroll
+    for (int jj = 0; jj < PB; ++jj) {
+      slot[jj] = (uint32_t)kBucket;
+      if (fbv[jj] >= 0) slot[jj] = atomicAdd(&fh[fbv[jj]], 1u);
+    }
+#pragma unroll
+    for (int jj = 0; jj < PB; ++jj)
+      if (slot[jj] < (uint32_t)kBucket)
+        __hip_atomic_store(&bkt[fbv[jj] * kBucket + slot[jj]], ((uint64_t)g.p << 32) | key[j0 + jj],
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  const uint32_t na_w = wave_sum_u32(na);
+  if (lane == 0) atomicAdd(&sh.bcast[5], na_w);
   __syncthreads();
-  uint32_t gt2;
-  const int bstar = (int)find_digit(sh, 2048, need1, &gt2);
-  const uint32_t need2 = need1 - min(need1, gt2);
+  if (tid == 0) st_agent(&g.xchg[2 * g.p], sh.bcast[5]);
+  group_barrier(g.bar, (uint32_t)P, g.err);
+  // --- threshold bin from the counts above and the fine histogram -------------
+  if (tid < P) s_qcnt[tid] = ld_agent(&g.xchg[2 * tid]);
+  for (int i = tid; i < 2048; i += SB) sh.hist[i] = ld_agent(&fh[i]);
+  __syncthreads();
+  uint32_t A = 0;
+  for (int q = 0; q < P; ++q) A += s_qcnt[q];
+  if (A >= m) {
+    __syncthreads();
+    return false;
+  }
+  const uint32_t need1 = m - A;
+  uint32_t gt2, total;
+  const int bstar = (int)find_digit(sh, 2048, need1, &gt2, &total);
   const uint32_t nc = sh.hist[bstar];
-  uint32_t tau;
-  if (nc <= (uint32_t)SB) {
-    // gather the bin's keys (wave-aggregated slots), then exact ranks
-#pragma unroll
-    for (int k = 0; k < kWinPT; ++k) {
-      const bool in = ck[k] != 0u && value_bin(ck[k], base2, inv2) == bstar;
-      const uint64_t bk = __ballot(in);
-      if (bk) {
-        uint32_t b0 = 0;
-        if (lane == 0) b0 = atomicAdd(&sh.bcast[6], (uint32_t)__popcll(bk));
-        b0 = (uint32_t)__shfl((int)b0, 0, 64);
-        if (in) sh.scan[b0 + (uint32_t)__popcll(bk & lt)] = ck[k];
-      }
-    }
+  if (total < need1 || nc > (uint32_t)kBucket) {
     __syncthreads();
-    if ((uint32_t)tid < nc) {
-      const uint32_t x = sh.scan[tid];
-      uint32_t ngt = 0, nge = 0;
-      for (uint32_t i = 0; i < nc; ++i) {
-        const uint32_t y = sh.scan[i];
-        ngt += y > x ? 1u : 0u;
-        nge += y >= x ? 1u : 0u;
-      }
-      if (ngt < need2 && need2 <= nge) sh.bcast[7] = x;
-    }
-    __syncthreads();
-    tau = sh.bcast[7];
-    __syncthreads();
-  } else {
-    tau = local_kth<kWinPT>(ck, need1, sh, 0, 0u);
+    return false;
   }
+  const uint32_t need2 = need1 - gt2;  // 1 <= need2 <= nc
+  // --- the threshold's bucket: exact rank, ties by workgroup ------------------
+  if (tid < (int)nc) {
+    const uint64_t e = __hip_atomic_load(&bkt[bstar * kBucket + tid], __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    sh.scan[tid] = (uint32_t)e;
+    sh.scan[kBucket + tid] = (uint32_t)(e >> 32);
+  }
+  __syncthreads();
+  if (tid < (int)nc) {
+    const uint32_t x = sh.scan[tid];
+    uint32_t ngt = 0, nge = 0;
+    for (uint32_t i = 0; i < nc; ++i) {
+      const uint32_t y = sh.scan[i];
+      ngt += y > x ? 1u : 0u;
+      nge += y >= x ? 1u : 0u;
+    }
+    if (ngt < need2 && need2 <= nge) sh.bcast[7] = x;
+  }
+  __syncthreads();
+  const uint32_t tau = sh.bcast[7];
+  // bucket keys above tau (all workgroups), equal to tau before / at this one
+  uint32_t b_gt = 0, eq_before = 0, te = 0;
+  for (uint32_t i = 0; i < nc; ++i) {
+    const uint32_t y = sh.scan[i], q = sh.scan[kBucket + i];
+    b_gt += y > tau ? 1u : 0u;
+    eq_before += (y == tau && q < (uint32_t)g.p) ? 1u : 0u;
+    te += (y == tau && q == (uint32_t)g.p) ? 1u : 0u;
+  }
+  __syncthreads();
   *tau_out = tau;
-  // --- counts around tau: window keys of earlier workgroups, all window keys
-  // above tau, and this workgroup's own keys above / equal to tau ------------
-  const uint32_t ulim = (uint32_t)(g.p * wcap);
-  uint32_t c_gtb = 0, c_eqb = 0, c_gta = 0;
-#pragma unroll
-  for (int k = 0; k < kWinPT; ++k) {
-    const uint32_t u = (uint32_t)(tid + k * SB);
-    const uint32_t x = ck[k];
-    const bool isgt = x != 0u && x > tau, iseq = x != 0u && x == tau;
-    c_gtb += (uint32_t)__popcll(__ballot(isgt && u < ulim));
-    c_eqb += (uint32_t)__popcll(__ballot(iseq && u < ulim));
-    c_gta += (uint32_t)__popcll(__ballot(isgt));
-  }
+  // keys equal to tau to take, handed out in workgroup (element) order; see
+  // radix_select_local for why this is written without a guarded subtraction
+  const uint32_t need = need2 - min(need2, b_gt);
+  const uint32_t eb = min(need, eq_before);
+  const uint32_t rem = need - eb;
+  const uint32_t take = min(rem, te);
   Mask gt_bits = 0, eq_bits = 0;
 #pragma unroll
   for (int j = 0; j < SPT; ++j) {
@@ -555,26 +528,6 @@ __device__ __forceinline__ bool sample_window_select(const uint32_t (&key)[SPT],
     if (k > tau) gt_bits |= 1u << j;
     else if (k == tau && k != 0u) eq_bits |= 1u << j;
   }
-  const uint32_t own_gt = wave_sum_u32((uint32_t)__popcll(gt_bits));
-  const uint32_t own_eq = wave_sum_u32((uint32_t)__popcll(eq_bits));
-  if (lane == 0) {
-    atomicAdd(&s_qcnt[2 * P + 0], c_gtb);
-    atomicAdd(&s_qcnt[2 * P + 1], c_eqb);
-    atomicAdd(&s_qcnt[2 * P + 2], c_gta);
-    atomicAdd(&s_qcnt[2 * P + 3], own_gt);
-    atomicAdd(&s_qcnt[2 * P + 4], own_eq);
-  }
-  __syncthreads();
-  const uint32_t gtb = s_qcnt[2 * P + 0], eqb = s_qcnt[2 * P + 1], gt_all = s_qcnt[2 * P + 2];
-  const uint32_t tg = s_qcnt[2 * P + 3], te = s_qcnt[2 * P + 4];
-  __syncthreads();
-  const uint32_t need = need1 - min(need1, gt_all);  // keys equal to tau to take
-  // see radix_select for why this is written without a guarded subtraction
-  const uint32_t eq_before = min(need, eqb);
-  const uint32_t rem = need - eq_before;
-  const uint32_t take = min(rem, te);
-  *offset = a_before + gtb + eq_before;
-  *count = tg + take;
   Mask sel = gt_bits;
   if (take == te) {
     sel |= eq_bits;
