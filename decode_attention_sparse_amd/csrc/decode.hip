@@ -117,11 +117,10 @@ struct RowsArgs {
   float* wpart;             // [rows, P, N] per-workgroup unnormalised weights
   float2* stats;            // [rows, P] (local max, local sum of exp)
   uint32_t* ghist;          // [rows, 2048]
-  uint32_t* fhist;          // [rows, 2048] window fine histograms (zeroed per call)
-  uint64_t* bucket;         // [rows, 2048, kBucket] window keys with owner tags
+  uint32_t* wtab;           // [rows, P, 2048] window tables: count | start << 16
   uint32_t* cand;           // [rows, P, chunk] threshold-bin candidates
   uint32_t* xchg;           // [rows, P, 2]
-  uint32_t* bar;            // [rows]
+  uint32_t* bar;            // [rows, 2] barrier counters
   uint32_t* err;
   uint32_t* ticket;         // [8] workgroup start-order counters, zeroed per call
   int xcd_map;              // per-XCD ticket classes (rows stay on one XCD)
@@ -282,7 +281,8 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   grp.p = p;
   grp.ghist = a.ghist + (int64_t)row * 2048;
   grp.xchg = a.xchg + (int64_t)row * a.P * 2;
-  grp.bar = a.bar + row;
+  grp.bar = a.bar + 2 * (int64_t)row;
+  grp.local = a.xcd_map != 0;
   grp.err = a.err;
   grp.cand = a.cand + (int64_t)row * a.P * a.chunk;
   grp.cap = a.chunk;
@@ -332,8 +332,7 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
     }
     nbar = 1;
     if (sample_window_select<SPT>(key, skey, (uint32_t)ns, (uint32_t)a.m, (uint32_t)a.T, sh, grp,
-                                  a.fhist + (int64_t)row * 2048,
-                                  a.bucket + (int64_t)row * 2048 * kBucket, &tau, &sel, s_qcnt)) {
+                                  a.wtab + (int64_t)row * a.P * 2048, &tau, &sel, s_qcnt)) {
       need_offset = a.sel_out != nullptr || a.s_high_out != nullptr;
     } else {
       sel = radix_select_coop<SPT>(key, (uint32_t)a.m, sh, grp, &offset, &count, &tau, s_qcnt, 1u);
@@ -360,7 +359,7 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   // debug outputs need the row-global position of this workgroup's entries
   if (need_offset) {
     if (tid == 0) st_agent(&grp.xchg[2 * p + 1], nsel);
-    group_barrier(grp.bar, (uint32_t)a.P * (nbar + 1u), grp.err);
+    group_barrier(grp.bar, (uint32_t)a.P, nbar + 1u, grp.local, grp.err);
     if (tid == 0) {
       uint32_t off = 0;
       for (int q = 0; q < p; ++q) off += ld_agent(&grp.xchg[2 * q + 1]);
@@ -574,50 +573,12 @@ __device__ __forceinline__ void wdv_merge16(const WdvArgs& a, const float* s_coe
   }
 }
 
-// 8 merged weights W[row][a0 .. a0+8) (zero outside the matrix); all loads of
-// up to 8 partials are issued before the multiply-adds.
-__device__ __forceinline__ void wdv_merge8(const WdvArgs& a, const float* s_coef, int r, int row,
-                                           int a0, float (&v)[8]) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = 0.f;
-  if (row >= a.rows) return;
-  const float* src = a.wpart + (int64_t)row * a.P * a.N + a0;
-  if (a0 + 8 <= a.N && (a.N & 3) == 0) {
-    for (int q0 = 0; q0 < a.P; q0 += 8) {
-      float4 x[8][2];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        if (q0 + q < a.P) {
-          const float4* sp = (const float4*)(src + (int64_t)(q0 + q) * a.N);
-          x[q][0] = sp[0];
-          x[q][1] = sp[1];
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        if (q0 + q < a.P) {
-          const float c = s_coef[r * kMaxRowP + q0 + q];
-          v[0] = fmaf(c, x[q][0].x, v[0]); v[1] = fmaf(c, x[q][0].y, v[1]);
-          v[2] = fmaf(c, x[q][0].z, v[2]); v[3] = fmaf(c, x[q][0].w, v[3]);
-          v[4] = fmaf(c, x[q][1].x, v[4]); v[5] = fmaf(c, x[q][1].y, v[5]);
-          v[6] = fmaf(c, x[q][1].z, v[6]); v[7] = fmaf(c, x[q][1].w, v[7]);
-        }
-      }
-    }
-  } else {
-    for (int q = 0; q < a.P; ++q) {
-      const float c = s_coef[r * kMaxRowP + q];
-      for (int e = 0; e < 8 && a0 + e < a.N; ++e) v[e] = fmaf(c, src[(int64_t)q * a.N + e], v[e]);
-    }
-  }
-  if (a.w_out) {
-    float* wo = a.w_out + (int64_t)row * a.N + a0;
-    for (int e = 0; e < 8 && a0 + e < a.N; ++e) wo[e] = v[e];
-  }
-}
-
 // 512 threads: the A tile (32 rows x 128 atoms) is merged 8 atoms per thread;
-// wave w computes output columns [16w, 16w+16) for both 16-row tiles.
+// wave w computes output columns [16w, 16w+16) for both 16-row tiles. The
+// loads of a sub-chunk (up to 8 weight partials per thread and the Dv rows)
+// are issued before anything waits on them; the first sub-chunk's loads go
+// out before the softmax-merge coefficients are computed.
+constexpr int WDV_PQ = 8;                 // partials per prefetched batch
 __global__ __launch_bounds__(512) void k_wdv_bf16(WdvArgs a) {
   __shared__ float s_coef[WRT * kMaxRowP];
   __shared__ __attribute__((aligned(16))) uint16_t s_ahi[WRT * WPITCH];
@@ -628,52 +589,127 @@ __global__ __launch_bounds__(512) void k_wdv_bf16(WdvArgs a) {
   const int L = xcd_tile(blockIdx.x, a.nchunks * a.nrt);
   const int chunk = L / a.nrt, rt = L % a.nrt;
   const int r0 = rt * WRT;
-  for (int r = w; r < WRT; r += 8) {
-    const int row = r0 + r;
-    float Mq = -INFINITY, lq = 0.f;
-    if (row < a.rows && l < a.P) {
-      const float2 st = a.stats[(int64_t)row * a.P + l];
-      Mq = st.x;
-      lq = st.y;
-    }
-    const float Mx = wave_max(Mq);
-    const float c = (lq > 0.f) ? __expf(Mq - Mx) : 0.f;
-    const float Lr = wave_sum(c * lq);
-    if (l < a.P) s_coef[r * kMaxRowP + l] = (Lr > 0.f) ? c / Lr : 0.f;
-  }
-  __syncthreads();
   const uint16_t* dv = (const uint16_t*)a.dv;
   const int ncol = a.d >> 4;
+  // this thread's A slot (row r, atoms c0 .. c0+8) and B items
+  const int ar = tid >> 4, ac0 = (tid & 15) * 8;
+  const int arow = r0 + ar;
+  const bool a_fast = (a.N & 3) == 0;
+  constexpr int BIT = (WSUB / 2) * (128 / 8) / 512;  // B items per thread (d = 128)
+  float4 px[WDV_PQ][2];
+  u32x4 bx[BIT][2];
+  auto load_sub = [&](int a0) {
+#pragma unroll
+    for (int q = 0; q < WDV_PQ; ++q) {
+      px[q][0] = make_float4(0.f, 0.f, 0.f, 0.f);
+      px[q][1] = px[q][0];
+      if (q < a.P && arow < a.rows && a_fast && a0 + ac0 + 8 <= a.N) {
+        const float4* sp = (const float4*)(a.wpart + ((int64_t)arow * a.P + q) * a.N + a0 + ac0);
+        px[q][0] = sp[0];
+        px[q][1] = sp[1];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < BIT; ++k) {
+      const int it = tid + k * 512;
+      const int ap = it % (WSUB / 2), sg = it / (WSUB / 2);
+      const int atom = a0 + 2 * ap;
+      bx[k][0] = u32x4{0u, 0u, 0u, 0u};
+      bx[k][1] = bx[k][0];
+      if (sg < (a.d >> 3)) {
+        if (atom < a.N) bx[k][0] = *(const u32x4*)(dv + (int64_t)atom * a.d + 8 * sg);
+        if (atom + 1 < a.N) bx[k][1] = *(const u32x4*)(dv + (int64_t)(atom + 1) * a.d + 8 * sg);
+      }
+    }
+  };
+  int a0 = chunk * a.nsub * WSUB;
+  if (a0 < a.N) load_sub(a0);
+
+  // softmax-merge coefficients of the tile's rows (all stats loads first)
+  {
+    float2 st[WRT / 8];
+#pragma unroll
+    for (int k = 0; k < WRT / 8; ++k) {
+      const int row = r0 + w + 8 * k;
+      st[k] = make_float2(-INFINITY, 0.f);
+      if (row < a.rows && l < a.P) st[k] = a.stats[(int64_t)row * a.P + l];
+    }
+#pragma unroll
+    for (int k = 0; k < WRT / 8; ++k) {
+      const float Mq = st[k].x, lq = st[k].y;
+      const float Mx = wave_max(Mq);
+      const float c = (lq > 0.f) ? __expf(Mq - Mx) : 0.f;
+      const float Lr = wave_sum(c * lq);
+      if (l < a.P) s_coef[(w + 8 * k) * kMaxRowP + l] = (Lr > 0.f) ? c / Lr : 0.f;
+    }
+  }
+  __syncthreads();
   f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 
   for (int sub = 0; sub < a.nsub; ++sub) {
-    const int a0 = (chunk * a.nsub + sub) * WSUB;
+    a0 = (chunk * a.nsub + sub) * WSUB;
     if (a0 >= a.N) break;
-    // A: merged weights, split into bf16 hi + lo
+    if (sub > 0) load_sub(a0);
+    // A: merged weights of (row ar, atoms ac0 .. ac0+8), split into bf16 hi + lo
     {
-      const int r = tid >> 4, c0 = (tid & 15) * 8;
       float v[8];
-      wdv_merge8(a, s_coef, r, r0 + r, a0 + c0, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = 0.f;
+      if (arow < a.rows) {
+        if (a_fast && a0 + ac0 + 8 <= a.N) {
+#pragma unroll
+          for (int q = 0; q < WDV_PQ; ++q) {
+            if (q < a.P) {
+              const float c = s_coef[ar * kMaxRowP + q];
+              v[0] = fmaf(c, px[q][0].x, v[0]); v[1] = fmaf(c, px[q][0].y, v[1]);
+              v[2] = fmaf(c, px[q][0].z, v[2]); v[3] = fmaf(c, px[q][0].w, v[3]);
+              v[4] = fmaf(c, px[q][1].x, v[4]); v[5] = fmaf(c, px[q][1].y, v[5]);
+              v[6] = fmaf(c, px[q][1].z, v[6]); v[7] = fmaf(c, px[q][1].w, v[7]);
+            }
+          }
+          // partials beyond the prefetched batch
+          for (int q = WDV_PQ; q < a.P; ++q) {
+            const float c = s_coef[ar * kMaxRowP + q];
+            const float4* sp = (const float4*)(a.wpart + ((int64_t)arow * a.P + q) * a.N + a0 + ac0);
+            const float4 x0 = sp[0], x1 = sp[1];
+            v[0] = fmaf(c, x0.x, v[0]); v[1] = fmaf(c, x0.y, v[1]);
+            v[2] = fmaf(c, x0.z, v[2]); v[3] = fmaf(c, x0.w, v[3]);
+            v[4] = fmaf(c, x1.x, v[4]); v[5] = fmaf(c, x1.y, v[5]);
+            v[6] = fmaf(c, x1.z, v[6]); v[7] = fmaf(c, x1.w, v[7]);
+          }
+        } else {
+          const float* src = a.wpart + (int64_t)arow * a.P * a.N + a0 + ac0;
+          for (int q = 0; q < a.P; ++q) {
+            const float c = s_coef[ar * kMaxRowP + q];
+            for (int e = 0; e < 8 && a0 + ac0 + e < a.N; ++e)
+              v[e] = fmaf(c, src[(int64_t)q * a.N + e], v[e]);
+          }
+        }
+        if (a.w_out) {
+          float* wo = a.w_out + (int64_t)arow * a.N + a0 + ac0;
+          for (int e = 0; e < 8 && a0 + ac0 + e < a.N; ++e) wo[e] = v[e];
+        }
+      }
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         const uint32_t h0 = f32_to_bf16_rne(v[e]), h1 = f32_to_bf16_rne(v[e + 1]);
         const uint32_t l0 = f32_to_bf16_rne(v[e] - __uint_as_float(h0 << 16));
         const uint32_t l1 = f32_to_bf16_rne(v[e + 1] - __uint_as_float(h1 << 16));
-        *(uint32_t*)&s_ahi[r * WPITCH + c0 + e] = h0 | (h1 << 16);
-        *(uint32_t*)&s_alo[r * WPITCH + c0 + e] = l0 | (l1 << 16);
+        *(uint32_t*)&s_ahi[ar * WPITCH + ac0 + e] = h0 | (h1 << 16);
+        *(uint32_t*)&s_alo[ar * WPITCH + ac0 + e] = l0 | (l1 << 16);
       }
     }
     // B: Dv rows a0..a0+127 transposed to [dim][atom pair]
-    for (int it = tid; it < (WSUB / 2) * (a.d >> 3); it += 512) {
-      const int ap = it % (WSUB / 2), sg = it / (WSUB / 2);
-      const int atom = a0 + 2 * ap;
-      u32x4 x0 = u32x4{0u, 0u, 0u, 0u}, x1 = u32x4{0u, 0u, 0u, 0u};
-      if (atom < a.N) x0 = *(const u32x4*)(dv + (int64_t)atom * a.d + 8 * sg);
-      if (atom + 1 < a.N) x1 = *(const u32x4*)(dv + (int64_t)(atom + 1) * a.d + 8 * sg);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s_bt[(8 * sg + 2 * i) * BPITCH + ap] = (x0[i] & 0xFFFFu) | (x1[i] << 16);
-        s_bt[(8 * sg + 2 * i + 1) * BPITCH + ap] = (x0[i] >> 16) | (x1[i] & 0xFFFF0000u);
+    for (int k = 0; k < BIT; ++k) {
+      const int it = tid + k * 512;
+      const int ap = it % (WSUB / 2), sg = it / (WSUB / 2);
+      if (sg < (a.d >> 3)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          s_bt[(8 * sg + 2 * i) * BPITCH + ap] = (bx[k][0][i] & 0xFFFFu) | (bx[k][1][i] << 16);
+          s_bt[(8 * sg + 2 * i + 1) * BPITCH + ap] = (bx[k][0][i] >> 16) | (bx[k][1][i] & 0xFFFF0000u);
+        }
       }
     }
     __syncthreads();
@@ -754,6 +790,8 @@ __global__ __launch_bounds__(256) void k_wdv_f32(WdvArgs a) {
 // out[o] = sum_c opart[c][o] in a fixed order: 16 threads per output each
 // sum every 16th chunk, then a fixed-order combine in LDS.
 constexpr int RED_OUT = 64;   // outputs per workgroup
+// Thread (o, q) sums chunks q, q+16, q+32, ... of output o; each block of 16
+// such loads is issued before it is summed. Fixed order: deterministic.
 __global__ __launch_bounds__(1024) void k_reduce_out(const float* opart, int nchunks, int64_t n,
                                                      float* out) {
   __shared__ float s_p[16][RED_OUT + 1];
@@ -761,13 +799,16 @@ __global__ __launch_bounds__(1024) void k_reduce_out(const float* opart, int nch
   const int64_t i = (int64_t)blockIdx.x * RED_OUT + o;
   float s = 0.f;
   if (i < n) {
-    int c = q;
-    for (; c + 48 < nchunks; c += 64) {
-      const float x0 = opart[(int64_t)c * n + i], x1 = opart[(int64_t)(c + 16) * n + i];
-      const float x2 = opart[(int64_t)(c + 32) * n + i], x3 = opart[(int64_t)(c + 48) * n + i];
-      s += x0; s += x1; s += x2; s += x3;
+    for (int c0 = q; c0 < nchunks; c0 += 256) {
+      float x[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int c = c0 + 16 * k;
+        x[k] = (c < nchunks) ? opart[(int64_t)c * n + i] : 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < 16; ++k) s += x[k];
     }
-    for (; c < nchunks; c += 16) s += opart[(int64_t)c * n + i];
   }
   s_p[q][o] = s;
   __syncthreads();
@@ -824,16 +865,15 @@ sdkv_status plan_decode(const sdkv_attn_args* a, DecodePlan* p) {
   q.off_stats = off;  off = align_up(off + (size_t)rows * q.P * 8, A);
   q.off_zero = off;
   q.off_ghist = off;  off += (q.P > 1) ? (size_t)rows * 2048 * 4 : 0;
-  q.off_fhist = off;  off += (q.P > 1) ? (size_t)rows * 2048 * 4 : 0;
   q.off_xchg = off;   off += (size_t)rows * q.P * 2 * 4;
-  q.off_bar = off;    off += (size_t)rows * 4;
+  q.off_bar = off;    off += (size_t)rows * 2 * 4;
   q.off_err = off;    off += 4;
   q.off_ticket = off; off += 8 * 4;
   off = align_up(off, A);
   q.zero_bytes = off - q.off_zero;
   q.off_opart = off;  off = align_up(off + (size_t)q.nchunks * rows * a->d * 4, A);
   q.off_cand = off;   off = align_up(off + (q.P > 1 ? (size_t)rows * q.P * q.chunk * 4 : 0), A);
-  q.off_bucket = off; off = align_up(off + (q.P > 1 ? (size_t)rows * 2048 * kBucket * 8 : 0), A);
+  q.off_wtab = off;   off = align_up(off + (q.P > 1 ? (size_t)rows * q.P * 2048 * 4 : 0), A);
   q.total = off;
   *p = q;
   return SDKV_OK;
@@ -915,8 +955,7 @@ sdkv_status launch_decode(const sdkv_attn_args* a, const DecodePlan& p, void* ws
   ra.wpart = wpart;
   ra.stats = stats;
   ra.ghist = ghist;
-  ra.fhist = (uint32_t*)(base + p.off_fhist);
-  ra.bucket = (uint64_t*)(base + p.off_bucket);
+  ra.wtab = (uint32_t*)(base + p.off_wtab);
   ra.cand = (uint32_t*)(base + p.off_cand);
   ra.xchg = xchg;
   ra.bar = bar;

@@ -132,36 +132,71 @@ __device__ __forceinline__ float block_sum(float v, float* tmp) {
   return r;
 }
 
-// --- cross-workgroup barrier among the workgroups sharing `ctr` ---------------
+// --- cross-workgroup barrier among the workgroups of one row -----------------
 // The workgroups must be co-resident (the callers assign work by start-order
 // tickets and check the capacity). MI355X has one L2 per XCD and the L2s are
-// not coherent with each other, so data that one workgroup writes and another
-// reads inside a kernel needs an agent-scope release / acquire pair: every
-// thread first completes its own memory operations (s_waitcnt) and meets the
-// others at the workgroup barrier; then one thread releases (write-back of
-// this XCD's L2, buffer_wbl2), arrives with an atomic add (performed
-// coherently), polls the counter, and acquires (invalidation of this XCD's L2,
-// buffer_inv) before the workgroup barrier lets the other threads read. The
-// cross-workgroup data itself is accessed with agent-scope atomic loads and
-// stores, which bypass the per-CU L1. One fence pair per workgroup, not one
-// per thread: per-thread fences measured ~65 us per barrier.
-// The spin is bounded: after ~2^24 polls the workgroup records the failure in
-// *err and continues, so no wave can wait forever.
-__device__ __forceinline__ void group_barrier(uint32_t* ctr, uint32_t target, uint32_t* err) {
+// not coherent with each other. Cross-workgroup data is written and read with
+// agent-scope atomic stores and loads (they bypass the per-CU L1), so
+// workgroups on one XCD see each other's data in their shared L2; across XCDs
+// an agent-scope release (write-back of the writer's L2, buffer_wbl2) and
+// acquire (invalidation of the reader's L2, buffer_inv) are needed, and they
+// are costly (about 6 us per barrier at the 128K layer step).
+//
+// `local`: the caller placed every workgroup of the row in one class of
+// workgroup ids (id % 8, the XCD the dispatcher sends them to). Each
+// workgroup checks this against the hardware XCC id. Arrival adds 1, plus
+// 1 << 16 if the workgroup is not on its class's XCD (or `local` is false);
+// such a workgroup releases before arriving. If, once all P have arrived,
+// any workgroup of the row was not on the common XCD, every workgroup
+// releases (if it has not), arrives at the row's second counter, waits for
+// all P there and acquires: exact either way, fence-free when the placement
+// holds. Without `local` every workgroup releases before arriving and
+// acquires after the wait. `round` counts this row's barriers (1, 2, ...). bar[0] / bar[1] are
+// the row's counters, zeroed before launch. Every thread first completes its
+// own memory operations (s_waitcnt) and meets the others at the workgroup
+// barrier; one thread does the rest. The spins are bounded: after ~2^24
+// polls the workgroup records the failure in *err and continues, so no wave
+// can wait forever.
+__device__ __forceinline__ uint32_t hw_xcc_id() {
+  return (uint32_t)__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 0xFu;  // HW_REG_XCC_ID
+}
+__device__ __forceinline__ bool spin_until(uint32_t* ctr, uint32_t mask, uint32_t target,
+                                           uint32_t* err, uint32_t* last) {
+  uint32_t spins = 0, v;
+  while (((v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) & mask) < target) {
+    __builtin_amdgcn_s_sleep(1);
+    if (++spins > (1u << 24)) {
+      __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+  }
+  *last = v;
+  return true;
+}
+__device__ __forceinline__ void group_barrier(uint32_t* bar, uint32_t P, uint32_t round,
+                                              bool local, uint32_t* err) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (threadIdx.x == 0 && !local) {
+    // rows spread over XCDs: everyone releases, arrives, waits, acquires
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    uint32_t spins = 0;
-    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      __builtin_amdgcn_s_sleep(1);
-      if (++spins > (1u << 24)) {
-        __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-    }
+    __hip_atomic_fetch_add(&bar[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t v;
+    spin_until(&bar[0], 0xFFFFu, P * round, err, &v);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  } else if (threadIdx.x == 0) {
+    const bool remote = hw_xcc_id() != (blockIdx.x & 7u);
+    if (remote) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __hip_atomic_fetch_add(&bar[0], 1u | ((uint32_t)remote << 16), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t v;
+    spin_until(&bar[0], 0xFFFFu, P * round, err, &v);
+    if ((v >> 16) != 0u) {
+      if (!remote) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __hip_atomic_fetch_add(&bar[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      spin_until(&bar[1], 0xFFFFFFFFu, P * round, err, &v);
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
   }
   __syncthreads();
 }

@@ -35,7 +35,8 @@ struct SelGroup {
   int p;              // this workgroup's position (element order)
   uint32_t* ghist;    // [2048] zeroed before launch (P > 1)
   uint32_t* xchg;     // [P][2]
-  uint32_t* bar;      // barrier counter, zeroed before launch
+  uint32_t* bar;      // [2] barrier counters, zeroed before launch
+  bool local;         // all workgroups of the row are in one id % 8 class
   uint32_t* err;      // set to 1 if a barrier wait gave up
   uint32_t* cand;     // [P][cap] candidate keys of each workgroup (P > 1)
   int64_t cap;        // candidate slots per workgroup (>= keys per workgroup)
@@ -137,7 +138,7 @@ __device__ __forceinline__ Mask radix_select_coop(const uint32_t (&key)[SPT], ui
     const uint32_t c = sh.hist[i];
     if (c) atomicAdd(&g.ghist[i], c);
   }
-  group_barrier(g.bar, (uint32_t)g.P * (bar_base + 1u), g.err);
+  group_barrier(g.bar, (uint32_t)g.P, bar_base + 1u, g.local, g.err);
   for (int i = tid; i < 2048; i += SB) sh.hist[i] = ld_agent(&g.ghist[i]);
   __syncthreads();
   uint32_t gt1;
@@ -165,7 +166,7 @@ __device__ __forceinline__ Mask radix_select_coop(const uint32_t (&key)[SPT], ui
     st_agent(&g.xchg[2 * g.p], tna);
     st_agent(&g.xchg[2 * g.p + 1], tnc);
   }
-  group_barrier(g.bar, (uint32_t)g.P * (bar_base + 2u), g.err);
+  group_barrier(g.bar, (uint32_t)g.P, bar_base + 2u, g.local, g.err);
 
   // --- every workgroup: counts per workgroup, then all candidates ------------
   // s_qcnt layout: [0,P) above-bin counts A_q, [P,2P) candidate counts c_q,
@@ -362,39 +363,38 @@ __device__ __forceinline__ int value_bin(uint32_t k, float base, float inv) {
 constexpr int kSampleN = 4096;             // shared sample size (tokens)
 constexpr int kSamplePT = kSampleN / SB;
 
-constexpr int kBucket = 16;  // keys kept per fine bin of a row's window
-
 // Sample-window select with one cross-workgroup synchronisation.
 //
 // Every workgroup of the row holds the keys `skey` of the same fixed sample
-// of ns of the row's T elements, so all derive the same window: the value
+// of ns of the row's T elements, so all derive the same window: the key
 // range between the sample's order statistics of rank m ns / T -/+ (5
 // standard deviations + 4), found with a linear 2048-bin histogram between
-// the sample's smallest and largest value. The window is divided into 2048
-// fine bins on a linear value scale (all bin functions are monotone in the
-// key, see value_bin). Each workgroup then
-//   * counts its keys above the window (published in xchg[2p]), and
-//   * adds each of its keys inside the window to the row's fine histogram
-//     `fh` (a global atomic), whose return value gives the key a slot in its
-//     bin's bucket `bkt` (kBucket keys per bin, tagged with the workgroup).
-// After the one barrier every workgroup reads the P counts and the 2048-bin
-// histogram, finds the bin holding the threshold, and reads only that bin's
-// bucket: the threshold is its need-th largest key, and the bucket's owner
-// tags give every workgroup's count of keys equal to it (for the tie quota,
-// lowest element index first). Keys above the threshold need no exchange:
-// each workgroup selects its own. If the window misses the threshold, or
-// the threshold's bin overflowed its bucket, the function returns false
-// having used one barrier, and the caller runs the two-barrier radix select;
-// the result is exact either way. The selection's global output offset is
-// not computed here (callers that need it exchange counts).
+// the sample's smallest and largest value. The window [lo_key, hi_key) is
+// split into 2048 fine bins, fine bin = (k - lo_key) * 2048 / span by a
+// fixed-point multiply (monotone in the key, identical in every workgroup).
+// Each workgroup
+//   * counts its keys at or above hi_key (published in xchg[2p]),
+//   * sorts its window keys by fine bin in LDS (a counting sort) and stores
+//     them to its list `wl` (row slots [p * cap, p * cap + cap)), with its
+//     2048-entry table `wt` of (count | start << 16) per bin.
+// There are no global atomics. After the one barrier every workgroup sums
+// the P count tables, finds the bin holding the threshold, and reads only
+// that bin's keys from each workgroup's list. The threshold is their
+// need-th largest key; their owners give each workgroup's count of keys
+// equal to it (tie quota, lowest element index first). Keys above the
+// threshold need no exchange: each workgroup selects its own. If the window
+// misses the threshold, or the threshold's bin holds more than SB/2 keys,
+// the function returns false having used one barrier, and the caller runs
+// the two-barrier radix select; the result is exact either way. The
+// selection's global output offset is not computed here.
 template <int SPT>
 __device__ __forceinline__ bool sample_window_select(const uint32_t (&key)[SPT],
                                                      const uint32_t (&skey)[kSamplePT],
                                                      uint32_t ns, uint32_t m, uint32_t T,
                                                      SelShared& sh, const SelGroup& g,
-                                                     uint32_t* fh, uint64_t* bkt,
-                                                     uint32_t* tau_out, Mask* sel_out,
-                                                     uint32_t* s_qcnt) {
+                                                     uint32_t* wt, uint32_t* tau_out,
+                                                     Mask* sel_out, uint32_t* s_qcnt) {
+  static_assert(SB * 2 == 2048, "two fine bins per thread");
   const int tid = threadIdx.x, w = wave_id(), lane = lane_id();
   const int P = g.P;
   // --- sample value range ------------------------------------------------------
@@ -416,7 +416,7 @@ __device__ __forceinline__ bool sample_window_select(const uint32_t (&key)[SPT],
   const float base = key_float(kmn);
   const float span = key_float(kmx) - base;
   const float inv = (kmx > kmn && span > 0.f && span < INFINITY) ? 2048.f / span : 0.f;
-  // --- window bins from the sample's rank estimates ---------------------------
+  // --- window from the sample's rank estimates --------------------------------
   const float rho = (ns >= T) ? (float)m : (float)((double)m * ns / T);
   const float sd = sqrtf(fmaxf(rho * (1.f - rho / (float)ns), 0.f));
   const float wd = (ns >= T) ? 0.f : 5.f * sd + 4.f;
@@ -429,46 +429,63 @@ __device__ __forceinline__ bool sample_window_select(const uint32_t (&key)[SPT],
   uint32_t gtx;
   const int b_hi = (int)find_digit(sh, 2048, r_hi, &gtx);
   const int b_lo = (int)find_digit(sh, 2048, r_lo, &gtx);
-  float base2 = base, inv2 = 0.f;
+  // key thresholds at the edges of the coarse bins b_lo and b_hi
+  uint32_t lo_key = 1u, hi_key = 0xFFFFFFFFu;
   if (inv > 0.f) {
-    base2 = base + (float)b_lo / inv;
-    inv2 = inv * (2048.f / (float)(b_hi - b_lo + 1));
+    lo_key = max(1u, float_key(base + (float)b_lo / inv));
+    hi_key = float_key(base + (float)(b_hi + 1) / inv);
   }
-  // --- publish: count above the window; window keys into the fine histogram ---
-  // in batches of 8 keys: all fine bins, then all histogram atomics (their
-  // returned slots are not waited for until the batch's stores)
+  if (hi_key <= lo_key) hi_key = lo_key + 1u;
+  const uint32_t mulc =
+      (uint32_t)fmin(4294967295.0, 2048.0 * 4294967296.0 / (double)(hi_key - lo_key));
+  // --- publish: count above the window; window keys sorted by fine bin --------
+  for (int i = tid; i < 2048; i += SB) sh.hist[i] = 0u;
+  __syncthreads();
   uint32_t na = 0;
-  constexpr int PB = SPT < 8 ? SPT : 8;
+  uint32_t pos[SPT];  // (fine bin << 16 | rank in bin) of window keys, else ~0
 #pragma unroll
-  for (int j0 = 0; j0 < SPT; j0 += PB) {
-    int fbv[PB];
-#pragma unroll
-    for (int jj = 0; jj < PB; ++jj) {
-      const uint32_t k = key[j0 + jj];
-      const int bk = value_bin(k, base, inv);
-      na += (k != 0u && bk > b_hi) ? 1u : 0u;
-      fbv[jj] = (k != 0u && bk >= b_lo && bk <= b_hi) ? value_bin(k, base2, inv2) : -1;
+  for (int j = 0; j < SPT; ++j) {
+    const uint32_t k = key[j];
+    na += (k >= hi_key) ? 1u : 0u;
+    pos[j] = 0xFFFFFFFFu;
+    if (k >= lo_key && k < hi_key) {
+      const uint32_t fb = min(2047u, __umulhi(k - lo_key, mulc));
+      pos[j] = (fb << 16) | atomicAdd(&sh.hist[fb], 1u);
     }
-    uint32_t slot[PB];
-#pragma unroll
-    for (int jj = 0; jj < PB; ++jj) {
-      slot[jj] = (uint32_t)kBucket;
-      if (fbv[jj] >= 0) slot[jj] = atomicAdd(&fh[fbv[jj]], 1u);
-    }
-#pragma unroll
-    for (int jj = 0; jj < PB; ++jj)
-      if (slot[jj] < (uint32_t)kBucket)
-        __hip_atomic_store(&bkt[fbv[jj] * kBucket + slot[jj]], ((uint64_t)g.p << 32) | key[j0 + jj],
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   const uint32_t na_w = wave_sum_u32(na);
   if (lane == 0) atomicAdd(&sh.bcast[5], na_w);
   __syncthreads();
+  // exclusive prefix over the 2048 bins, two per thread
+  const uint32_t c0 = sh.hist[2 * tid], c1 = sh.hist[2 * tid + 1];
+  uint32_t tot;
+  const uint32_t ex = block_excl_scan<SNW>(c0 + c1, sh.tmp, &tot);
+  uint32_t* mywt = wt + (int64_t)g.p * 2048;
+  __hip_atomic_store((uint64_t*)(mywt + 2 * tid),
+                     ((uint64_t)(c1 | ((ex + c0) << 16)) << 32) | (c0 | (ex << 16)),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  sh.hist[2 * tid] = ex;
+  sh.hist[2 * tid + 1] = ex + c0;
   if (tid == 0) st_agent(&g.xchg[2 * g.p], sh.bcast[5]);
-  group_barrier(g.bar, (uint32_t)P, g.err);
-  // --- threshold bin from the counts above and the fine histogram -------------
+  __syncthreads();
+  uint32_t* mywl = g.cand + (int64_t)g.p * g.cap;
+#pragma unroll
+  for (int j = 0; j < SPT; ++j)
+    if (pos[j] != 0xFFFFFFFFu) st_agent(&mywl[sh.hist[pos[j] >> 16] + (pos[j] & 0xFFFFu)], key[j]);
+  group_barrier(g.bar, (uint32_t)P, 1u, g.local, g.err);
+  // --- threshold bin from the counts above and the summed count tables --------
   if (tid < P) s_qcnt[tid] = ld_agent(&g.xchg[2 * tid]);
-  for (int i = tid; i < 2048; i += SB) sh.hist[i] = ld_agent(&fh[i]);
+  {
+    uint32_t h0 = 0, h1 = 0;
+    for (int q = 0; q < P; ++q) {
+      const uint64_t e = __hip_atomic_load((const uint64_t*)(wt + (int64_t)q * 2048 + 2 * tid),
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      h0 += (uint32_t)e & 0xFFFFu;
+      h1 += (uint32_t)(e >> 32) & 0xFFFFu;
+    }
+    sh.hist[2 * tid] = h0;
+    sh.hist[2 * tid + 1] = h1;
+  }
   __syncthreads();
   uint32_t A = 0;
   for (int q = 0; q < P; ++q) A += s_qcnt[q];
@@ -480,17 +497,24 @@ __device__ __forceinline__ bool sample_window_select(const uint32_t (&key)[SPT],
   uint32_t gt2, total;
   const int bstar = (int)find_digit(sh, 2048, need1, &gt2, &total);
   const uint32_t nc = sh.hist[bstar];
-  if (total < need1 || nc > (uint32_t)kBucket) {
+  if (total < need1 || nc > (uint32_t)(SB / 2)) {
     __syncthreads();
     return false;
   }
   const uint32_t need2 = need1 - gt2;  // 1 <= need2 <= nc
-  // --- the threshold's bucket: exact rank, ties by workgroup ------------------
+  // --- the threshold bin's keys from every workgroup --------------------------
+  if (tid < P) {
+    const uint32_t e = ld_agent(&wt[(int64_t)tid * 2048 + bstar]);
+    s_qcnt[P + tid] = e & 0xFFFFu;   // count
+    s_qcnt[2 * P + tid] = e >> 16;   // start
+  }
+  __syncthreads();
   if (tid < (int)nc) {
-    const uint64_t e = __hip_atomic_load(&bkt[bstar * kBucket + tid], __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-    sh.scan[tid] = (uint32_t)e;
-    sh.scan[kBucket + tid] = (uint32_t)(e >> 32);
+    int q = 0;
+    uint32_t off = 0;
+    while (q + 1 < P && off + s_qcnt[P + q] <= (uint32_t)tid) { off += s_qcnt[P + q]; ++q; }
+    sh.scan[tid] = ld_agent(&g.cand[(int64_t)q * g.cap + s_qcnt[2 * P + q] + (tid - off)]);
+    sh.scan[SB / 2 + tid] = (uint32_t)q;
   }
   __syncthreads();
   if (tid < (int)nc) {
@@ -505,10 +529,10 @@ __device__ __forceinline__ bool sample_window_select(const uint32_t (&key)[SPT],
   }
   __syncthreads();
   const uint32_t tau = sh.bcast[7];
-  // bucket keys above tau (all workgroups), equal to tau before / at this one
+  // keys of the bin above tau (all workgroups), equal to tau before / at this one
   uint32_t b_gt = 0, eq_before = 0, te = 0;
   for (uint32_t i = 0; i < nc; ++i) {
-    const uint32_t y = sh.scan[i], q = sh.scan[kBucket + i];
+    const uint32_t y = sh.scan[i], q = sh.scan[SB / 2 + i];
     b_gt += y > tau ? 1u : 0u;
     eq_before += (y == tau && q < (uint32_t)g.p) ? 1u : 0u;
     te += (y == tau && q == (uint32_t)g.p) ? 1u : 0u;

@@ -18,7 +18,7 @@ struct TopkArgs {
   uint32_t* ghist;  // [rows, 2048]
   uint32_t* cand;   // [rows, P, chunk]
   uint32_t* xchg;   // [rows, P, 2]
-  uint32_t* bar;    // [rows]
+  uint32_t* bar;    // [rows, 2] barrier counters
   uint32_t* err;
   uint32_t* ticket; // [8] workgroup start-order counters (see k_rows)
   int xcd_map;
@@ -55,7 +55,8 @@ __global__ __launch_bounds__(SB) void k_topk(TopkArgs a) {
   grp.p = p;
   grp.ghist = a.ghist + row * 2048;
   grp.xchg = a.xchg + row * a.P * 2;
-  grp.bar = a.bar + row;
+  grp.bar = a.bar + 2 * (int64_t)row;
+  grp.local = a.xcd_map != 0;
   grp.err = a.err;
   grp.cand = a.cand + row * a.P * a.chunk;
   grp.cap = a.chunk;
@@ -93,7 +94,7 @@ sdkv_status plan_topk(int64_t rows, int64_t n, int64_t k, TopkPlan* p) {
   size_t off = 0;
   q.off_ghist = off;  off += (q.P > 1) ? (size_t)rows * 2048 * 4 : 0;
   q.off_xchg = off;   off += (size_t)rows * q.P * 2 * 4;
-  q.off_bar = off;    off += (size_t)rows * 4;
+  q.off_bar = off;    off += (size_t)rows * 2 * 4;
   q.off_err = off;    off += 4;
   q.off_ticket = off; off += 8 * 4;
   q.zero_bytes = align_up(off, 256);
