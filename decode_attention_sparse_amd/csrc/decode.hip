@@ -340,21 +340,30 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
     }
   }
 
-  // 4. compaction: the selected tokens of this workgroup in token order, as
-  // offsets within the chunk in LDS (this workgroup's region of the global
-  // list when they do not fit).
+  // 4. compaction: the selected tokens of this workgroup as offsets within
+  // the chunk in LDS (this workgroup's region of the global list when they
+  // do not fit), thread-major: thread t's tokens, in element order, follow
+  // those of threads below t (one block scan of per-thread counts).
   int32_t* sel_g = a.sel + ((int64_t)row * a.P + p) * a.chunk;
   float* sh_g = a.s_high + ((int64_t)row * a.P + p) * a.chunk;
-  const uint32_t nsel = ordered_ranks<SPT>(sel, sh, [&](int j, uint32_t r) {
-    if (r < (uint32_t)kListCap) s_lt[r] = (uint16_t)(j * SB + tid);
-    else sel_g[r] = (int32_t)(t0 + (int64_t)j * SB + tid);
-  });
+  uint32_t nsel;
+  const uint32_t lbase = block_excl_scan<SNW>((uint32_t)__popc(sel), sh.tmp, &nsel);
+#pragma unroll
+  for (int j = 0; j < SPT; ++j) {
+    if ((sel >> j) & 1u) {
+      const uint32_t r = lbase + (uint32_t)__popc(sel & ((1u << j) - 1u));
+      if (r < (uint32_t)kListCap) s_lt[r] = (uint16_t)(j * SB + tid);
+      else sel_g[r] = (int32_t)(t0 + (int64_t)j * SB + tid);
+    }
+  }
   const int64_t cnt = nsel;
   const bool in_lds = cnt <= kListCap;
+  __syncthreads();
   if (!in_lds) {
     // the whole list goes to the global region (entries below kListCap too)
     for (int64_t i = tid; i < min(cnt, (int64_t)kListCap); i += SB) sel_g[i] = (int32_t)(t0 + s_lt[i]);
     __threadfence_block();
+    __syncthreads();
   }
   // debug outputs need the row-global position of this workgroup's entries
   if (need_offset) {
@@ -371,10 +380,6 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   }
   int32_t* sel_dbg = a.sel_out ? a.sel_out + (int64_t)row * a.m : nullptr;
   float* sh_dbg = a.s_high_out ? a.s_high_out + (int64_t)row * a.m : nullptr;
-  if (sel_dbg)
-    for (int64_t i = tid; i < cnt; i += SB)
-      if ((int64_t)offset + i < a.m) sel_dbg[offset + i] = in_lds ? (int32_t)(t0 + s_lt[i]) : sel_g[i];
-  __syncthreads();
 
   // 5. Khigh rescore, one thread per selected token (entries i = tid + k*SB;
   // the same thread handles the same entries in every later loop). Value
@@ -419,7 +424,6 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
       if (i < cnt) {
         if (in_lds) s_ls[i] = s;
         else sh_g[i] = s;
-        if (sh_dbg && (int64_t)offset + i < a.m) sh_dbg[offset + i] = s;
         if (s > lmax) {
           vb = vb * __expf(lmax - s) + va;
           lmax = s;
@@ -434,6 +438,20 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   // rescaling of each thread's running sum to the workgroup max)
   vb = (lmax > -INFINITY) ? vb * __expf(lmax - M) : 0.f;
   const float vsum = block_sum<SNW>(vb, s_red) * 1.0001f;
+
+  // debug outputs: the selection in token order with its s_high
+  if (sel_dbg || sh_dbg) {
+    __threadfence_block();
+    __syncthreads();
+    ordered_ranks<SPT>(sel, sh, [&](int j, uint32_t r) {
+      const int64_t i = (int64_t)offset + r;
+      if (i < a.m) {
+        const uint32_t lp = lbase + (uint32_t)__popc(sel & ((1u << j) - 1u));
+        if (sel_dbg) sel_dbg[i] = (int32_t)(t0 + (int64_t)j * SB + tid);
+        if (sh_dbg) sh_dbg[i] = in_lds ? s_ls[lp] : sh_g[lp];
+      }
+    });
+  }
 
   // 6. softmax weights and per-atom value weights. LDS integer atomics are
   // much faster than float ones on gfx950, so weights accumulate in int32

@@ -57,31 +57,49 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 
 // --- wave / block primitives ------------------------------------------------
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+// wave index as a scalar (uniform) value
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t t = __shfl_up(v, o, 64);
-    if (lane >= o) v += t;
-  }
+// Inclusive scan over the 64 lanes of a wave with DPP moves (no LDS traffic):
+// shifts by 1, 2, 4, 8 within each row of 16 lanes, then the last lane of
+// row 0 (row 2) is added to row 1 (row 3) and lane 31 to rows 2 and 3.
+// Lanes a move does not write keep `ident`, the operation's identity.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_scan_dpp(uint32_t v, uint32_t ident, Op op) {
+  const int id = (int)ident;
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x111, 0xF, 0xF, false));  // row_shr:1
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x112, 0xF, 0xF, false));  // row_shr:2
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x114, 0xF, 0xF, false));  // row_shr:4
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x118, 0xF, 0xF, false));  // row_shr:8
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast:31
   return v;
+}
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  return wave_scan_dpp(v, 0u, [](uint32_t x, uint32_t y) { return x + y; });
+}
+// reductions: the scan's last lane, returned to every lane as a scalar
+__device__ __forceinline__ uint32_t wave_last(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  const uint32_t r = wave_scan_dpp(__float_as_uint(v), __float_as_uint(-INFINITY), [](uint32_t x, uint32_t y) {
+    return __float_as_uint(fmaxf(__uint_as_float(x), __uint_as_float(y)));
+  });
+  return __uint_as_float(wave_last(r));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  const uint32_t r = wave_scan_dpp(__float_as_uint(v), 0u, [](uint32_t x, uint32_t y) {
+    return __float_as_uint(__uint_as_float(x) + __uint_as_float(y));
+  });
+  return __uint_as_float(wave_last(r));
 }
-__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) { return wave_last(wave_incl_scan(v)); }
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  return wave_last(wave_scan_dpp(v, 0xFFFFFFFFu, [](uint32_t x, uint32_t y) { return min(x, y); }));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  return wave_last(wave_scan_dpp(v, 0u, [](uint32_t x, uint32_t y) { return max(x, y); }));
 }
 // sum within aligned groups of G lanes (G = 16 or 32)
 template <int G>

@@ -78,41 +78,59 @@ __device__ __forceinline__ uint32_t ordered_ranks(Mask bits, SelShared& sh, F&& 
   return tot;
 }
 
-// Finds digit v of an nbins-bin histogram in sh.hist with
-// #(digit > v) < need <= #(digit >= v). Returns v; *above = #(digit > v);
-// *total (optional) = the histogram's total. Uniform across the block. (If
-// fewer than `need` keys exist, v = 0 and *above = 0.)
-__device__ __forceinline__ uint32_t find_digit(SelShared& sh, int nbins, uint32_t need,
-                                               uint32_t* above_out, uint32_t* total = nullptr) {
+// Finds, for each of NQ <= 2 ranks need[q], the digit v[q] of an
+// nbins-bin histogram in sh.hist with #(digit > v) < need <= #(digit >= v);
+// above[q] = #(digit > v[q]); *total (optional) = the histogram's total. All
+// uniform across the block. (If fewer than need[q] keys exist, v[q] = 0 and
+// above[q] = 0.) One prefix scan over the per-thread bin sums serves every
+// rank: the count above thread t's bins is total - (inclusive prefix at t).
+template <int NQ>
+__device__ __forceinline__ void find_digits(SelShared& sh, int nbins, const uint32_t (&need)[NQ],
+                                            uint32_t (&v)[NQ], uint32_t (&above_out)[NQ],
+                                            uint32_t* total = nullptr) {
+  static_assert(NQ >= 1 && NQ <= 2, "bcast holds two (digit, above) pairs");
   const int tid = threadIdx.x;
   const int bpt = nbins / SB;
   uint32_t loc = 0;
   for (int i = 0; i < bpt; ++i) loc += sh.hist[tid * bpt + i];
-  sh.scan[SB - 1 - tid] = loc;  // reversed order: a prefix scan gives suffix sums
-  if (tid == 0) { sh.bcast[0] = 0u; sh.bcast[1] = 0u; }
-  __syncthreads();
-  const uint32_t rv = sh.scan[tid];
+  if (tid == 0)
+    for (int q = 0; q < 2 * NQ; ++q) sh.bcast[q] = 0u;
   uint32_t tot;
-  const uint32_t above = block_excl_scan<SNW>(rv, sh.tmp, &tot);
-  const int o = SB - 1 - tid;
-  if (above < need && above + rv >= need) {
-    uint32_t run = above;
-    for (int i = bpt - 1; i >= 0; --i) {
-      const uint32_t c = sh.hist[o * bpt + i];
-      if (run + c >= need) {
-        sh.bcast[0] = (uint32_t)(o * bpt + i);
-        sh.bcast[1] = run;
-        break;
+  const uint32_t ex = block_excl_scan<SNW>(loc, sh.tmp, &tot);
+  const uint32_t above = tot - ex - loc;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    if (above < need[q] && above + loc >= need[q]) {
+      uint32_t run = above;
+      for (int i = bpt - 1; i >= 0; --i) {
+        const uint32_t c = sh.hist[tid * bpt + i];
+        if (run + c >= need[q]) {
+          sh.bcast[2 * q] = (uint32_t)(tid * bpt + i);
+          sh.bcast[2 * q + 1] = run;
+          break;
+        }
+        run += c;
       }
-      run += c;
     }
   }
   __syncthreads();
-  const uint32_t v = sh.bcast[0];
-  *above_out = sh.bcast[1];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    v[q] = sh.bcast[2 * q];
+    above_out[q] = sh.bcast[2 * q + 1];
+  }
   if (total) *total = tot;
   __syncthreads();
-  return v;
+}
+
+// find_digits for one rank: returns v; *above_out = #(digit > v).
+__device__ __forceinline__ uint32_t find_digit(SelShared& sh, int nbins, uint32_t need,
+                                               uint32_t* above_out, uint32_t* total = nullptr) {
+  const uint32_t nq[1] = {need};
+  uint32_t v[1], ab[1];
+  find_digits<1>(sh, nbins, nq, v, ab, total);
+  *above_out = ab[0];
+  return v[0];
 }
 
 // Multi-workgroup select with two cross-workgroup synchronisations:
@@ -402,11 +420,8 @@ __device__ __forceinline__ bool sample_window_select(const uint32_t (&key)[SPT],
 #pragma unroll
   for (int j = 0; j < kSamplePT; ++j)
     if (skey[j] != 0u) { kmn = min(kmn, skey[j]); kmx = max(kmx, skey[j]); }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    kmn = min(kmn, (uint32_t)__shfl_xor((int)kmn, o, 64));
-    kmx = max(kmx, (uint32_t)__shfl_xor((int)kmx, o, 64));
-  }
+  kmn = wave_min_u32(kmn);
+  kmx = wave_max_u32(kmx);
   if (lane == 0) { sh.tmp[w] = kmn; sh.tmp[SNW + w] = kmx; }
   if (tid == 0) { sh.bcast[5] = 0u; sh.bcast[7] = 0u; }
   for (int i = tid; i < 2048; i += SB) sh.hist[i] = 0u;
@@ -426,9 +441,10 @@ __device__ __forceinline__ bool sample_window_select(const uint32_t (&key)[SPT],
   for (int j = 0; j < kSamplePT; ++j)
     if (skey[j] != 0u) atomicAdd(&sh.hist[value_bin(skey[j], base, inv)], 1u);
   __syncthreads();  // also: every thread has read sh.tmp
-  uint32_t gtx;
-  const int b_hi = (int)find_digit(sh, 2048, r_hi, &gtx);
-  const int b_lo = (int)find_digit(sh, 2048, r_lo, &gtx);
+  const uint32_t rr[2] = {r_hi, r_lo};
+  uint32_t bb[2], gtx[2];
+  find_digits<2>(sh, 2048, rr, bb, gtx);
+  const int b_hi = (int)bb[0], b_lo = (int)bb[1];
   // key thresholds at the edges of the coarse bins b_lo and b_hi
   uint32_t lo_key = 1u, hi_key = 0xFFFFFFFFu;
   if (inv > 0.f) {
