@@ -310,13 +310,8 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
         const int64_t i = min((int64_t)(tid + j * SB), ns - 1);
         const int64_t t = all ? i : (((i >> 4) * a.T) >> 8) + (i & 15);
         wps[j] = lo + t * lw;
-        if (low3) {
-          const Words3 v = *(const Words3*)wps[j];
-          wd[j][0] = v.x; wd[j][1] = v.y; wd[j][2] = v.z; wd[j][3] = v.z;
-        } else {
 #pragma unroll
-          for (int c = 0; c < 4; ++c) wd[j][c] = wps[j][min(c, a.klow - 1)];
-        }
+        for (int c = 0; c < 4; ++c) wd[j][c] = wps[j][min(c, a.klow - 1)];
       }
 #pragma unroll
       for (int j = 0; j < kSamplePT; ++j) {
