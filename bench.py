@@ -148,7 +148,8 @@ def bench_decode(args, torch, sd, synth, ev):
     base = dict(q=torch.from_numpy(case.q).to(dev).to(torch.bfloat16),
                 dk=torch.from_numpy(case.dk).to(dev).to(torch.bfloat16),
                 dv=torch.from_numpy(case.dv).to(dev).to(torch.bfloat16),
-                kc=up_words(case.key_codes), vc=up_words(case.val_codes),
+                # each token's key record, then its value record: [B, Hkv, T, 2, K]
+                kv=up_words(np.stack([case.key_codes, case.val_codes], axis=3)),
                 kl=up_words(case.key_low))
     set_bytes = sum(t.numel() * t.element_size() for t in base.values())
     nsets = max(2, int(np.ceil(600e6 / set_bytes)))
@@ -158,7 +159,7 @@ def bench_decode(args, torch, sd, synth, ev):
     ws = sd.Workspace()
     stream = torch.cuda.current_stream()
     nstage = 5  # SDKV_DECODE_STAGES + 1
-    calls = [sd.DecodeCall(s["q"], s["dk"], s["dv"], s["kc"], s["vc"], klow=case.klow,
+    calls = [sd.DecodeCall(s["q"], s["dk"], s["dv"], s["kv"], None, klow=case.klow,
                            khigh=case.khigh, top_num=case.top_num, top_den=case.top_den,
                            scale=case.scale, key_low=s["kl"], out=out, workspace=ws)
              for s in sets]
@@ -375,7 +376,8 @@ def main():
         "vs_baseline": None, "dtype": "f32",
         "data": "synthetic (seeded; unit-norm Gaussian bf16 dictionaries, random codes)",
         "config": {"workload": "llama3.1-8b-shaped layer decode step at 128K context",
-                   **dec["config"], "storage": "bf16 dictionaries/query, uint16+fp16 codes"},
+                   **dec["config"], "storage": "bf16 dictionaries/query, uint16+fp16 codes",
+                   "code_layout": "key and value records side by side per token"},
         "roofline": dec["roofline"],
         "path_roofline": dec["path"],
         "stage_us": {k: round(v * 1e3, 2) for k, v in dec["stage_ms"].items()},

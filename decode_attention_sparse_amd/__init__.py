@@ -46,7 +46,7 @@ class AttnArgs(ctypes.Structure):
                 ("dv", c_void_p), ("dict_dtype", c_int32), ("n_atoms", c_int32),
                 ("B", c_int32), ("Hq", c_int32), ("Hkv", c_int32), ("d", c_int32),
                 ("T", c_int64), ("key_low", c_void_p), ("key_codes", c_void_p),
-                ("val_codes", c_void_p), ("K", c_int32), ("klow", c_int32),
+                ("val_codes", c_void_p), ("code_stride", c_int64), ("K", c_int32), ("klow", c_int32),
                 ("khigh", c_int32), ("top_num", c_int64), ("top_den", c_int64),
                 ("scale", c_float), ("out", c_void_p), ("u", c_void_p),
                 ("s_low", c_void_p), ("sel", c_void_p), ("s_high", c_void_p),
@@ -225,11 +225,20 @@ def sdkv_encode(x, dictionary, K: int, *, codes=None, coef_f32=None, resid_norm=
 def attn_args(q, dk, dv, key_codes, val_codes, klow, khigh, top_num, top_den, scale, out,
               key_low=None, u=None, s_low=None, sel=None, s_high=None, w=None) -> AttnArgs:
     B, Hq, d = q.shape
-    _, Hkv, T, K = key_codes.shape
+    if val_codes is None:
+        # one tensor [B, Hkv, T, 2, K]: each token's key record, then its value record
+        if key_codes.dim() != 5 or key_codes.shape[3] != 2:
+            raise ValueError("with val_codes=None, key_codes must be [B, Hkv, T, 2, K]")
+        _, Hkv, T, _, K = key_codes.shape
+        kp = _dev(key_codes, "key_codes")
+        vp, stride = kp + 4 * K, 2 * K
+    else:
+        _, Hkv, T, K = key_codes.shape
+        kp, vp, stride = _dev(key_codes, "key_codes"), _dev(val_codes, "val_codes"), 0
     return AttnArgs(q=_dev(q, "q"), q_dtype=_dtype_code(q), dk=_dev(dk, "dk"), dv=_dev(dv, "dv"),
                     dict_dtype=_dtype_code(dk), n_atoms=dk.shape[0], B=B, Hq=Hq, Hkv=Hkv, d=d,
-                    T=T, key_low=_dev(key_low, "key_low"), key_codes=_dev(key_codes, "key_codes"),
-                    val_codes=_dev(val_codes, "val_codes"), K=K, klow=klow, khigh=khigh,
+                    T=T, key_low=_dev(key_low, "key_low"), key_codes=kp,
+                    val_codes=vp, code_stride=stride, K=K, klow=klow, khigh=khigh,
                     top_num=top_num, top_den=top_den, scale=scale, out=_dev(out, "out"),
                     u=_dev(u, "u"), s_low=_dev(s_low, "s_low"), sel=_dev(sel, "sel"),
                     s_high=_dev(s_high, "s_high"), w=_dev(w, "w"))
@@ -247,9 +256,11 @@ def sdkv_decode_attn(q, dk, dv, key_codes, val_codes, *, klow: int, khigh: int,
                      key_low=None, out=None, debug: bool = False,
                      workspace: Optional[Workspace] = None, stream=None, stage_events=None):
     """Hierarchical coded decode attention. q [B,Hq,d] bf16; dk, dv
-    [n_atoms,d] bf16/fp32; key_codes, val_codes int32 [B,Hkv,T,K]; optional
-    key_low int32 [B,Hkv,T,klow]. Returns out fp32 [B,Hq,d], or with
-    debug=True a dict that also holds u, s_low, sel, s_high and w."""
+    [n_atoms,d] bf16/fp32; key_codes, val_codes int32 [B,Hkv,T,K], or
+    key_codes int32 [B,Hkv,T,2,K] (each token's key record, then its value
+    record) with val_codes=None; optional key_low int32 [B,Hkv,T,klow].
+    Returns out fp32 [B,Hq,d], or with debug=True a dict that also holds u,
+    s_low, sel, s_high and w."""
     torch = _torch()
     B, Hq, d = q.shape
     T = key_codes.shape[2]

@@ -74,6 +74,7 @@ static sdkv_status check_attn(const sdkv_attn_args* a) {
   if (a->T < 1 || a->T > 0x7FFFFFFF) return SDKV_ERR_SHAPE;
   if (a->n_atoms < 1 || a->n_atoms > 65536) return SDKV_ERR_SHAPE;
   if (a->K < 1 || a->K > 32) return SDKV_ERR_SHAPE;
+  if (a->code_stride != 0 && (a->code_stride < a->K || a->code_stride > 65536)) return SDKV_ERR_SHAPE;
   if (a->klow < 1 || a->klow > a->khigh || a->khigh > a->K) return SDKV_ERR_SHAPE;
   if (a->top_num < 1 || a->top_den < a->top_num || a->top_den > 0x7FFFFFFF) return SDKV_ERR_SHAPE;
   if (!isfinite(a->scale)) return SDKV_ERR_SHAPE;

@@ -104,8 +104,9 @@ struct RowsArgs {
   const float* U;           // [rows, N]
   const uint32_t* low;      // low-plane source; `low_words` words per token
   int low_words;
-  const uint32_t* kc;       // [B, Hkv, T, K]
+  const uint32_t* kc;       // [B, Hkv, T] records of K words, `rs` words apart
   const uint32_t* vc;
+  int64_t rs;
   int N, K, klow, khigh, Hq, Hkv, G, P;
   int row0, nrows;
   int64_t T, m, chunk;
@@ -297,8 +298,9 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
     sel = radix_select_local<SPT>(key, (uint32_t)a.m, sh, &offset, &count, &tau);
   } else {
     // s_low of a fixed sample of the row's tokens (the same in every
-    // workgroup of the row): all tokens if T <= kSampleN, else 256 runs of
-    // 16 consecutive tokens, run g starting at floor(g T / 256)
+    // workgroup of the row): all tokens if T <= kSampleN, else R = kSampleN /
+    // 16 runs of 16 consecutive tokens, run g starting at floor(g T / R)
+    // (inside the row: T > kSampleN = 16 R, so (R - 1) T / R + 15 < T)
     const int64_t ns = min((int64_t)kSampleN, a.T);
     const bool all = a.T <= kSampleN;
     uint32_t skey[kSamplePT];
@@ -308,7 +310,7 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
 #pragma unroll
       for (int j = 0; j < kSamplePT; ++j) {
         const int64_t i = min((int64_t)(tid + j * SB), ns - 1);
-        const int64_t t = all ? i : (((i >> 4) * a.T) >> 8) + (i & 15);
+        const int64_t t = all ? i : ((i >> 4) * a.T) / kSampleRuns + (i & 15);
         wps[j] = lo + t * lw;
 #pragma unroll
         for (int c = 0; c < 4; ++c) wd[j][c] = wps[j][min(c, a.klow - 1)];
@@ -380,8 +382,8 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   // the same thread handles the same entries in every later loop). Value
   // records are fetched in the same pass; their |coefficient| sums bound the
   // value weights for the fixed-point accumulation below.
-  const uint32_t* kbase = a.kc + kv * a.T * a.K;
-  const uint32_t* vbase = a.vc + kv * a.T * a.K;
+  const uint32_t* kbase = a.kc + kv * a.T * a.rs;
+  const uint32_t* vbase = a.vc + kv * a.T * a.rs;
   const bool one_batch = cnt <= (int64_t)SB * kTokBatch;
   // (lmax, vb): running max of s_high and sum_t exp(s_t - lmax) sum_j |kappa^v_tj|
   float lmax = -INFINITY, vb = 0.f;
@@ -398,8 +400,8 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
     uint32_t kw[kTokBatch][32];
 #pragma unroll
     for (int r = 0; r < kTokBatch; ++r) {
-      load_record<FAST>(kbase + tt[r] * a.K, a.K, a.khigh, kw[r]);
-      load_record<FAST>(vbase + tt[r] * a.K, a.K, a.K, vw[r]);
+      load_record<FAST>(kbase + tt[r] * a.rs, a.K, a.khigh, kw[r]);
+      load_record<FAST>(vbase + tt[r] * a.rs, a.K, a.K, vw[r]);
     }
 #pragma unroll
     for (int r = 0; r < kTokBatch; ++r) {
@@ -472,7 +474,7 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
         tt[r] = min(max(t, (int64_t)0), a.T - 1);
       }
 #pragma unroll
-      for (int r = 0; r < kTokBatch; ++r) load_record<FAST>(vbase + tt[r] * a.K, a.K, a.K, vw[r]);
+      for (int r = 0; r < kTokBatch; ++r) load_record<FAST>(vbase + tt[r] * a.rs, a.K, a.K, vw[r]);
     }
 #pragma unroll
     for (int r = 0; r < kTokBatch; ++r) {
@@ -946,7 +948,8 @@ sdkv_status launch_decode(const sdkv_attn_args* a, const DecodePlan& p, void* ws
   RowsArgs ra;
   ra.U = U;
   ra.low = a->key_low ? a->key_low : a->key_codes;
-  ra.low_words = a->key_low ? a->klow : a->K;
+  ra.rs = a->code_stride ? a->code_stride : a->K;
+  ra.low_words = a->key_low ? a->klow : (int)ra.rs;
   ra.kc = a->key_codes;
   ra.vc = a->val_codes;
   ra.N = a->n_atoms;
@@ -973,7 +976,8 @@ sdkv_status launch_decode(const sdkv_attn_args* a, const DecodePlan& p, void* ws
   ra.xchg = xchg;
   ra.bar = bar;
   ra.err = err;
-  const bool aligned = (((uintptr_t)a->key_codes | (uintptr_t)a->val_codes) & 15u) == 0;
+  const bool aligned = (((uintptr_t)a->key_codes | (uintptr_t)a->val_codes) & 15u) == 0 &&
+                       ra.rs % 4 == 0;
   const void* kfn = pick_rows_kernel(p.spt, p.fast && aligned);
   if (!kfn) return SDKV_ERR_UNSUPPORTED;
   ra.ticket = (uint32_t*)(base + p.off_ticket);

@@ -380,6 +380,8 @@ __device__ __forceinline__ int value_bin(uint32_t k, float base, float inv) {
 
 constexpr int kSampleN = 4096;             // shared sample size (tokens)
 constexpr int kSamplePT = kSampleN / SB;
+constexpr int kSampleRuns = kSampleN / 16;  // runs of 16 consecutive tokens
+static_assert(kSampleN % SB == 0 && (kSampleRuns & (kSampleRuns - 1)) == 0, "sample layout");
 
 // Sample-window select with one cross-workgroup synchronisation.
 //

@@ -45,7 +45,7 @@ extern "C" {
 #define SDKV_API
 #endif
 
-#define SDKV_ABI_VERSION 1
+#define SDKV_ABI_VERSION 2
 
 typedef int32_t sdkv_status;
 #define SDKV_OK 0
@@ -126,8 +126,15 @@ typedef struct sdkv_attn_args {
   int64_t T;            /* cached tokens, >= 1                            */
   const uint32_t* key_low;   /* [B, Hkv, T, klow] first klow key words, or
                                 NULL to read them from key_codes          */
-  const uint32_t* key_codes; /* [B, Hkv, T, K] key code words             */
-  const uint32_t* val_codes; /* [B, Hkv, T, K] value code words           */
+  const uint32_t* key_codes; /* [B, Hkv, T] records of K key code words    */
+  const uint32_t* val_codes; /* [B, Hkv, T] records of K value code words  */
+  int64_t code_stride;  /* words from one token's record to the next, in
+                           both key_codes and val_codes: 0 means K (dense
+                           [B, Hkv, T, K] arrays); 2K with val_codes =
+                           key_codes + K stores each token's key and value
+                           records side by side ([B, Hkv, T, 2, K]), so
+                           that both come in one 128-byte line at K = 16.
+                           Must be 0 or in [K, 65536].                    */
   int32_t K;            /* 1 .. 32                                        */
   int32_t klow, khigh;  /* 1 <= klow <= khigh <= K                        */
   int64_t top_num, top_den; /* selected fraction, 0 < top_num <= top_den  */

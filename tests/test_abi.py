@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) == 9, names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.sdkv_abi_version() == 1
+    assert lib.sdkv_abi_version() == 2
 
 
 def test_status_strings():
@@ -77,6 +77,8 @@ def test_decode_workspace_query():
     ("q_dtype", 7, sd.SDKV_ERR_DTYPE), ("dict_dtype", -1, sd.SDKV_ERR_DTYPE),
     ("q_dtype", sd.SDKV_F32, sd.SDKV_ERR_UNSUPPORTED),
     ("n_atoms", 40000, sd.SDKV_ERR_UNSUPPORTED),
+    ("code_stride", 15, sd.SDKV_ERR_SHAPE), ("code_stride", -32, sd.SDKV_ERR_SHAPE),
+    ("code_stride", 65537, sd.SDKV_ERR_SHAPE),
 ])
 def test_decode_validation(field, value, status):
     a = good_attn(**{field: value})
@@ -84,6 +86,14 @@ def test_decode_validation(field, value, status):
     assert st == status
     # the compute entry point rejects it the same way, before any enqueue
     assert sd.lib().sdkv_decode_attn(ctypes.byref(a), ctypes.c_void_p(FAKE), 1 << 40, None) == status
+
+
+def test_decode_code_stride_accepted():
+    # dense (0), interleaved key/value records (2K) and any stride >= K plan the same workspace
+    base = ws_status(good_attn())
+    assert base[0] == sd.SDKV_OK
+    for stride in (16, 32, 17, 65536):
+        assert ws_status(good_attn(code_stride=stride)) == base
 
 
 def test_decode_workspace_errors():

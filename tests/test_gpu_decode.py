@@ -11,7 +11,7 @@ from tests import gpu_helpers as H
 pytestmark = pytest.mark.gpu
 
 
-def run_gpu(case, debug=True, key_low=True, ws=None):
+def run_gpu(case, debug=True, key_low=True, ws=None, interleaved=False):
     import decode_attention_sparse_amd as sd
     torch = H.torch_mod()
     q = H.to_bf16(case.q)
@@ -19,7 +19,12 @@ def run_gpu(case, debug=True, key_low=True, ws=None):
         dk, dv = H.to_bf16(case.dk), H.to_bf16(case.dv)
     else:
         dk, dv = H.to_f32(case.dk), H.to_f32(case.dv)
-    kc, vc = H.to_words(case.key_codes), H.to_words(case.val_codes)
+    if interleaved:
+        # [B, Hkv, T, 2, K]: each token's key record, then its value record
+        kc = H.to_words(np.stack([case.key_codes, case.val_codes], axis=3))
+        vc = None
+    else:
+        kc, vc = H.to_words(case.key_codes), H.to_words(case.val_codes)
     kl = H.to_words(case.key_low) if key_low else None
     r = sd.sdkv_decode_attn(q, dk, dv, kc, vc, klow=case.klow, khigh=case.khigh,
                             top_num=case.top_num, top_den=case.top_den, scale=case.scale,
@@ -180,3 +185,27 @@ def test_long_rows_many_workgroups():
     H.log("decode B=1 Hq=32 Hkv=8 T=262144")
     case = synth.decode_case(B=1, Hq=32, Hkv=8, T=262144, seed=12)
     compare(case, run_gpu(case))
+
+
+def test_interleaved_key_value_records():
+    """Key and value records side by side per token ([B, Hkv, T, 2, K], a
+    record stride of 2K words): the same results as separate arrays, with and
+    without a separate low plane, and against the oracle."""
+    H.log("decode interleaved records B=2 Hq=8 Hkv=2 T=40000")
+    case = synth.decode_case(B=2, Hq=8, Hkv=2, T=40000, seed=13, n_atoms=4096)
+    a = run_gpu(case)
+    for kl in (True, False):
+        b = run_gpu(case, key_low=kl, interleaved=True)
+        for k in ("u", "s_low", "sel", "s_high", "w", "out"):
+            assert np.array_equal(a[k], b[k]), (kl, k)
+    compare(case, b)
+
+
+def test_interleaved_records_128k_layer():
+    """The benchmark's launch (non-debug, interleaved records) on the 128K
+    layer equals the separate-array launch bit for bit."""
+    H.log("decode llama_layer_128k interleaved vs separate (non-debug)")
+    case = synth.decode_case("llama_layer_128k")
+    a = run_gpu(case, debug=False)["out"]
+    b = run_gpu(case, debug=False, interleaved=True)["out"]
+    assert np.array_equal(a, b)
