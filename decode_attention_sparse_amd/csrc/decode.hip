@@ -509,10 +509,13 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   float* dst = a.wpart + ((int64_t)row * a.P + p) * a.N;
   const float invS = 1.f / S;
   const int n4 = a.N >> 2;
+  // (streaming stores: the partials are read once, by the next kernel)
   for (int i = tid; i < n4; i += SB) {
     const int4 v = ((const int4*)s_w)[i];
-    ((float4*)dst)[i] = make_float4((float)v.x * invS, (float)v.y * invS, (float)v.z * invS,
-                                    (float)v.w * invS);
+    __builtin_nontemporal_store((float)v.x * invS, &dst[4 * i]);
+    __builtin_nontemporal_store((float)v.y * invS, &dst[4 * i + 1]);
+    __builtin_nontemporal_store((float)v.z * invS, &dst[4 * i + 2]);
+    __builtin_nontemporal_store((float)v.w * invS, &dst[4 * i + 3]);
   }
   for (int i = (n4 << 2) + tid; i < a.N; i += SB) dst[i] = (float)s_w[i] * invS;
   if (tid == 0) a.stats[(int64_t)row * a.P + p] = make_float2(cnt > 0 ? M : -INFINITY, lsum_all);
