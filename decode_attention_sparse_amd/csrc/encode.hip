@@ -12,7 +12,11 @@
 //     scaled by a power of two and rounded to fp16; the dictionary is an fp16
 //     copy (exact for bf16 atoms of unit-norm size). Each lane keeps, per
 //     output row it owns, the largest |c| seen in its atom column and that
-//     atom's tile (strict '>' keeps the lowest index within the lane).
+//     atom's tile, packed in one word: |c| with its low 12 mantissa bits
+//     replaced by the complement of the tile index, so a single unsigned
+//     max keeps the larger value and, among equal truncated values, the
+//     lower tile. (The truncation, at most 2^-11 of |c|, is well inside the
+//     recheck window below.)
 //   * exact pick: per vector, the 16 column winners whose screened |c| lie
 //     within a window of the best are recomputed in fp32 from the original
 //     dictionary; the largest exact |c| wins, lowest atom index on ties.
@@ -163,12 +167,14 @@ __global__ __launch_bounds__(EB) void k_encode(EncArgs a) {
     }
 
     // --- screen sweep over all atoms ------------------------------------------
-    float best[4][4];
-    int32_t bidx[4][4];
+    // running best per output: |c| with its low 12 mantissa bits replaced by
+    // the complement of the 16-atom tile index, so one unsigned max keeps the
+    // larger |c| and, among equal truncated values, the lower tile
+    uint32_t bkey[4][4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { best[rt][i] = -1.f; bidx[rt][i] = 0; }
+      for (int i = 0; i < 4; ++i) bkey[rt][i] = 0u;
 
     constexpr int SEGS = D / 8;                  // 16-byte segments per atom row
     constexpr int LOADS = (ECH * SEGS) / EB;     // 16-byte loads per thread per chunk
@@ -201,20 +207,20 @@ __global__ __launch_bounds__(EB) void k_encode(EncArgs a) {
 #pragma unroll
         for (int s = 0; s < KS; ++s)
           bfr[s] = *(const u32x4*)(&s_b[buf][(tt * 16 + (l & 15)) * BP + 32 * s + 8 * (l >> 4)]);
-        const int tile = c * (ECH / 16) + tt;
+        const uint32_t tcode = ~(uint32_t)(c * (ECH / 16) + tt) & 0xFFFu;
+        // the four row tiles' accumulations interleaved (independent chains)
+        f32x4 acc[4];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int s = 0; s < KS; ++s) acc = mfma_f16(af[rt][s], bfr[s], acc);
+        for (int s = 0; s < KS; ++s)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float v = fabsf(acc[i]);
-            const bool gt = v > best[rt][i];
-            best[rt][i] = gt ? v : best[rt][i];
-            bidx[rt][i] = gt ? tile : bidx[rt][i];
-          }
-        }
+          for (int rt = 0; rt < 4; ++rt) acc[rt] = mfma_f16(af[rt][s], bfr[s], acc[rt]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            bkey[rt][i] = max(bkey[rt][i], (__float_as_uint(acc[rt][i]) & 0x7FFFF000u) | tcode);
       }
       if (c + 1 < nchunks) store_chunk(buf ^ 1);
       __syncthreads();
@@ -226,8 +232,8 @@ __global__ __launch_bounds__(EB) void k_encode(EncArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int rl = w * 64 + rt * 16 + 4 * (l >> 4) + i;
-        s_wv[rl * 16 + (l & 15)] = best[rt][i];
-        s_wi[rl * 16 + (l & 15)] = bidx[rt][i] * 16 + (l & 15);
+        s_wv[rl * 16 + (l & 15)] = __uint_as_float(bkey[rt][i] & 0x7FFFF000u);
+        s_wi[rl * 16 + (l & 15)] = (int)((~bkey[rt][i]) & 0xFFFu) * 16 + (l & 15);
       }
     __syncthreads();
 
