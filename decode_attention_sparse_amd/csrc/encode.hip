@@ -171,6 +171,9 @@ __global__ __launch_bounds__(EB) void k_encode(EncArgs a) {
     // the complement of the 16-atom tile index, so one unsigned max keeps the
     // larger |c| and, among equal truncated values, the lower tile
     uint32_t bkey[4][4];
+    // the mask lives in a register, so (x & mask) | code is one 3-input op
+    uint32_t vmask = 0x7FFFF000u;
+    asm volatile("" : "+v"(vmask));
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -201,26 +204,34 @@ __global__ __launch_bounds__(EB) void k_encode(EncArgs a) {
     for (int c = 0; c < nchunks; ++c) {
       const int buf = c & 1;
       if (c + 1 < nchunks) load_chunk(c + 1);
+      // tiles in pairs: 8 independent accumulation chains, then one 3-way
+      // max per output for the two tiles
 #pragma unroll
-      for (int tt = 0; tt < ECH / 16; ++tt) {
-        u32x4 bfr[KS];
+      for (int tt = 0; tt < ECH / 16; tt += 2) {
+        f32x4 acc[2][4];
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
-          bfr[s] = *(const u32x4*)(&s_b[buf][(tt * 16 + (l & 15)) * BP + 32 * s + 8 * (l >> 4)]);
-        const uint32_t tcode = ~(uint32_t)(c * (ECH / 16) + tt) & 0xFFFu;
-        // the four row tiles' accumulations interleaved (independent chains)
-        f32x4 acc[4];
+        for (int h = 0; h < 2; ++h) {
+          u32x4 bfr[KS];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int s = 0; s < KS; ++s)
+            bfr[s] = *(const u32x4*)(&s_b[buf][((tt + h) * 16 + (l & 15)) * BP + 32 * s + 8 * (l >> 4)]);
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
+          for (int rt = 0; rt < 4; ++rt) acc[h][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int rt = 0; rt < 4; ++rt) acc[rt] = mfma_f16(af[rt][s], bfr[s], acc[rt]);
+          for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) acc[h][rt] = mfma_f16(af[rt][s], bfr[s], acc[h][rt]);
+        }
+        const uint32_t tc0 = ~(uint32_t)(c * (ECH / 16) + tt) & 0xFFFu;
+        const uint32_t tc1 = tc0 - 1u;  // the next tile's code
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            bkey[rt][i] = max(bkey[rt][i], (__float_as_uint(acc[rt][i]) & 0x7FFFF000u) | tcode);
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t k0 = (__float_as_uint(acc[0][rt][i]) & vmask) | tc0;
+            const uint32_t k1 = (__float_as_uint(acc[1][rt][i]) & vmask) | tc1;
+            bkey[rt][i] = max(bkey[rt][i], max(k0, k1));
+          }
       }
       if (c + 1 < nchunks) store_chunk(buf ^ 1);
       __syncthreads();
