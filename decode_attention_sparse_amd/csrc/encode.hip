@@ -63,12 +63,6 @@ __global__ __launch_bounds__(256) void k_prep_dict(const void* dict, int dict_f3
 }
 
 template <int D>
-__device__ __forceinline__ float dict_elem(const EncArgs& a, int atom, int k) {
-  return a.dict_f32 ? ((const float*)a.dict)[(int64_t)atom * D + k]
-                    : bf16_to_f32(((const uint16_t*)a.dict)[(int64_t)atom * D + k]);
-}
-
-template <int D>
 __device__ __forceinline__ float exact_corr(const EncArgs& a, const float* rrow, int atom) {
   float s = 0.f;
   if (a.dict_f32) {
@@ -267,11 +261,37 @@ __global__ __launch_bounds__(EB) void k_encode(EncArgs a) {
           if (ax > babs || (ax == babs && atom < ba)) { babs = ax; bc = cx; ba = atom; }
         }
         if (ba == 0x7FFFFFFF) { ba = 0; bc = exact_corr<D>(a, rr, 0); }
+        // update with vector loads and stores, in element order
         float nrm = 0.f;
-        for (int k = 0; k < D; ++k) {
-          const float v = fmaf(-bc, dict_elem<D>(a, ba, k), rr[k]);
-          rr[k] = v;
-          nrm = fmaf(v, v, nrm);
+        if (a.dict_f32) {
+          const float4* dp = (const float4*)((const float*)a.dict + (int64_t)ba * D);
+#pragma unroll 4
+          for (int k = 0; k < D / 4; ++k) {
+            const float4 dv = dp[k];
+            float4 v = ((const float4*)rr)[k];
+            v.x = fmaf(-bc, dv.x, v.x); nrm = fmaf(v.x, v.x, nrm);
+            v.y = fmaf(-bc, dv.y, v.y); nrm = fmaf(v.y, v.y, nrm);
+            v.z = fmaf(-bc, dv.z, v.z); nrm = fmaf(v.z, v.z, nrm);
+            v.w = fmaf(-bc, dv.w, v.w); nrm = fmaf(v.w, v.w, nrm);
+            ((float4*)rr)[k] = v;
+          }
+        } else {
+          const u32x4* dp = (const u32x4*)((const uint16_t*)a.dict + (int64_t)ba * D);
+#pragma unroll 4
+          for (int k = 0; k < D / 8; ++k) {
+            const u32x4 dv = dp[k];
+            float4 v0 = ((const float4*)rr)[2 * k], v1 = ((const float4*)rr)[2 * k + 1];
+            v0.x = fmaf(-bc, bf16_lo(dv[0]), v0.x); nrm = fmaf(v0.x, v0.x, nrm);
+            v0.y = fmaf(-bc, bf16_hi(dv[0]), v0.y); nrm = fmaf(v0.y, v0.y, nrm);
+            v0.z = fmaf(-bc, bf16_lo(dv[1]), v0.z); nrm = fmaf(v0.z, v0.z, nrm);
+            v0.w = fmaf(-bc, bf16_hi(dv[1]), v0.w); nrm = fmaf(v0.w, v0.w, nrm);
+            v1.x = fmaf(-bc, bf16_lo(dv[2]), v1.x); nrm = fmaf(v1.x, v1.x, nrm);
+            v1.y = fmaf(-bc, bf16_hi(dv[2]), v1.y); nrm = fmaf(v1.y, v1.y, nrm);
+            v1.z = fmaf(-bc, bf16_lo(dv[3]), v1.z); nrm = fmaf(v1.z, v1.z, nrm);
+            v1.w = fmaf(-bc, bf16_hi(dv[3]), v1.w); nrm = fmaf(v1.w, v1.w, nrm);
+            ((float4*)rr)[2 * k] = v0;
+            ((float4*)rr)[2 * k + 1] = v1;
+          }
         }
         s_rnorm[rl] = sqrtf(nrm);
         a.codes[rowg * a.K + step] = (uint32_t)ba | (f32_to_f16_bits(bc) << 16);
