@@ -201,6 +201,18 @@ def test_interleaved_key_value_records():
     compare(case, b)
 
 
+def test_interleaved_records_generic_path():
+    """Interleaved records on the generic (K = 32, d = 64) path."""
+    H.log("decode interleaved records d=64 K=32")
+    case = synth.decode_case(B=1, Hq=6, Hkv=3, T=3001, seed=14, n_atoms=3000, d=64, K=32,
+                             klow=5, khigh=20, top_num=1, top_den=4)
+    a = run_gpu(case)
+    b = run_gpu(case, interleaved=True)
+    for k in ("u", "s_low", "sel", "s_high", "w", "out"):
+        assert np.array_equal(a[k], b[k]), k
+    compare(case, b)
+
+
 def test_interleaved_records_128k_layer():
     """The benchmark's launch (non-debug, interleaved records) on the 128K
     layer equals the separate-array launch bit for bit."""
