@@ -201,6 +201,7 @@ def bench_decode(args, torch, sd, synth, ev):
     traffic = read_traffic(names[dom], "llama_layer_128k")
     res = dict(
         value=B * T / (ms * 1e-3), ms=ms, stage_ms=dict(zip(names, stage_ms)),
+        dk=base["dk"], dv=base["dv"],
         roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                   "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                   "traffic": traffic, "kernel": names[dom],
@@ -217,6 +218,50 @@ def bench_decode(args, torch, sd, synth, ev):
 # ---------------------------------------------------------------------------
 # encode (prefill)
 # ---------------------------------------------------------------------------
+def bench_append(args, torch, sd, synth, ev, dec):
+    """One decode step's append on the 128K layer shape: the new token's 8 key
+    and 8 value vectors encoded (K=16 over the layer's two 32,768-atom
+    dictionaries) into a slot of an interleaved code cache."""
+    case = dec["case"]
+    dev = "cuda"
+    B, Hkv, d, K = case.B, case.Hkv, case.d, case.K
+    rng = np.random.default_rng(7)
+    dk = dec["dk"]
+    dv = dec["dv"]
+    Tc = 64
+    kv = torch.zeros((B, Hkv, Tc, 2, K), dtype=torch.int32, device=dev)
+    low = torch.zeros((B, Hkv, Tc, case.klow), dtype=torch.int32, device=dev)
+    xs = [(torch.from_numpy(rng.standard_normal((B, Hkv, d), dtype=np.float32)).to(dev).to(torch.bfloat16),
+           torch.from_numpy(rng.standard_normal((B, Hkv, d), dtype=np.float32)).to(dev).to(torch.bfloat16))
+          for _ in range(4)]
+    ws = sd.Workspace()
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        xk, xv = xs[i % len(xs)]
+        sd.sdkv_append_tokens(xk, xv, dk, dv, kv, None, i % Tc, key_low=low, workspace=ws)
+
+    for i in range(5):
+        step(i)
+    torch.cuda.synchronize()
+    n = 20
+    t0, t1 = ev.create(2)
+    ev.record(t0, stream.cuda_stream)
+    for i in range(n):
+        step(i)
+    ev.record(t1, stream.cuda_stream)
+    torch.cuda.synchronize()
+    ms = ev.ms(t0, t1) / n
+    dict_bytes = 2 * K * case.n_atoms * d * 2  # each pursuit step reads its dictionary once
+    return {"metric": "decode-step append encode", "us_per_step": round(ms * 1e3, 2),
+            "vectors": 2 * B * Hkv, "value": round(2 * B * Hkv / (ms * 1e-3), 1),
+            "unit": "vectors/s", "launches": K + 1,
+            "dictionary_bytes_per_step": dict_bytes,
+            "dictionary_GBs": round(dict_bytes / (ms * 1e-3) / 1e9, 1),
+            "config": {"B": B, "Hkv": Hkv, "d": d, "K": K, "n_atoms": case.n_atoms,
+                       "path": "small-batch exact pursuit (n <= 64), key and value encodes sharing launches"}}
+
+
 def bench_encode(args, torch, sd, synth, ev):
     dev = "cuda"
     streams = []
@@ -356,6 +401,8 @@ def main():
     dec = bench_decode(args, torch, sd, synth, ev)
     log(f"  {dec['ms'] * 1e3:.1f} us/step, stages (us): "
         + ", ".join(f"{k} {v * 1e3:.1f}" for k, v in dec["stage_ms"].items()))
+    app = bench_append(args, torch, sd, synth, ev, dec)
+    log(f"  decode-step append (16 vectors): {app['us_per_step']:.1f} us")
     enc = None
     if not args.no_encode:
         log("encode benchmark (524,288 vectors)")
@@ -383,6 +430,7 @@ def main():
         "stage_us": {k: round(v * 1e3, 2) for k, v in dec["stage_ms"].items()},
         "cpu_baseline": cpu,
     }
+    line["append"] = app
     if enc is not None:
         line["encode"] = {
             "metric": "KV vectors encoded/s", "value": round(enc["value"], 1),

@@ -36,8 +36,8 @@ class EncodeArgs(ctypes.Structure):
     _fields_ = [("x", c_void_p), ("x_dtype", c_int32), ("dict", c_void_p),
                 ("dict_dtype", c_int32), ("n", c_int64), ("d", c_int32),
                 ("n_atoms", c_int32), ("K", c_int32), ("codes", c_void_p),
-                ("coef_f32", c_void_p), ("resid_norm", c_void_p),
-                ("low_plane", c_void_p), ("klow", c_int32),
+                ("codes_ld", c_int64), ("coef_f32", c_void_p), ("resid_norm", c_void_p),
+                ("low_plane", c_void_p), ("low_ld", c_int64), ("klow", c_int32),
                 ("stage_events", c_void_p)]
 
 
@@ -89,6 +89,10 @@ def _lib():
         lib.sdkv_encode_workspace.argtypes = [P(EncodeArgs), P(c_size_t)]
         lib.sdkv_encode.restype = c_int32
         lib.sdkv_encode.argtypes = [P(EncodeArgs), c_void_p, c_size_t, c_void_p]
+        lib.sdkv_encode_pair_workspace.restype = c_int32
+        lib.sdkv_encode_pair_workspace.argtypes = [P(EncodeArgs), P(EncodeArgs), P(c_size_t)]
+        lib.sdkv_encode_pair.restype = c_int32
+        lib.sdkv_encode_pair.argtypes = [P(EncodeArgs), P(EncodeArgs), c_void_p, c_size_t, c_void_p]
         lib.sdkv_decode_attn_workspace.restype = c_int32
         lib.sdkv_decode_attn_workspace.argtypes = [P(AttnArgs), P(c_size_t)]
         lib.sdkv_decode_attn.restype = c_int32
@@ -290,6 +294,77 @@ def sdkv_decode_attn(q, dk, dv, key_codes, val_codes, *, klow: int, khigh: int,
     return out
 
 
+def _encode_rows_args(x, dictionary, K, codes_ptr, codes_ld, low_ptr, low_ld, klow):
+    """EncodeArgs writing code rows at codes_ptr + i * codes_ld words (and
+    low-plane rows at low_ptr + i * low_ld), for appends into a cache."""
+    n, d = x.shape
+    return EncodeArgs(x=_dev(x, "x"), x_dtype=_dtype_code(x), dict=_dev(dictionary, "dictionary"),
+                      dict_dtype=_dtype_code(dictionary), n=n, d=d, n_atoms=dictionary.shape[0],
+                      K=K, codes=codes_ptr, codes_ld=codes_ld, low_plane=low_ptr, low_ld=low_ld,
+                      klow=klow if low_ptr else 0)
+
+
+def _encode_into(a, workspace, stream):
+    nb = c_size_t(0)
+    _check(_lib().sdkv_encode_workspace(ctypes.byref(a), ctypes.byref(nb)), "sdkv_encode_workspace")
+    wp, wn = _ws(workspace, nb.value)
+    _check(_lib().sdkv_encode(ctypes.byref(a), ctypes.c_void_p(wp), wn, _stream(stream)),
+           "sdkv_encode")
+
+
+def sdkv_encode_pair(ak: "EncodeArgs", av: "EncodeArgs", workspace: Optional[Workspace] = None,
+                     stream=None):
+    """Two small encodes (n <= 64, same shape) in one sequence of launches,
+    from marshalled EncodeArgs; each side gets what sdkv_encode gives it."""
+    nb = c_size_t(0)
+    _check(_lib().sdkv_encode_pair_workspace(ctypes.byref(ak), ctypes.byref(av), ctypes.byref(nb)),
+           "sdkv_encode_pair_workspace")
+    wp, wn = _ws(workspace if workspace is not None else Workspace(), nb.value)
+    _check(_lib().sdkv_encode_pair(ctypes.byref(ak), ctypes.byref(av), ctypes.c_void_p(wp), wn,
+                                   _stream(stream)), "sdkv_encode_pair")
+
+
+def sdkv_append_tokens(xk, xv, dk, dv, key_codes, val_codes, t: int, *, key_low=None,
+                       workspace: Optional[Workspace] = None, stream=None):
+    """Encode one decode step's new key and value vectors xk, xv [B, Hkv, d]
+    and write their codes into slot t of the cache, in place: key_codes and
+    val_codes int32 [B, Hkv, T, K], or key_codes [B, Hkv, T, 2, K] with
+    val_codes=None (records side by side); key_low int32 [B, Hkv, T, klow]
+    receives the key's first klow words. With n = B*Hkv <= 64 both sides
+    take the exact small-batch path together, in one sequence of K + 1
+    launches (sdkv_encode_pair); larger batches make two sdkv_encode calls."""
+    B, Hkv, d = xk.shape
+    if val_codes is None:
+        if key_codes.dim() != 5 or key_codes.shape[3] != 2:
+            raise ValueError("with val_codes=None, key_codes must be [B, Hkv, T, 2, K]")
+        T, K = key_codes.shape[2], key_codes.shape[4]
+        base = _dev(key_codes, "key_codes")
+        stride = 2 * K
+        kp, vp = base + 4 * t * stride, base + 4 * (t * stride + K)
+    else:
+        T, K = key_codes.shape[2], key_codes.shape[3]
+        stride = K
+        kp = _dev(key_codes, "key_codes") + 4 * t * K
+        vp = _dev(val_codes, "val_codes") + 4 * t * K
+    if not 0 <= t < T:
+        raise ValueError(f"slot {t} outside the cache's {T} tokens")
+    if tuple(key_codes.shape[:2]) != (B, Hkv) or tuple(xv.shape) != (B, Hkv, d):
+        raise ValueError("cache and new-token shapes disagree")
+    lp, lld, klow = 0, 0, 0
+    if key_low is not None:
+        klow = key_low.shape[3]
+        lp = _dev(key_low, "key_low") + 4 * t * klow
+        lld = T * klow
+    ws = workspace if workspace is not None else Workspace()
+    ak = _encode_rows_args(xk.reshape(B * Hkv, d), dk, K, kp, T * stride, lp, lld, klow)
+    av = _encode_rows_args(xv.reshape(B * Hkv, d), dv, K, vp, T * stride, 0, 0, 0)
+    if B * Hkv <= 64 and dk.shape == dv.shape and dk.dtype == dv.dtype:
+        sdkv_encode_pair(ak, av, ws, stream)
+    else:
+        _encode_into(ak, ws, stream)
+        _encode_into(av, ws, stream)
+
+
 class DecodeCall:
     """A decode-attention call whose arguments and workspace are marshalled
     once; launch() then costs one C call. Keeps references to every tensor it
@@ -396,4 +471,5 @@ def sdkv_select_topk(scores, k: int, *, idx_out=None, thr_out=None,
 
 __all__ = ["sdkv_encode", "sdkv_decode_attn", "sdkv_select_topk", "selected_count",
            "Workspace", "SdkvError", "lib", "LIB_PATH", "HEADER", "EncodeArgs", "AttnArgs",
+           "sdkv_append_tokens", "sdkv_encode_pair",
            "attn_args", "decode_attn_workspace_bytes", "DecodeCall", "EncodeCall"]

@@ -61,6 +61,10 @@ static sdkv_status check_encode(const sdkv_encode_args* a) {
   if (a->n_atoms < 1 || a->n_atoms > 65536) return SDKV_ERR_SHAPE;
   if (a->K < 1 || a->K > 32) return SDKV_ERR_SHAPE;
   if (a->low_plane && (a->klow < 1 || a->klow > a->K)) return SDKV_ERR_SHAPE;
+  if (a->codes_ld != 0 && (a->codes_ld < a->K || a->codes_ld > ((int64_t)1 << 40)))
+    return SDKV_ERR_SHAPE;
+  if (a->low_plane && a->low_ld != 0 && (a->low_ld < a->klow || a->low_ld > ((int64_t)1 << 40)))
+    return SDKV_ERR_SHAPE;
   if (a->n > ((int64_t)1 << 40)) return SDKV_ERR_UNSUPPORTED;
   return SDKV_OK;
 }
@@ -132,6 +136,52 @@ sdkv_status sdkv_encode(const sdkv_encode_args* args, void* ws, size_t ws_bytes,
     if (p.total > 0 && !ws) return SDKV_ERR_NULL;
     if (ws_bytes < p.total) return SDKV_ERR_WORKSPACE;
     return launch_encode(args, p, ws, (hipStream_t)stream);
+  } catch (...) {
+    return SDKV_ERR_DEVICE;
+  }
+}
+
+static sdkv_status plan_pair(const sdkv_encode_args* a0, const sdkv_encode_args* a1,
+                             EncodePlan* p0, EncodePlan* p1, size_t* off1, size_t* total) {
+  sdkv_status s = check_encode(a0);
+  if (s != SDKV_OK) return s;
+  s = check_encode(a1);
+  if (s != SDKV_OK) return s;
+  if (a0->n != a1->n || a0->d != a1->d || a0->n_atoms != a1->n_atoms || a0->K != a1->K ||
+      a0->dict_dtype != a1->dict_dtype)
+    return SDKV_ERR_SHAPE;
+  if ((s = plan_encode(a0, p0)) != SDKV_OK || (s = plan_encode(a1, p1)) != SDKV_OK) return s;
+  if (!p0->small || !p1->small) return SDKV_ERR_UNSUPPORTED;
+  *off1 = align_up(p0->total, 256);
+  *total = *off1 + p1->total;
+  return SDKV_OK;
+}
+
+sdkv_status sdkv_encode_pair_workspace(const sdkv_encode_args* a0, const sdkv_encode_args* a1,
+                                       size_t* bytes) {
+  try {
+    if (!bytes) return SDKV_ERR_NULL;
+    EncodePlan p0, p1;
+    size_t off1 = 0, total = 0;
+    const sdkv_status s = plan_pair(a0, a1, &p0, &p1, &off1, &total);
+    if (s != SDKV_OK) return s;
+    *bytes = total;
+    return SDKV_OK;
+  } catch (...) {
+    return SDKV_ERR_DEVICE;
+  }
+}
+
+sdkv_status sdkv_encode_pair(const sdkv_encode_args* a0, const sdkv_encode_args* a1, void* ws,
+                             size_t ws_bytes, void* stream) {
+  try {
+    EncodePlan p0, p1;
+    size_t off1 = 0, total = 0;
+    const sdkv_status s = plan_pair(a0, a1, &p0, &p1, &off1, &total);
+    if (s != SDKV_OK) return s;
+    if (!ws) return SDKV_ERR_NULL;
+    if (ws_bytes < total) return SDKV_ERR_WORKSPACE;
+    return launch_encode_pair(a0, p0, (char*)ws, a1, p1, (char*)ws + off1, (hipStream_t)stream);
   } catch (...) {
     return SDKV_ERR_DEVICE;
   }

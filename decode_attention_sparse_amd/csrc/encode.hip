@@ -43,9 +43,11 @@ struct EncArgs {
   int64_t n;
   int N, npad, K, klow;
   uint32_t* codes;
+  int64_t codes_ld;
   float* coef_f32;
   float* resid_norm;
   uint32_t* low_plane;
+  int64_t low_ld;
 };
 
 // fp16 screen copy of the dictionary, zero rows past N.
@@ -294,7 +296,7 @@ __global__ __launch_bounds__(EB) void k_encode(EncArgs a) {
           }
         }
         s_rnorm[rl] = sqrtf(nrm);
-        a.codes[rowg * a.K + step] = (uint32_t)ba | (f32_to_f16_bits(bc) << 16);
+        a.codes[rowg * a.codes_ld + step] = (uint32_t)ba | (f32_to_f16_bits(bc) << 16);
         if (a.coef_f32) a.coef_f32[rowg * a.K + step] = bc;
       }
     }
@@ -306,13 +308,340 @@ __global__ __launch_bounds__(EB) void k_encode(EncArgs a) {
   if (rowg < a.n) {
     if (a.resid_norm) a.resid_norm[rowg] = s_rnorm[tid];
     if (a.low_plane)
-      for (int j = 0; j < a.klow; ++j) a.low_plane[rowg * a.klow + j] = a.codes[rowg * a.K + j];
+      for (int j = 0; j < a.klow; ++j) a.low_plane[rowg * a.low_ld + j] = a.codes[rowg * a.codes_ld + j];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Few vectors (n <= kSmallN, e.g. one decode step's new tokens): the same
+// pursuit with every correlation exact in fp32 and the atoms spread over the
+// device, one launch per step. Launch `step` (0 .. K) of k_small, for the
+// problem blockIdx.y (a key and a value encode can share the launches):
+//   * loads, all at once: its atom row, r_{step-1} (x at step 0) and the
+//     per-workgroup winners of step - 1;
+//   * every workgroup reduces the same winners (largest |c|, lowest atom on
+//     ties), so all agree on (g, a), and forms r_step = r_{step-1} - g d_a;
+//     workgroup 0 stores r_step and the code word of step - 1;
+//   * step < K: correlates r_step with its ECHS atoms and stores its
+//     per-vector winner (c, atom);
+//   * step == K: workgroup 0 writes the residual norms and the low plane.
+// Residuals and winners alternate between two buffers by step parity.
+// ---------------------------------------------------------------------------
+constexpr int kSmallN = 64;        // vectors per call on this path
+constexpr int ECHS = 128;          // atoms per workgroup
+constexpr int ESB = 256;           // threads per workgroup
+constexpr int kSmallMaxG = 512;    // workgroups at 65,536 atoms
+
+struct SmallArgs {                 // one encode problem
+  const void* x;
+  const void* dict;
+  float* r;                        // [2][n][D]
+  int2* part;                      // [2][n][G]: (float bits of c, atom)
+  uint32_t* codes;
+  int64_t codes_ld;
+  float* coef_f32;
+  float* resid_norm;
+  uint32_t* low_plane;
+  int64_t low_ld;
+  int x_f32;
+  int klow;
+};
+
+struct SmallLaunch {               // up to two problems of one shape
+  SmallArgs p[2];
+  int n, N, K, G;
+};
+
+// (c, atom) pairs: larger |c| wins, then the lower atom
+__device__ __forceinline__ bool small_better(float c, int at, float bc, int ba) {
+  const float ac = fabsf(c), ab = fabsf(bc);
+  return ac > ab || (ac == ab && at < ba);
+}
+
+// r (fp32) as hi + mid + lo bf16 parts, exactly: each part is the bf16
+// rounding (v_cvt_pk_bf16_f32) of what the previous ones left, and the
+// remainder after two 8-bit parts fits the third.
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split3_bf16(const float (&v)[8], u32x4& hi, u32x4& mid, u32x4& lo) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const f32x2v x = {v[2 * e], v[2 * e + 1]};
+    const bf16x2v h = __builtin_convertvector(x, bf16x2v);
+    const f32x2v r1 = x - __builtin_convertvector(h, f32x2v);
+    const bf16x2v m = __builtin_convertvector(r1, bf16x2v);
+    const f32x2v r2 = r1 - __builtin_convertvector(m, f32x2v);
+    hi[e] = __builtin_bit_cast(uint32_t, h);
+    mid[e] = __builtin_bit_cast(uint32_t, m);
+    lo[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r2, bf16x2v));
+  }
+}
+
+// NV: vectors per call at most (16 or kSmallN); PPL: per-workgroup winners
+// per lane and vector at most (G <= 64 * PPL). Both size unrolled code, which
+// each launch fetches anew, so the common small cases get small kernels.
+template <int D, bool F32D, int NV, int PPL>
+__global__ __launch_bounds__(ESB) void k_small(SmallLaunch L, int step) {
+  static_assert(ECHS * 2 == ESB && ECHS == 32 * (ESB / 64), "atom tiles per wave");
+  static_assert(NV <= kSmallN && 64 * PPL <= kSmallMaxG, "launch limits");
+  constexpr int NW = ESB / 64;
+  constexpr int RP = D + 4;                       // LDS row pitch of the residuals
+  constexpr int RPT = NV * D / ESB;               // residual elements per thread, at most
+  constexpr int KS = D / 32;                      // MFMA k-steps over a row
+  __shared__ __attribute__((aligned(16))) float s_r[NV * RP];
+  __shared__ float s_c[F32D ? NV * ECHS : 1];
+  __shared__ float s_bc[NW * NV];
+  __shared__ int s_ba[NW * NV];
+  __shared__ float s_g[NV];
+  __shared__ int s_a[NV];
+  const SmallArgs a = blockIdx.y ? L.p[1] : L.p[0];
+  const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+  const int n = L.n, G = L.G, wg = blockIdx.x, nD = n * D;
+  const bool corr = step < L.K;
+
+  // --- independent loads first: atom rows, residual, winners ----------------
+  // bf16 dictionary: wave w owns atoms wg*ECHS + 32w .. +31 as two 16-atom
+  // MFMA B tiles (lane: atom l & 15, eight k values from 8 * (l >> 4)).
+  // fp32 dictionary: thread (atom tid % ECHS, half tid / ECHS) holds its row.
+  u32x4 bt[2][KS];
+  float4 frow[F32D ? D / 4 : 1];
+  if constexpr (!F32D) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int at = wg * ECHS + 32 * w + 16 * t + (l & 15);
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        bt[t][k] = u32x4{0u, 0u, 0u, 0u};
+        if (corr && at < L.N)
+          bt[t][k] = *(const u32x4*)((const uint16_t*)a.dict + (int64_t)at * D + 32 * k + 8 * (l >> 4));
+      }
+    }
+  } else {
+    const int at = wg * ECHS + tid % ECHS;
+    if (corr && at < L.N) {
+      const float4* dp = (const float4*)((const float*)a.dict + (int64_t)at * D);
+#pragma unroll
+      for (int q = 0; q < D / 4; ++q) frow[q] = dp[q];
+    }
+  }
+  float rr[RPT];
+  if (step == 0) {
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+      const int i = tid + j * ESB;
+      if (i < nD) rr[j] = a.x_f32 ? ((const float*)a.x)[i] : bf16_to_f32(((const uint16_t*)a.x)[i]);
+    }
+  } else {
+    const float* rp = a.r + (int64_t)((step - 1) & 1) * nD;
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+      const int i = tid + j * ESB;
+      if (i < nD) rr[j] = rp[i];
+    }
+    // winners of step - 1: wave w reduces vectors w, w + NW, ... two at a time
+    const int2* pp = a.part + (int64_t)((step - 1) & 1) * n * G;
+    for (int v = w; v < n; v += 2 * NW) {
+      int2 e[2][PPL];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int t = 0; t < PPL; ++t) {
+          const int vv = v + u * NW, q = l + 64 * t;
+          e[u][t] = (vv < n && q < G) ? pp[(int64_t)vv * G + q] : make_int2(0, 0x7FFFFFFF);
+        }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        float bc = __int_as_float(e[u][0].x);
+        int ba = e[u][0].y;
+#pragma unroll
+        for (int t = 1; t < PPL; ++t) {
+          const float c = __int_as_float(e[u][t].x);
+          if (small_better(c, e[u][t].y, bc, ba)) { bc = c; ba = e[u][t].y; }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+          const float c = __shfl_xor(bc, o, 64);
+          const int at = __shfl_xor(ba, o, 64);
+          if (small_better(c, at, bc, ba)) { bc = c; ba = at; }
+        }
+        const int vv = v + u * NW;
+        if (l == 0 && vv < n) { s_g[vv] = bc; s_a[vv] = ba; }
+      }
+    }
+  }
+  __syncthreads();
+
+  // --- r_step = r_{step-1} - g d_a, one fmaf per element ---------------------
+  if (step > 0) {
+    float dk[RPT];
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+      const int i = tid + j * ESB;
+      if (i < nD) {
+        const int64_t e = (int64_t)s_a[i / D] * D + i % D;
+        dk[j] = F32D ? ((const float*)a.dict)[e] : bf16_to_f32(((const uint16_t*)a.dict)[e]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+      const int i = tid + j * ESB;
+      if (i < nD) rr[j] = fmaf(-s_g[i / D], dk[j], rr[j]);
+    }
+    if (wg == 0) {
+      for (int v = tid; v < n; v += ESB) {
+        a.codes[(int64_t)v * a.codes_ld + step - 1] = (uint32_t)s_a[v] | (f32_to_f16_bits(s_g[v]) << 16);
+        if (a.coef_f32) a.coef_f32[(int64_t)v * L.K + step - 1] = s_g[v];
+      }
+    }
+  }
+  float* rq = a.r + (int64_t)(step & 1) * nD;
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) {
+    const int i = tid + j * ESB;
+    if (i < nD) {
+      s_r[(i / D) * RP + i % D] = rr[j];
+      if (wg == 0 && corr) rq[i] = rr[j];
+    }
+  }
+  __syncthreads();
+
+  if (corr) {
+    int2* pq = a.part + (int64_t)(step & 1) * n * G;
+    if constexpr (!F32D) {
+      // --- correlations on the matrix cores: C[vector][atom] over 16-vector
+      // tiles, r split exactly into three bf16 parts (every product exact,
+      // fp32 accumulation); per wave the best of its 32 atoms per vector ------
+      for (int v0 = 0; v0 < n; v0 += 16) {
+        f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        const int vr = v0 + (l & 15);
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+          float rv[8];
+          if (vr < n) {
+            const float4 p0 = *(const float4*)&s_r[vr * RP + 32 * k + 8 * (l >> 4)];
+            const float4 p1 = *(const float4*)&s_r[vr * RP + 32 * k + 8 * (l >> 4) + 4];
+            rv[0] = p0.x; rv[1] = p0.y; rv[2] = p0.z; rv[3] = p0.w;
+            rv[4] = p1.x; rv[5] = p1.y; rv[6] = p1.z; rv[7] = p1.w;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) rv[e] = 0.f;
+          }
+          u32x4 hi, mid, lo;
+          split3_bf16(rv, hi, mid, lo);
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            acc[t] = mfma_bf16(hi, bt[t][k], acc[t]);
+            acc[t] = mfma_bf16(mid, bt[t][k], acc[t]);
+            acc[t] = mfma_bf16(lo, bt[t][k], acc[t]);
+          }
+        }
+        // lane holds vectors v0 + 4 * (l >> 4) + i, atoms (tile t) 16t + (l & 15)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float bc = 0.f;
+          int ba = 0x7FFFFFFF;
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int at = wg * ECHS + 32 * w + 16 * t + (l & 15);
+            if (at < L.N && small_better(acc[t][i], at, bc, ba)) { bc = acc[t][i]; ba = at; }
+          }
+#pragma unroll
+          for (int o = 8; o > 0; o >>= 1) {
+            const float c = __shfl_xor(bc, o, 64);
+            const int at = __shfl_xor(ba, o, 64);
+            if (small_better(c, at, bc, ba)) { bc = c; ba = at; }
+          }
+          const int v = v0 + 4 * (l >> 4) + i;
+          if ((l & 15) == 0 && v < n) { s_bc[w * NV + v] = bc; s_ba[w * NV + v] = ba; }
+        }
+      }
+      __syncthreads();
+      // the workgroup's winner per vector: the best of the waves' winners
+      for (int v = tid; v < n; v += ESB) {
+        float bc = s_bc[v];
+        int ba = s_ba[v];
+#pragma unroll
+        for (int q = 1; q < NW; ++q)
+          if (small_better(s_bc[q * NV + v], s_ba[q * NV + v], bc, ba)) {
+            bc = s_bc[q * NV + v]; ba = s_ba[q * NV + v];
+          }
+        pq[(int64_t)v * G + wg] = make_int2(__float_as_int(bc), ba);
+      }
+    } else {
+      // --- correlations on the vector ALUs (fp32 dictionary): thread (atom,
+      // half) takes the vectors of its half, each a sequential fp32 dot
+      // product over k ---------------------------------------------------------
+      const int al = tid % ECHS, half = tid / ECHS;
+      const int atom = wg * ECHS + al;
+      const int nh = (n + 1) / 2;  // vectors [half * nh, min(n, half * nh + nh))
+      const int v0 = half * nh, v1 = min(n, v0 + nh);
+      if (atom < L.N) {
+#pragma unroll
+        for (int j = 0; j < NV / 2; ++j) {
+          if (v0 + j < v1) {
+            float sacc = 0.f;
+#pragma unroll
+            for (int q = 0; q < D / 4; ++q) {
+              const float4 r4 = *(const float4*)&s_r[(v0 + j) * RP + 4 * q];
+              sacc = fmaf(r4.x, frow[q].x, sacc); sacc = fmaf(r4.y, frow[q].y, sacc);
+              sacc = fmaf(r4.z, frow[q].z, sacc); sacc = fmaf(r4.w, frow[q].w, sacc);
+            }
+            s_c[(v0 + j) * ECHS + al] = sacc;
+          }
+        }
+      }
+      __syncthreads();
+      // per vector: the best of this workgroup's atoms (wave w: vectors w, w+NW, ...)
+      for (int v = w; v < n; v += NW) {
+        float bc = 0.f;
+        int ba = 0x7FFFFFFF;
+#pragma unroll
+        for (int t = 0; t < ECHS / 64; ++t) {
+          const int q = l + 64 * t, at = wg * ECHS + q;
+          if (at < L.N && small_better(s_c[v * ECHS + q], at, bc, ba)) { bc = s_c[v * ECHS + q]; ba = at; }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+          const float c = __shfl_xor(bc, o, 64);
+          const int at = __shfl_xor(ba, o, 64);
+          if (small_better(c, at, bc, ba)) { bc = c; ba = at; }
+        }
+        if (l == 0) pq[(int64_t)v * G + wg] = make_int2(__float_as_int(bc), ba);
+      }
+    }
+  } else if (wg == 0) {
+    // --- final outputs -----------------------------------------------------------
+    for (int v = w; v < n; v += NW) {
+      float s2 = 0.f;
+      for (int k = l; k < D; k += 64) s2 = fmaf(s_r[v * RP + k], s_r[v * RP + k], s2);
+      s2 = wave_sum(s2);
+      if (l == 0 && a.resid_norm) a.resid_norm[v] = sqrtf(s2);
+    }
+    // words of steps before K - 1 come from earlier launches; the last one
+    // from this workgroup's own reduction
+    if (a.low_plane)
+      for (int i = tid; i < n * a.klow; i += ESB) {
+        const int v = i / a.klow, j = i % a.klow;
+        a.low_plane[(int64_t)v * a.low_ld + j] =
+            j == L.K - 1 ? (uint32_t)s_a[v] | (f32_to_f16_bits(s_g[v]) << 16)
+                         : a.codes[(int64_t)v * a.codes_ld + j];
+      }
   }
 }
 
 sdkv_status plan_encode(const sdkv_encode_args* a, EncodePlan* p) {
   EncodePlan q;
   q.n = a->n;
+  if (a->n <= kSmallN) {
+    q.small = 1;
+    q.G = (a->n_atoms + ECHS - 1) / ECHS;
+    size_t off = 0;
+    q.off_r = off;     off = align_up(off + (size_t)2 * a->n * a->d * 4, 256);
+    q.off_part = off;  off = align_up(off + (size_t)2 * q.G * a->n * 8, 256);
+    q.total = off;
+    *p = q;
+    return SDKV_OK;
+  }
   q.npad = (a->n_atoms + ECH - 1) / ECH * ECH;
   q.rows_per_wg = EROWS;
   q.nwg = (a->n + EROWS - 1) / EROWS;
@@ -324,9 +653,83 @@ sdkv_status plan_encode(const sdkv_encode_args* a, EncodePlan* p) {
   return SDKV_OK;
 }
 
+static SmallArgs small_args(const sdkv_encode_args* a, const EncodePlan& p, char* base) {
+  SmallArgs s;
+  s.x = a->x;
+  s.dict = a->dict;
+  s.r = (float*)(base + p.off_r);
+  s.part = (int2*)(base + p.off_part);
+  s.codes = a->codes;
+  s.codes_ld = a->codes_ld ? a->codes_ld : a->K;
+  s.coef_f32 = a->coef_f32;
+  s.resid_norm = a->resid_norm;
+  s.low_plane = a->low_plane;
+  s.low_ld = a->low_ld ? a->low_ld : a->klow;
+  s.x_f32 = a->x_dtype == SDKV_F32;
+  s.klow = a->low_plane ? a->klow : 0;
+  return s;
+}
+
+template <int D, bool F32D>
+static void launch_small_kernel(bool few, bool narrow, dim3 grid, hipStream_t stream,
+                                const SmallLaunch& L, int step) {
+  if (few && narrow)  hipLaunchKernelGGL((k_small<D, F32D, 16, 4>), grid, dim3(ESB), 0, stream, L, step);
+  else if (few)       hipLaunchKernelGGL((k_small<D, F32D, 16, 8>), grid, dim3(ESB), 0, stream, L, step);
+  else if (narrow)    hipLaunchKernelGGL((k_small<D, F32D, kSmallN, 4>), grid, dim3(ESB), 0, stream, L, step);
+  else                hipLaunchKernelGGL((k_small<D, F32D, kSmallN, 8>), grid, dim3(ESB), 0, stream, L, step);
+}
+
+// The K + 1 launches of the small path for `count` (1 or 2) problems of one
+// shape (n, d, n_atoms, K and dictionary dtype equal).
+static sdkv_status launch_small(const sdkv_encode_args* const* a, const EncodePlan* const* p,
+                                char* const* base, int count, hipStream_t stream) {
+  SmallLaunch L;
+  for (int i = 0; i < 2; ++i) L.p[i] = small_args(a[i < count ? i : 0], *p[i < count ? i : 0], base[i < count ? i : 0]);
+  L.n = (int)a[0]->n;
+  L.N = a[0]->n_atoms;
+  L.K = a[0]->K;
+  L.G = p[0]->G;
+  const bool f32d = a[0]->dict_dtype == SDKV_F32;
+  const dim3 grid((unsigned)L.G, (unsigned)count);
+  const bool few = L.n <= 16, narrow = L.G <= 256;
+  for (int step = 0; step <= L.K; ++step) {
+    if (a[0]->d == 128) {
+      if (f32d) launch_small_kernel<128, true>(few, narrow, grid, stream, L, step);
+      else      launch_small_kernel<128, false>(few, narrow, grid, stream, L, step);
+    } else {
+      if (f32d) launch_small_kernel<64, true>(few, narrow, grid, stream, L, step);
+      else      launch_small_kernel<64, false>(few, narrow, grid, stream, L, step);
+    }
+    if (hipGetLastError() != hipSuccess) return SDKV_ERR_DEVICE;
+  }
+  return SDKV_OK;
+}
+
+sdkv_status launch_encode_pair(const sdkv_encode_args* a0, const EncodePlan& p0, char* ws0,
+                               const sdkv_encode_args* a1, const EncodePlan& p1, char* ws1,
+                               hipStream_t stream) {
+  const sdkv_encode_args* a[2] = {a0, a1};
+  const EncodePlan* p[2] = {&p0, &p1};
+  char* base[2] = {ws0, ws1};
+  return launch_small(a, p, base, 2, stream);
+}
+
 sdkv_status launch_encode(const sdkv_encode_args* a, const EncodePlan& p, void* ws,
                           hipStream_t stream) {
   char* base = (char*)ws;
+  const int64_t codes_ld = a->codes_ld ? a->codes_ld : a->K;
+  const int64_t low_ld = a->low_ld ? a->low_ld : a->klow;
+  if (p.small) {
+    void* const* ev = a->stage_events;
+    if (!record_stage(ev, 0, stream) || !record_stage(ev, 1, stream)) return SDKV_ERR_DEVICE;
+    const sdkv_encode_args* aa[1] = {a};
+    const EncodePlan* pp[1] = {&p};
+    char* bb[1] = {base};
+    const sdkv_status st = launch_small(aa, pp, bb, 1, stream);
+    if (st != SDKV_OK) return st;
+    if (!record_stage(ev, 2, stream)) return SDKV_ERR_DEVICE;
+    return SDKV_OK;
+  }
   uint16_t* dh = (uint16_t*)(base + p.off_dh);
   const int dict_f32 = a->dict_dtype == SDKV_F32;
   void* const* ev = a->stage_events;
@@ -351,9 +754,11 @@ sdkv_status launch_encode(const sdkv_encode_args* a, const EncodePlan& p, void* 
   e.K = a->K;
   e.klow = a->low_plane ? a->klow : 0;
   e.codes = a->codes;
+  e.codes_ld = codes_ld;
   e.coef_f32 = a->coef_f32;
   e.resid_norm = a->resid_norm;
   e.low_plane = a->low_plane;
+  e.low_ld = low_ld;
   const int64_t max_grid = 0x7FFFFFFF;
   if (p.nwg > max_grid) return SDKV_ERR_UNSUPPORTED;
   if (!record_stage(ev, 1, stream)) return SDKV_ERR_DEVICE;

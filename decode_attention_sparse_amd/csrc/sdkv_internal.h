@@ -68,9 +68,16 @@ struct EncodePlan {
   int rows_per_wg = 0;
   int64_t nwg = 0;
   size_t off_dh = 0, off_r = 0, off_rh = 0, off_scale = 0;
+  int small = 0;         // n <= 64: exact pursuit spread over the device
+  int G = 0;             // small path: workgroups (atom slices)
+  size_t off_part = 0;   // small path: per-workgroup winners [2][G][n]
   size_t total = 0;
 };
 sdkv_status plan_encode(const sdkv_encode_args* a, EncodePlan* p);
+// Both problems on the small path, same n, d, n_atoms, K and dictionary dtype.
+sdkv_status launch_encode_pair(const sdkv_encode_args* a0, const EncodePlan& p0, char* ws0,
+                               const sdkv_encode_args* a1, const EncodePlan& p1, char* ws1,
+                               hipStream_t stream);
 sdkv_status launch_encode(const sdkv_encode_args* a, const EncodePlan& p, void* ws,
                           hipStream_t stream);
 

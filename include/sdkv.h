@@ -45,7 +45,7 @@ extern "C" {
 #define SDKV_API
 #endif
 
-#define SDKV_ABI_VERSION 2
+#define SDKV_ABI_VERSION 3
 
 typedef int32_t sdkv_status;
 #define SDKV_OK 0
@@ -67,9 +67,12 @@ typedef int32_t sdkv_status;
  *     r = x;  for k < K:  a_k = argmax_a |<r, d_a>|  (lowest a on ties),
  *                          g_k = <r, d_{a_k}>,  r -= g_k d_{a_k}.
  * Atoms are expected to have unit norm (the coefficient is not divided by
- * |d|^2). The argmax is found with an fp16 matrix-core screen of all atoms
- * followed by an exact fp32 re-check of the best candidates; g_k and the
- * residual are fp32.
+ * |d|^2). g_k and the residual are fp32. For n > 64 vectors the argmax is
+ * found with an fp16 matrix-core screen of all atoms followed by an exact
+ * fp32 re-check of the best candidates. For n <= 64 (a decode step's new
+ * tokens, which the cache appends as codes: review page, Strengths, on
+ * write endurance) every correlation is computed exactly in fp32, with the
+ * atoms spread over the whole device; that path takes K + 1 launches.
  * ---------------------------------------------------------------------- */
 typedef struct sdkv_encode_args {
   const void* x;        /* [n, d] vectors, dtype x_dtype (SDKV_BF16/F32)  */
@@ -80,10 +83,17 @@ typedef struct sdkv_encode_args {
   int32_t d;            /* 64 or 128                                      */
   int32_t n_atoms;      /* 1 .. 65536                                     */
   int32_t K;            /* code length, 1 .. 32                           */
-  uint32_t* codes;      /* OUT [n, K] code words, pursuit order; required */
+  uint32_t* codes;      /* OUT code words of vector i at codes[i * codes_ld
+                           + k], k < K, pursuit order; required           */
+  int64_t codes_ld;     /* words between vectors' code rows: 0 means K,
+                           else >= K. Pointing `codes` at slot t of a
+                           [rows, T, stride] cache with codes_ld = T *
+                           stride appends one token per row in place.     */
   float* coef_f32;      /* OUT [n, K] unrounded g_k, or NULL              */
   float* resid_norm;    /* OUT [n] |r_K|_2, or NULL                       */
-  uint32_t* low_plane;  /* OUT [n, klow] first klow code words, or NULL   */
+  uint32_t* low_plane;  /* OUT first klow code words of vector i at
+                           low_plane[i * low_ld + j], or NULL             */
+  int64_t low_ld;       /* 0 means klow, else >= klow                     */
   int32_t klow;         /* 1 .. K when low_plane != NULL                  */
   /* Optional stage timing: NULL, or SDKV_ENCODE_STAGES + 1 hipEvent_t
      handles (created by the caller); event i is recorded on `stream` before
@@ -97,6 +107,20 @@ typedef struct sdkv_encode_args {
 SDKV_API sdkv_status sdkv_encode_workspace(const sdkv_encode_args* args, size_t* bytes);
 SDKV_API sdkv_status sdkv_encode(const sdkv_encode_args* args, void* ws, size_t ws_bytes,
                         void* stream);
+
+/* Two small encodes in one sequence of K + 1 launches: a decode step's new
+ * key vectors over the key dictionary and its value vectors over the value
+ * dictionary (review page, Strengths, on write endurance: a new token is
+ * appended as codes). Each side gets the codes, coefficients, norms and low
+ * plane that sdkv_encode gives it alone, bit for bit. Both must take the
+ * small path (n <= 64) and agree in n, d, n_atoms, K and dict_dtype, else
+ * SDKV_ERR_UNSUPPORTED (n > 64) or SDKV_ERR_SHAPE; stage_events are not
+ * recorded. The workspace holds both sides' scratch; outputs must not
+ * overlap the inputs or each other. */
+SDKV_API sdkv_status sdkv_encode_pair_workspace(const sdkv_encode_args* key,
+                                                const sdkv_encode_args* val, size_t* bytes);
+SDKV_API sdkv_status sdkv_encode_pair(const sdkv_encode_args* key, const sdkv_encode_args* val,
+                                      void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Decode attention for one layer and one decode step (review page, Summary:

@@ -20,10 +20,10 @@ def declared_symbols():
 def test_library_exports_every_declared_symbol():
     lib = sd.lib()
     names = declared_symbols()
-    assert len(names) == 9, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.sdkv_abi_version() == 2
+    assert lib.sdkv_abi_version() == 3
 
 
 def test_status_strings():
@@ -120,6 +120,7 @@ def good_enc(**kw):
     ("n", 0, sd.SDKV_ERR_SHAPE), ("n_atoms", 65537, sd.SDKV_ERR_SHAPE),
     ("K", 0, sd.SDKV_ERR_SHAPE), ("K", 33, sd.SDKV_ERR_SHAPE),
     ("x_dtype", 5, sd.SDKV_ERR_DTYPE),
+    ("codes_ld", 15, sd.SDKV_ERR_SHAPE), ("codes_ld", -1, sd.SDKV_ERR_SHAPE),
 ])
 def test_encode_validation(field, value, status):
     a = good_enc(**{field: value})
@@ -149,3 +150,51 @@ def test_topk_validation():
     assert lib.sdkv_select_topk(V(FAKE), 4, 1000, 999, 10, V(FAKE), None, V(FAKE), 1 << 30, None) == sd.SDKV_ERR_SHAPE
     assert lib.sdkv_select_topk(V(FAKE), 4, 1000, 1000, 10, V(FAKE), None, None, 1 << 30, None) == sd.SDKV_ERR_NULL
     assert lib.sdkv_select_topk(V(FAKE), 4, 1000, 1000, 10, V(FAKE), None, V(FAKE), 0, None) == sd.SDKV_ERR_WORKSPACE
+
+
+def test_encode_strides_and_small_plan():
+    nb = ctypes.c_size_t(0)
+    lib = sd.lib()
+    # a low-plane stride below klow is rejected; row strides >= the row are accepted
+    a = good_enc(low_plane=FAKE, klow=3, low_ld=2)
+    assert lib.sdkv_encode_workspace(ctypes.byref(a), ctypes.byref(nb)) == sd.SDKV_ERR_SHAPE
+    a = good_enc(low_plane=FAKE, klow=3, low_ld=96, codes_ld=32 * 131072)
+    assert lib.sdkv_encode_workspace(ctypes.byref(a), ctypes.byref(nb)) == 0
+    # up to 64 vectors take the small path: two residual buffers plus two
+    # winner tables of (n_atoms / 128) x n pairs, no dictionary copy
+    for n in (1, 16, 64):
+        a = good_enc(n=n)
+        assert lib.sdkv_encode_workspace(ctypes.byref(a), ctypes.byref(nb)) == 0
+        want = -(-2 * n * 128 * 4 // 256) * 256 + -(-2 * 256 * n * 8 // 256) * 256
+        assert nb.value == want, (n, nb.value, want)
+    a = good_enc(n=65)
+    assert lib.sdkv_encode_workspace(ctypes.byref(a), ctypes.byref(nb)) == 0
+    assert nb.value > 32768 * 128 * 2  # batch path: fp16 dictionary copy
+
+
+def test_encode_pair_validation():
+    lib = sd.lib()
+    nb = ctypes.c_size_t(0)
+    k, v = good_enc(n=8), good_enc(n=8)
+    assert lib.sdkv_encode_pair_workspace(ctypes.byref(k), ctypes.byref(v), ctypes.byref(nb)) == 0
+    one = ctypes.c_size_t(0)
+    assert lib.sdkv_encode_workspace(ctypes.byref(k), ctypes.byref(one)) == 0
+    assert nb.value == 2 * one.value  # both sides' scratch, each 256-byte aligned
+    for field, value, status in (("n", 9, sd.SDKV_ERR_SHAPE), ("K", 8, sd.SDKV_ERR_SHAPE),
+                                 ("n_atoms", 4096, sd.SDKV_ERR_SHAPE), ("d", 64, sd.SDKV_ERR_SHAPE),
+                                 ("dict_dtype", sd.SDKV_F32, sd.SDKV_ERR_SHAPE),
+                                 ("codes", None, sd.SDKV_ERR_NULL)):
+        v2 = good_enc(n=8)
+        setattr(v2, field, value)
+        assert lib.sdkv_encode_pair_workspace(ctypes.byref(k), ctypes.byref(v2), ctypes.byref(nb)) == status
+        assert lib.sdkv_encode_pair(ctypes.byref(k), ctypes.byref(v2), ctypes.c_void_p(FAKE), 1 << 30,
+                                    None) == status
+    big_k, big_v = good_enc(n=65), good_enc(n=65)
+    assert lib.sdkv_encode_pair_workspace(ctypes.byref(big_k), ctypes.byref(big_v),
+                                          ctypes.byref(nb)) == sd.SDKV_ERR_UNSUPPORTED
+    k.x_dtype = sd.SDKV_F32  # input dtypes may differ
+    assert lib.sdkv_encode_pair_workspace(ctypes.byref(k), ctypes.byref(v), ctypes.byref(nb)) == 0
+    assert lib.sdkv_encode_pair(ctypes.byref(k), ctypes.byref(v), None, 1 << 30, None) == sd.SDKV_ERR_NULL
+    assert lib.sdkv_encode_pair(ctypes.byref(k), ctypes.byref(v), ctypes.c_void_p(FAKE), nb.value - 1,
+                                None) == sd.SDKV_ERR_WORKSPACE
+    assert lib.sdkv_encode_pair_workspace(ctypes.byref(k), ctypes.byref(v), None) == sd.SDKV_ERR_NULL
