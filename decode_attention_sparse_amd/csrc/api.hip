@@ -53,6 +53,7 @@ sdkv_status coresident_blocks(const void* kernel, int threads, size_t dyn_lds, i
 }  // namespace sdkv
 
 static bool valid_dtype(int32_t t) { return t == SDKV_BF16 || t == SDKV_F32; }
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 static sdkv_status check_encode(const sdkv_encode_args* a) {
   if (!a || !a->x || !a->dict || !a->codes) return SDKV_ERR_NULL;
@@ -66,6 +67,7 @@ static sdkv_status check_encode(const sdkv_encode_args* a) {
   if (a->low_plane && a->low_ld != 0 && (a->low_ld < a->klow || a->low_ld > ((int64_t)1 << 40)))
     return SDKV_ERR_SHAPE;
   if (a->n > ((int64_t)1 << 40)) return SDKV_ERR_UNSUPPORTED;
+  if (!aligned16(a->x) || !aligned16(a->dict)) return SDKV_ERR_UNSUPPORTED;
   return SDKV_OK;
 }
 
@@ -85,6 +87,7 @@ static sdkv_status check_attn(const sdkv_attn_args* a) {
   if (a->q_dtype != SDKV_BF16) return SDKV_ERR_UNSUPPORTED;
   if (a->n_atoms > kMaxAtomsDecode) return SDKV_ERR_UNSUPPORTED;
   if ((int64_t)a->B * a->Hq > 0x7FFFFFFF / 64) return SDKV_ERR_UNSUPPORTED;
+  if (!aligned16(a->q) || !aligned16(a->dk) || !aligned16(a->dv)) return SDKV_ERR_UNSUPPORTED;
   return SDKV_OK;
 }
 
@@ -135,6 +138,7 @@ sdkv_status sdkv_encode(const sdkv_encode_args* args, void* ws, size_t ws_bytes,
     if (s != SDKV_OK) return s;
     if (p.total > 0 && !ws) return SDKV_ERR_NULL;
     if (ws_bytes < p.total) return SDKV_ERR_WORKSPACE;
+    if (!aligned16(ws)) return SDKV_ERR_UNSUPPORTED;
     return launch_encode(args, p, ws, (hipStream_t)stream);
   } catch (...) {
     return SDKV_ERR_DEVICE;
@@ -181,6 +185,7 @@ sdkv_status sdkv_encode_pair(const sdkv_encode_args* a0, const sdkv_encode_args*
     if (s != SDKV_OK) return s;
     if (!ws) return SDKV_ERR_NULL;
     if (ws_bytes < total) return SDKV_ERR_WORKSPACE;
+    if (!aligned16(ws)) return SDKV_ERR_UNSUPPORTED;
     return launch_encode_pair(a0, p0, (char*)ws, a1, p1, (char*)ws + off1, (hipStream_t)stream);
   } catch (...) {
     return SDKV_ERR_DEVICE;
@@ -211,6 +216,7 @@ sdkv_status sdkv_decode_attn(const sdkv_attn_args* args, void* ws, size_t ws_byt
     if (s != SDKV_OK) return s;
     if (!ws) return SDKV_ERR_NULL;
     if (ws_bytes < p.total) return SDKV_ERR_WORKSPACE;
+    if (!aligned16(ws)) return SDKV_ERR_UNSUPPORTED;
     return launch_decode(args, p, ws, (hipStream_t)stream);
   } catch (...) {
     return SDKV_ERR_DEVICE;
@@ -244,6 +250,7 @@ sdkv_status sdkv_select_topk(const float* scores, int64_t rows, int64_t n, int64
     if (s != SDKV_OK) return s;
     if (!ws) return SDKV_ERR_NULL;
     if (ws_bytes < p.total) return SDKV_ERR_WORKSPACE;
+    if (!aligned16(ws)) return SDKV_ERR_UNSUPPORTED;
     return launch_topk(scores, ld, idx_out, thr_out, p, ws, (hipStream_t)stream);
   } catch (...) {
     return SDKV_ERR_DEVICE;

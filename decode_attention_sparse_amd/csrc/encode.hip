@@ -314,18 +314,24 @@ __global__ __launch_bounds__(EB) void k_encode(EncArgs a) {
 
 // ---------------------------------------------------------------------------
 // Few vectors (n <= kSmallN, e.g. one decode step's new tokens): the same
-// pursuit with every correlation exact in fp32 and the atoms spread over the
-// device, one launch per step. Launch `step` (0 .. K) of k_small, for the
-// problem blockIdx.y (a key and a value encode can share the launches):
-//   * loads, all at once: its atom row, r_{step-1} (x at step 0) and the
+// pursuit with the atoms spread over the device, one launch per step.
+// Launch `step` (0 .. K) of k_small, for the problem blockIdx.y (a key and a
+// value encode can share the launches):
+//   * loads, all at once: its atom rows, r_{step-1} (x at step 0) and the
 //     per-workgroup winners of step - 1;
-//   * every workgroup reduces the same winners (largest |c|, lowest atom on
-//     ties), so all agree on (g, a), and forms r_step = r_{step-1} - g d_a;
-//     workgroup 0 stores r_step and the code word of step - 1;
+//   * every workgroup reduces the same winners, so all agree on (g, a), and
+//     forms r_step = r_{step-1} - g d_a; workgroup 0 stores r_step and the
+//     code word of step - 1;
 //   * step < K: correlates r_step with its ECHS atoms and stores its
-//     per-vector winner (c, atom);
+//     per-vector winner;
 //   * step == K: workgroup 0 writes the residual norms and the low plane.
-// Residuals and winners alternate between two buffers by step parity.
+// Residuals and winners alternate between two buffers by step parity. A
+// winner is one 64-bit key, so every reduction is a plain maximum: |c| (fp32
+// bits) above 0xFFFF - atom above the sign of c -- the larger |c| wins, then
+// the lower atom, and c is recovered exactly.
+// Each launch fetches its code anew, so the kernels keep their unrolled code
+// small: NV (16 or kSmallN) bounds the vectors and PPL the winners per lane
+// (G <= 64 * PPL) that a kernel is built for.
 // ---------------------------------------------------------------------------
 constexpr int kSmallN = 64;        // vectors per call on this path
 constexpr int ECHS = 128;          // atoms per workgroup
@@ -336,7 +342,7 @@ struct SmallArgs {                 // one encode problem
   const void* x;
   const void* dict;
   float* r;                        // [2][n][D]
-  int2* part;                      // [2][n][G]: (float bits of c, atom)
+  uint64_t* part;                  // [2][n][G] winner keys
   uint32_t* codes;
   int64_t codes_ld;
   float* coef_f32;
@@ -352,11 +358,15 @@ struct SmallLaunch {               // up to two problems of one shape
   int n, N, K, G;
 };
 
-// (c, atom) pairs: larger |c| wins, then the lower atom
-__device__ __forceinline__ bool small_better(float c, int at, float bc, int ba) {
-  const float ac = fabsf(c), ab = fabsf(bc);
-  return ac > ab || (ac == ab && at < ba);
+__device__ __forceinline__ uint64_t win_key(float c, int atom) {
+  const uint32_t u = __float_as_uint(c);
+  return ((uint64_t)(u & 0x7FFFFFFFu) << 32) | ((uint32_t)(0xFFFF - atom) << 16) | (u >> 31);
 }
+__device__ __forceinline__ float key_coef(uint64_t k) {
+  return __uint_as_float((uint32_t)(k >> 32) | ((uint32_t)k << 31));
+}
+__device__ __forceinline__ int key_atom(uint64_t k) { return 0xFFFF - (int)(((uint32_t)k >> 16) & 0xFFFFu); }
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
 // r (fp32) as hi + mid + lo bf16 parts, exactly: each part is the bf16
 // rounding (v_cvt_pk_bf16_f32) of what the previous ones left, and the
@@ -377,245 +387,235 @@ __device__ __forceinline__ void split3_bf16(const float (&v)[8], u32x4& hi, u32x
   }
 }
 
-// NV: vectors per call at most (16 or kSmallN); PPL: per-workgroup winners
-// per lane and vector at most (G <= 64 * PPL). Both size unrolled code, which
-// each launch fetches anew, so the common small cases get small kernels.
+__device__ __forceinline__ void split3_bf16x4(float4 v, uint2& hi, uint2& mid, uint2& lo) {
+  const float a[8] = {v.x, v.y, v.z, v.w, 0.f, 0.f, 0.f, 0.f};
+  u32x4 h, m, o;
+  split3_bf16(a, h, m, o);
+  hi = make_uint2(h[0], h[1]);
+  mid = make_uint2(m[0], m[1]);
+  lo = make_uint2(o[0], o[1]);
+}
+
 template <int D, bool F32D, int NV, int PPL>
 __global__ __launch_bounds__(ESB) void k_small(SmallLaunch L, int step) {
   static_assert(ECHS * 2 == ESB && ECHS == 32 * (ESB / 64), "atom tiles per wave");
-  static_assert(NV <= kSmallN && 64 * PPL <= kSmallMaxG, "launch limits");
+  static_assert(NV <= kSmallN && NV % 16 == 0 && 64 * PPL <= kSmallMaxG, "launch limits");
   constexpr int NW = ESB / 64;
   constexpr int RP = D + 4;                       // LDS row pitch of the residuals
-  constexpr int RPT = NV * D / ESB;               // residual elements per thread, at most
+  constexpr int NQ = NV * D / (4 * ESB);          // residual float4 groups per thread, at most
   constexpr int KS = D / 32;                      // MFMA k-steps over a row
-  __shared__ __attribute__((aligned(16))) float s_r[NV * RP];
+  constexpr int RPB = D + 8;                      // pitch of the bf16 parts (elements)
+  // fp32 dictionary: r_step in fp32; bf16 dictionary: its three bf16 parts
+  __shared__ __attribute__((aligned(16))) float s_r[F32D ? NV * RP : 4];
+  __shared__ __attribute__((aligned(16))) uint16_t s_p[F32D ? 8 : 3 * NV * RPB];
   __shared__ float s_c[F32D ? NV * ECHS : 1];
-  __shared__ float s_bc[NW * NV];
-  __shared__ int s_ba[NW * NV];
+  __shared__ uint64_t s_key[NW * NV];
   __shared__ float s_g[NV];
   __shared__ int s_a[NV];
   const SmallArgs a = blockIdx.y ? L.p[1] : L.p[0];
   const int tid = threadIdx.x, w = wave_id(), l = lane_id();
-  const int n = L.n, G = L.G, wg = blockIdx.x, nD = n * D;
+  const int n = L.n, G = L.G, wg = blockIdx.x, nq = n * D / 4;
   const bool corr = step < L.K;
 
   // --- independent loads first: atom rows, residual, winners ----------------
   // bf16 dictionary: wave w owns atoms wg*ECHS + 32w .. +31 as two 16-atom
   // MFMA B tiles (lane: atom l & 15, eight k values from 8 * (l >> 4)).
   // fp32 dictionary: thread (atom tid % ECHS, half tid / ECHS) holds its row.
+  // Indices past the end are clamped; what they load is never used.
   u32x4 bt[2][KS];
   float4 frow[F32D ? D / 4 : 1];
-  if constexpr (!F32D) {
+  if (corr) {
+    if constexpr (!F32D) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int at = wg * ECHS + 32 * w + 16 * t + (l & 15);
+      for (int t = 0; t < 2; ++t) {
+        const int at = min(wg * ECHS + 32 * w + 16 * t + (l & 15), L.N - 1);
 #pragma unroll
-      for (int k = 0; k < KS; ++k) {
-        bt[t][k] = u32x4{0u, 0u, 0u, 0u};
-        if (corr && at < L.N)
+        for (int k = 0; k < KS; ++k)
           bt[t][k] = *(const u32x4*)((const uint16_t*)a.dict + (int64_t)at * D + 32 * k + 8 * (l >> 4));
       }
-    }
-  } else {
-    const int at = wg * ECHS + tid % ECHS;
-    if (corr && at < L.N) {
+    } else {
+      const int at = min(wg * ECHS + tid % ECHS, L.N - 1);
       const float4* dp = (const float4*)((const float*)a.dict + (int64_t)at * D);
 #pragma unroll
       for (int q = 0; q < D / 4; ++q) frow[q] = dp[q];
     }
   }
-  float rr[RPT];
+  // residual: thread owns float4 groups tid + j * ESB (elements 4g .. 4g+3)
+  float4 rr[NQ];
   if (step == 0) {
+    if (a.x_f32) {
 #pragma unroll
-    for (int j = 0; j < RPT; ++j) {
-      const int i = tid + j * ESB;
-      if (i < nD) rr[j] = a.x_f32 ? ((const float*)a.x)[i] : bf16_to_f32(((const uint16_t*)a.x)[i]);
+      for (int j = 0; j < NQ; ++j) rr[j] = ((const float4*)a.x)[min(tid + j * ESB, nq - 1)];
+    } else {
+#pragma unroll
+      for (int j = 0; j < NQ; ++j) {
+        const uint2 u = ((const uint2*)a.x)[min(tid + j * ESB, nq - 1)];
+        rr[j] = make_float4(bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y));
+      }
     }
   } else {
-    const float* rp = a.r + (int64_t)((step - 1) & 1) * nD;
+    const float4* rp = (const float4*)(a.r + (int64_t)((step - 1) & 1) * n * D);
 #pragma unroll
-    for (int j = 0; j < RPT; ++j) {
-      const int i = tid + j * ESB;
-      if (i < nD) rr[j] = rp[i];
-    }
-    // winners of step - 1: wave w reduces vectors w, w + NW, ... two at a time
-    const int2* pp = a.part + (int64_t)((step - 1) & 1) * n * G;
-    for (int v = w; v < n; v += 2 * NW) {
-      int2 e[2][PPL];
+    for (int j = 0; j < NQ; ++j) rr[j] = rp[min(tid + j * ESB, nq - 1)];
+    // winners of step - 1: a row of 16 lanes per vector, each lane the
+    // maximum over every 16th workgroup, then over the row
+    const uint64_t* pp = a.part + (int64_t)((step - 1) & 1) * n * G;
+    for (int vb = 0; vb < n; vb += ESB / 16) {
+      const int v = vb + (tid >> 4);
+      const uint64_t* pv = pp + (int64_t)min(v, n - 1) * G;
+      uint64_t e[4 * PPL];
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int t = 0; t < 4 * PPL; ++t) e[t] = pv[min((tid & 15) + 16 * t, G - 1)];
+      uint64_t k = e[0];
 #pragma unroll
-        for (int t = 0; t < PPL; ++t) {
-          const int vv = v + u * NW, q = l + 64 * t;
-          e[u][t] = (vv < n && q < G) ? pp[(int64_t)vv * G + q] : make_int2(0, 0x7FFFFFFF);
-        }
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        float bc = __int_as_float(e[u][0].x);
-        int ba = e[u][0].y;
-#pragma unroll
-        for (int t = 1; t < PPL; ++t) {
-          const float c = __int_as_float(e[u][t].x);
-          if (small_better(c, e[u][t].y, bc, ba)) { bc = c; ba = e[u][t].y; }
-        }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-          const float c = __shfl_xor(bc, o, 64);
-          const int at = __shfl_xor(ba, o, 64);
-          if (small_better(c, at, bc, ba)) { bc = c; ba = at; }
-        }
-        const int vv = v + u * NW;
-        if (l == 0 && vv < n) { s_g[vv] = bc; s_a[vv] = ba; }
-      }
+      for (int t = 1; t < 4 * PPL; ++t) k = max_u64(k, e[t]);
+      k = row_max_u64(k);
+      if ((tid & 15) == 0 && v < n) { s_g[v] = key_coef(k); s_a[v] = key_atom(k); }
     }
   }
   __syncthreads();
 
   // --- r_step = r_{step-1} - g d_a, one fmaf per element ---------------------
   if (step > 0) {
-    float dk[RPT];
+    float4 dk[NQ];
 #pragma unroll
-    for (int j = 0; j < RPT; ++j) {
-      const int i = tid + j * ESB;
-      if (i < nD) {
-        const int64_t e = (int64_t)s_a[i / D] * D + i % D;
-        dk[j] = F32D ? ((const float*)a.dict)[e] : bf16_to_f32(((const uint16_t*)a.dict)[e]);
+    for (int j = 0; j < NQ; ++j) {
+      const int i = 4 * min(tid + j * ESB, nq - 1);
+      const int64_t e = (int64_t)s_a[i / D] * D + i % D;
+      if constexpr (F32D) {
+        dk[j] = *(const float4*)((const float*)a.dict + e);
+      } else {
+        const uint2 u = *(const uint2*)((const uint16_t*)a.dict + e);
+        dk[j] = make_float4(bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y));
       }
     }
 #pragma unroll
-    for (int j = 0; j < RPT; ++j) {
-      const int i = tid + j * ESB;
-      if (i < nD) rr[j] = fmaf(-s_g[i / D], dk[j], rr[j]);
+    for (int j = 0; j < NQ; ++j) {
+      const int i = 4 * min(tid + j * ESB, nq - 1);
+      const float g = s_g[i / D];
+      rr[j].x = fmaf(-g, dk[j].x, rr[j].x); rr[j].y = fmaf(-g, dk[j].y, rr[j].y);
+      rr[j].z = fmaf(-g, dk[j].z, rr[j].z); rr[j].w = fmaf(-g, dk[j].w, rr[j].w);
     }
-    if (wg == 0) {
-      for (int v = tid; v < n; v += ESB) {
-        a.codes[(int64_t)v * a.codes_ld + step - 1] = (uint32_t)s_a[v] | (f32_to_f16_bits(s_g[v]) << 16);
-        if (a.coef_f32) a.coef_f32[(int64_t)v * L.K + step - 1] = s_g[v];
-      }
+    if (wg == 0 && tid < n) {
+      a.codes[(int64_t)tid * a.codes_ld + step - 1] = (uint32_t)s_a[tid] | (f32_to_f16_bits(s_g[tid]) << 16);
+      if (a.coef_f32) a.coef_f32[(int64_t)tid * L.K + step - 1] = s_g[tid];
     }
   }
-  float* rq = a.r + (int64_t)(step & 1) * nD;
+  float4* rq = (float4*)(a.r + (int64_t)(step & 1) * n * D);
 #pragma unroll
-  for (int j = 0; j < RPT; ++j) {
-    const int i = tid + j * ESB;
-    if (i < nD) {
-      s_r[(i / D) * RP + i % D] = rr[j];
-      if (wg == 0 && corr) rq[i] = rr[j];
+  for (int j = 0; j < NQ; ++j) {
+    const int gq = tid + j * ESB;
+    if (gq < nq) {
+      const int v = 4 * gq / D, kk = (4 * gq) % D;
+      if constexpr (F32D) {
+        *(float4*)&s_r[v * RP + kk] = rr[j];
+      } else {
+        uint2 hi, mid, lo;
+        split3_bf16x4(rr[j], hi, mid, lo);
+        *(uint2*)&s_p[v * RPB + kk] = hi;
+        *(uint2*)&s_p[(NV + v) * RPB + kk] = mid;
+        *(uint2*)&s_p[(2 * NV + v) * RPB + kk] = lo;
+      }
+      if (wg == 0 && corr) rq[gq] = rr[j];
     }
   }
   __syncthreads();
 
   if (corr) {
-    int2* pq = a.part + (int64_t)(step & 1) * n * G;
+    uint64_t* pq = a.part + (int64_t)(step & 1) * n * G;
     if constexpr (!F32D) {
-      // --- correlations on the matrix cores: C[vector][atom] over 16-vector
+      // --- correlations on the matrix cores: C[atom][vector] over 16-vector
       // tiles, r split exactly into three bf16 parts (every product exact,
       // fp32 accumulation); per wave the best of its 32 atoms per vector ------
       for (int v0 = 0; v0 < n; v0 += 16) {
         f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-        const int vr = v0 + (l & 15);
+        const int vr = min(v0 + (l & 15), n - 1);  // columns past n are never stored
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
-          float rv[8];
-          if (vr < n) {
-            const float4 p0 = *(const float4*)&s_r[vr * RP + 32 * k + 8 * (l >> 4)];
-            const float4 p1 = *(const float4*)&s_r[vr * RP + 32 * k + 8 * (l >> 4) + 4];
-            rv[0] = p0.x; rv[1] = p0.y; rv[2] = p0.z; rv[3] = p0.w;
-            rv[4] = p1.x; rv[5] = p1.y; rv[6] = p1.z; rv[7] = p1.w;
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) rv[e] = 0.f;
-          }
-          u32x4 hi, mid, lo;
-          split3_bf16(rv, hi, mid, lo);
+          const int off = vr * RPB + 32 * k + 8 * (l >> 4);
+          const u32x4 hi = *(const u32x4*)&s_p[off];
+          const u32x4 mid = *(const u32x4*)&s_p[NV * RPB + off];
+          const u32x4 lo = *(const u32x4*)&s_p[2 * NV * RPB + off];
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
-            acc[t] = mfma_bf16(hi, bt[t][k], acc[t]);
-            acc[t] = mfma_bf16(mid, bt[t][k], acc[t]);
-            acc[t] = mfma_bf16(lo, bt[t][k], acc[t]);
+            acc[t] = mfma_bf16(bt[t][k], hi, acc[t]);
+            acc[t] = mfma_bf16(bt[t][k], mid, acc[t]);
+            acc[t] = mfma_bf16(bt[t][k], lo, acc[t]);
           }
         }
-        // lane holds vectors v0 + 4 * (l >> 4) + i, atoms (tile t) 16t + (l & 15)
+        // lane holds vector v0 + (l & 15) against atoms 16t + 4 * (l >> 4) + i;
+        // the four lanes of a vector (l ^ 16, l ^ 32) then combine
+        uint64_t k = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float bc = 0.f;
-          int ba = 0x7FFFFFFF;
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const int at = wg * ECHS + 32 * w + 16 * t + (l & 15);
-            if (at < L.N && small_better(acc[t][i], at, bc, ba)) { bc = acc[t][i]; ba = at; }
+          for (int i = 0; i < 4; ++i) {
+            const int at = wg * ECHS + 32 * w + 16 * t + 4 * (l >> 4) + i;
+            if (at < L.N) k = max_u64(k, win_key(acc[t][i], at));
           }
 #pragma unroll
-          for (int o = 8; o > 0; o >>= 1) {
-            const float c = __shfl_xor(bc, o, 64);
-            const int at = __shfl_xor(ba, o, 64);
-            if (small_better(c, at, bc, ba)) { bc = c; ba = at; }
-          }
-          const int v = v0 + 4 * (l >> 4) + i;
-          if ((l & 15) == 0 && v < n) { s_bc[w * NV + v] = bc; s_ba[w * NV + v] = ba; }
+        for (int o = 16; o <= 32; o <<= 1) {
+          const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)k, o, 64);
+          const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(k >> 32), o, 64);
+          k = max_u64(k, ((uint64_t)hi << 32) | lo);
         }
+        const int v = v0 + l;
+        if (l < 16 && v < n) s_key[w * NV + v] = k;
       }
       __syncthreads();
       // the workgroup's winner per vector: the best of the waves' winners
-      for (int v = tid; v < n; v += ESB) {
-        float bc = s_bc[v];
-        int ba = s_ba[v];
+      if (tid < n) {
+        uint64_t k = s_key[tid];
 #pragma unroll
-        for (int q = 1; q < NW; ++q)
-          if (small_better(s_bc[q * NV + v], s_ba[q * NV + v], bc, ba)) {
-            bc = s_bc[q * NV + v]; ba = s_ba[q * NV + v];
-          }
-        pq[(int64_t)v * G + wg] = make_int2(__float_as_int(bc), ba);
+        for (int q = 1; q < NW; ++q) k = max_u64(k, s_key[q * NV + tid]);
+        pq[(int64_t)tid * G + wg] = k;
       }
     } else {
       // --- correlations on the vector ALUs (fp32 dictionary): thread (atom,
       // half) takes the vectors of its half, each a sequential fp32 dot
       // product over k ---------------------------------------------------------
       const int al = tid % ECHS, half = tid / ECHS;
-      const int atom = wg * ECHS + al;
       const int nh = (n + 1) / 2;  // vectors [half * nh, min(n, half * nh + nh))
       const int v0 = half * nh, v1 = min(n, v0 + nh);
-      if (atom < L.N) {
 #pragma unroll
-        for (int j = 0; j < NV / 2; ++j) {
-          if (v0 + j < v1) {
-            float sacc = 0.f;
+      for (int j = 0; j < NV / 2; ++j) {
+        if (v0 + j < v1) {
+          float sacc = 0.f;
 #pragma unroll
-            for (int q = 0; q < D / 4; ++q) {
-              const float4 r4 = *(const float4*)&s_r[(v0 + j) * RP + 4 * q];
-              sacc = fmaf(r4.x, frow[q].x, sacc); sacc = fmaf(r4.y, frow[q].y, sacc);
-              sacc = fmaf(r4.z, frow[q].z, sacc); sacc = fmaf(r4.w, frow[q].w, sacc);
-            }
-            s_c[(v0 + j) * ECHS + al] = sacc;
+          for (int q = 0; q < D / 4; ++q) {
+            const float4 r4 = *(const float4*)&s_r[(v0 + j) * RP + 4 * q];
+            sacc = fmaf(r4.x, frow[q].x, sacc); sacc = fmaf(r4.y, frow[q].y, sacc);
+            sacc = fmaf(r4.z, frow[q].z, sacc); sacc = fmaf(r4.w, frow[q].w, sacc);
           }
+          s_c[(v0 + j) * ECHS + al] = sacc;
         }
       }
       __syncthreads();
       // per vector: the best of this workgroup's atoms (wave w: vectors w, w+NW, ...)
       for (int v = w; v < n; v += NW) {
-        float bc = 0.f;
-        int ba = 0x7FFFFFFF;
+        uint64_t k = 0;
 #pragma unroll
         for (int t = 0; t < ECHS / 64; ++t) {
           const int q = l + 64 * t, at = wg * ECHS + q;
-          if (at < L.N && small_better(s_c[v * ECHS + q], at, bc, ba)) { bc = s_c[v * ECHS + q]; ba = at; }
+          if (at < L.N) k = max_u64(k, win_key(s_c[v * ECHS + q], at));
         }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-          const float c = __shfl_xor(bc, o, 64);
-          const int at = __shfl_xor(ba, o, 64);
-          if (small_better(c, at, bc, ba)) { bc = c; ba = at; }
-        }
-        if (l == 0) pq[(int64_t)v * G + wg] = make_int2(__float_as_int(bc), ba);
+        k = wave_max_u64(k);
+        if (l == 0) pq[(int64_t)v * G + wg] = k;
       }
     }
   } else if (wg == 0) {
     // --- final outputs -----------------------------------------------------------
-    for (int v = w; v < n; v += NW) {
-      float s2 = 0.f;
-      for (int k = l; k < D; k += 64) s2 = fmaf(s_r[v * RP + k], s_r[v * RP + k], s2);
-      s2 = wave_sum(s2);
-      if (l == 0 && a.resid_norm) a.resid_norm[v] = sqrtf(s2);
+    // |r_K|: a vector's D/4 groups sit in D/4 consecutive lanes of one pass
+    if (a.resid_norm) {
+#pragma unroll
+      for (int j = 0; j < NQ; ++j) {
+        float s2 = rr[j].x * rr[j].x;
+        s2 = fmaf(rr[j].y, rr[j].y, s2); s2 = fmaf(rr[j].z, rr[j].z, s2); s2 = fmaf(rr[j].w, rr[j].w, s2);
+#pragma unroll
+        for (int o = D / 8; o > 0; o >>= 1) s2 += __shfl_xor(s2, o, 64);
+        const int gq = tid + j * ESB;
+        if (gq < nq && gq % (D / 4) == 0) a.resid_norm[4 * gq / D] = sqrtf(s2);
+      }
     }
     // words of steps before K - 1 come from earlier launches; the last one
     // from this workgroup's own reduction
@@ -658,7 +658,7 @@ static SmallArgs small_args(const sdkv_encode_args* a, const EncodePlan& p, char
   s.x = a->x;
   s.dict = a->dict;
   s.r = (float*)(base + p.off_r);
-  s.part = (int2*)(base + p.off_part);
+  s.part = (uint64_t*)(base + p.off_part);
   s.codes = a->codes;
   s.codes_ld = a->codes_ld ? a->codes_ld : a->K;
   s.coef_f32 = a->coef_f32;

@@ -101,6 +101,36 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return wave_last(wave_scan_dpp(v, 0u, [](uint32_t x, uint32_t y) { return max(x, y); }));
 }
+// 64-bit maximum over each row of 16 lanes (row_ror 1, 2, 4, 8), in every lane
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t row_max_u64(uint64_t v) {
+  uint64_t t;
+  t = dpp_u64<0x121>(v); v = t > v ? t : v;
+  t = dpp_u64<0x122>(v); v = t > v ? t : v;
+  t = dpp_u64<0x124>(v); v = t > v ? t : v;
+  t = dpp_u64<0x128>(v); v = t > v ? t : v;
+  return v;
+}
+__device__ __forceinline__ uint64_t lane_u64(uint64_t v, int lane) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+  return ((uint64_t)hi << 32) | lo;
+}
+// 64-bit maximum over the wave, returned to every lane as a scalar
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = row_max_u64(v);
+  uint64_t r = lane_u64(v, 0), t;
+  t = lane_u64(v, 16); r = t > r ? t : r;
+  t = lane_u64(v, 32); r = t > r ? t : r;
+  t = lane_u64(v, 48); r = t > r ? t : r;
+  return r;
+}
+
 // sum within aligned groups of G lanes (G = 16 or 32)
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {

@@ -28,6 +28,9 @@
  *    that share a workspace must not overlap in time.
  *  - Inputs must be finite. Code indices must be < n_atoms; other indices
  *    give unspecified (but in-bounds) results.
+ *  - Dictionaries, encode inputs x, queries q and workspaces must start at
+ *    16-byte aligned addresses (every torch allocation does), else
+ *    SDKV_ERR_UNSUPPORTED; other pointers need their element's alignment.
  */
 #ifndef SDKV_H
 #define SDKV_H

@@ -198,3 +198,19 @@ def test_encode_pair_validation():
     assert lib.sdkv_encode_pair(ctypes.byref(k), ctypes.byref(v), ctypes.c_void_p(FAKE), nb.value - 1,
                                 None) == sd.SDKV_ERR_WORKSPACE
     assert lib.sdkv_encode_pair_workspace(ctypes.byref(k), ctypes.byref(v), None) == sd.SDKV_ERR_NULL
+
+
+def test_misaligned_pointers_rejected():
+    lib = sd.lib()
+    nb = ctypes.c_size_t(0)
+    for field in ("x", "dict"):
+        a = good_enc(**{field: FAKE + 8})
+        assert lib.sdkv_encode_workspace(ctypes.byref(a), ctypes.byref(nb)) == sd.SDKV_ERR_UNSUPPORTED
+    for field in ("q", "dk", "dv"):
+        assert ws_status(good_attn(**{field: FAKE + 2}))[0] == sd.SDKV_ERR_UNSUPPORTED
+    a = good_enc()
+    assert lib.sdkv_encode_workspace(ctypes.byref(a), ctypes.byref(nb)) == 0
+    assert lib.sdkv_encode(ctypes.byref(a), ctypes.c_void_p(FAKE + 4), nb.value, None) == sd.SDKV_ERR_UNSUPPORTED
+    at = good_attn()
+    _, anb = ws_status(at)
+    assert lib.sdkv_decode_attn(ctypes.byref(at), ctypes.c_void_p(FAKE + 4), anb, None) == sd.SDKV_ERR_UNSUPPORTED
