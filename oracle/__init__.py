@@ -17,6 +17,8 @@ Sources (pages of "LLM Inference in a Flash!"):
     16 atom indices plus coefficients; three atoms are enough to rank most
     tokens.
   * abstract page: keys and values are sums of fixed dictionary vectors.
+  * review page, Summary and Strengths (integer-only execution): the
+    integer softmax of integer_softmax.py.
 
 Every function here has a pin in tests/test_oracle_*.py (closed forms,
 invariants, brute force with exact rational arithmetic, hand-worked golden
@@ -27,3 +29,4 @@ from .sdkv_oracle import (  # noqa: F401
     unpack_codes, pack_codes, mp_encode, decode_attn, select_topk,
     selected_count,
 )
+from .integer_softmax import int_softmax, int_exp_consts, INT_SOFTMAX_P_BITS  # noqa: F401

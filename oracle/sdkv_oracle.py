@@ -7,6 +7,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from oracle.integer_softmax import INT_SOFTMAX_P_BITS, int_softmax
+
 __all__ = ["unpack_codes", "pack_codes", "mp_encode", "decode_attn",
            "select_topk", "selected_count"]
 
@@ -112,7 +114,8 @@ def select_topk(scores: np.ndarray, k: int) -> np.ndarray:
 
 
 def decode_attn(q, dk, dv, key_codes, val_codes, klow: int, khigh: int,
-                top_num: int, top_den: int, scale: float, sel=None):
+                top_num: int, top_den: int, scale: float, sel=None, softmax: str = "float",
+                s_high_in=None):
     """Hierarchical coded decode attention for one layer.
 
     Review page, Summary: every token is scored from its first Klow atoms
@@ -140,6 +143,15 @@ def decode_attn(q, dk, dv, key_codes, val_codes, klow: int, khigh: int,
     to re-evaluate the output on another implementation's selection when two
     selections differ only by tokens tied with the threshold.
 
+    softmax="int" replaces p by the integer-only softmax of
+    oracle.int_softmax (review page, Summary and Strengths: token-wise INT16
+    requantization, integer polynomial exp, shift guards, fixed-point
+    reciprocal) applied to s_high rounded to fp32, the precision in which
+    the scores reach the requantization; p = p_int / 2^15 and w, out follow
+    in fp64. `s_high_in` (optional [B,Hq,m], with `sel`) supplies those fp32
+    scores instead, so the integer steps can be checked bit for bit on
+    another implementation's scores. The result then also holds p_int.
+
     Returns a dict of float64 arrays: u [B,Hq,N], s_low [B,Hq,T],
     sel int64 [B,Hq,m] ascending, s_high [B,Hq,m], p [B,Hq,m],
     w [B,Hq,N], out [B,Hq,d], and m.
@@ -161,6 +173,10 @@ def decode_attn(q, dk, dv, key_codes, val_codes, klow: int, khigh: int,
     res["w"] = np.zeros((B, Hq, N))
     res["out"] = np.zeros((B, Hq, d))
     res["m"] = m
+    if softmax == "int":
+        res["p_int"] = np.zeros((B, Hq, m), dtype=np.int64)
+    elif softmax != "float":
+        raise ValueError(softmax)
     for b in range(B):
         for g in range(Hkv):
             ki, kc = unpack_codes(key_codes[b, g])
@@ -174,8 +190,15 @@ def decode_attn(q, dk, dv, key_codes, val_codes, klow: int, khigh: int,
                 else:
                     S = np.sort(np.asarray(sel[b, h], dtype=np.int64))
                 s_high = (kc[S, :khigh] * u[ki[S, :khigh]]).sum(axis=1)
-                e = np.exp(s_high - s_high.max())
-                p = e / e.sum()
+                if softmax == "int":
+                    s32 = (np.asarray(s_high_in[b, h], dtype=np.float32) if s_high_in is not None
+                           else s_high.astype(np.float32))
+                    pi = int_softmax(s32)
+                    res["p_int"][b, h] = pi
+                    p = pi.astype(np.float64) / 2.0 ** INT_SOFTMAX_P_BITS
+                else:
+                    e = np.exp(s_high - s_high.max())
+                    p = e / e.sum()
                 w = np.bincount(vi[S].ravel(), weights=(p[:, None] * vc[S]).ravel(),
                                 minlength=N)
                 res["u"][b, h] = u

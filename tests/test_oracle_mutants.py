@@ -83,3 +83,81 @@ def test_unmutated_source_passes():
     m = build(("import numpy as np", "import numpy as np"))
     assert not _fails(pins.DECODE_CHECKS, m.decode_attn)
     assert not _fails(pins.ENCODE_CHECKS, lambda X, D, K: m.mp_encode(X, D, K))
+
+
+# --- the integer softmax -------------------------------------------------------
+import math  # noqa: E402
+
+import numpy as np  # noqa: E402
+
+import oracle.integer_softmax as isx_mod  # noqa: E402
+
+ISX_SRC = inspect.getsource(isx_mod)
+
+INT_MUTANTS = {
+    "guard_truncates": ("e2 = (e + (1 << (h - 1))) >> h if h > 0 else e", "e2 = e >> h"),
+    "no_max_subtract": ("e = int_exp(q - q.max(), c)", "e = int_exp(np.minimum(q, 0), c)"),
+    "short_reciprocal": ("r = (1 << 62) // tot\n    p = (e2 * r) >> 32",
+                         "r = (1 << 31) // tot\n    p = (e2 * r) >> 1"),
+    "b_shift_off_by_one": ('"q_b": B_Q30 >> (Q - k)', '"q_b": B_Q30 >> (Q - k - 1)'),
+    "scale_off_by_one": ("return min(K_MAX, max(K_MIN, IN_BITS - E))",
+                         "return min(K_MAX, max(K_MIN, IN_BITS - E + 1))"),
+    "reduction_precision": ("qp = -((X - z * LN2_Q30) >> (Q - k))",
+                            "qp = -((X - z * LN2_Q30) >> (Q - k + 1))"),
+    "poly_sign": ('t = (qp + c["q_b"]) >> c["g"]', 't = (c["q_b"] - qp) >> c["g"]'),
+}
+
+
+def _int_checks(m):
+    """The integer-softmax pins, run on module m."""
+    def golden():
+        assert m.int_softmax(np.array([1.0, 0.0], np.float32)).tolist() == [784850122, 288891701]
+
+    def exp_bound():
+        for k in (8, 14, 20):
+            c = m.int_exp_consts(k)
+            kk = k - c["g"]
+            qd = np.arange(-40000, 1, dtype=np.int64)
+            approx = m.int_exp(qd, c).astype(np.float64) * 0.3585 / 2.0 ** (2 * kk)
+            x = qd / 2.0 ** k
+            z = np.floor(-x / math.log(2) + 1e-12)
+            keep = z <= 12
+            bound = 1.1 * (3.2e-3 + 1.1 * 2.0 ** -k + 7 * 2.0 ** -kk + 0.72 * 2.0 ** (z - 2 * kk))
+            assert np.all((np.abs(approx - np.exp(x)) / np.exp(x))[keep] <= bound[keep])
+
+    def float_agreement():
+        rng = np.random.default_rng(3)
+        for scale, n in ((1.0, 410), (3.0, 2000), (0.01, 5000)):
+            s = (rng.standard_normal(n) * scale).astype(np.float32)
+            p = m.int_softmax(s) / 2.0 ** 30
+            e = np.exp(s.astype(np.float64) - s.max())
+            pf = e / e.sum()
+            assert abs(p.sum() - 1) <= 2e-5 and np.abs(p - pf).sum() <= 2e-2
+
+    return [golden, exp_bound, float_agreement]
+
+
+def _int_fails(m):
+    for chk in _int_checks(m):
+        try:
+            chk()
+        except Exception:
+            return True
+    return False
+
+
+def _build_isx(mutation):
+    old, new = mutation
+    assert old in ISX_SRC, old
+    mod = types.ModuleType("isx_mutant")
+    exec(compile(ISX_SRC.replace(old, new), "<isx-mutant>", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(INT_MUTANTS))
+def test_int_softmax_mutant_is_caught(name):
+    assert _int_fails(_build_isx(INT_MUTANTS[name])), f"no pin catches integer-softmax mutant {name}"
+
+
+def test_unmutated_int_softmax_passes():
+    assert not _int_fails(_build_isx(("import math", "import math")))
