@@ -187,6 +187,25 @@ def bench_decode(args, torch, sd, synth, ev):
     torch.cuda.synchronize()
     stage_ms = [float(np.mean([ev.ms(e[j], e[j + 1]) for e in evs])) for j in range(nstage - 1)]
 
+    # the same step with the integer-only softmax (a flag of the same call)
+    icalls = [sd.DecodeCall(s["q"], s["dk"], s["dv"], s["kv"], None, klow=case.klow,
+                            khigh=case.khigh, top_num=case.top_num, top_den=case.top_den,
+                            scale=case.scale, key_low=s["kl"], out=out, workspace=ws,
+                            softmax="int")
+              for s in sets]
+    for i in range(args.warmup):
+        icalls[i % nsets].launch()
+    torch.cuda.synchronize()
+    ev.record(t0, stream.cuda_stream)
+    for i in range(args.steps):
+        icalls[i % nsets].launch()
+    ev.record(t1, stream.cuda_stream)
+    torch.cuda.synchronize()
+    ims = ev.ms(t0, t1) / args.steps
+    int_res = {"metric": "decode step with the integer-only softmax",
+               "us_per_step": round(ims * 1e3, 2), "value": round(B * T / (ims * 1e-3), 1),
+               "unit": "context-tokens/s", "relative_to_fp32_softmax_step": round(ims / ms, 3)}
+
     # algorithmic bytes (HBM): what the method must read per step
     low_b = B * Hkv * T * case.klow * 4
     refine_b = B * Hq * m * (case.khigh - case.klow) * 4
@@ -211,7 +230,7 @@ def bench_decode(args, torch, sd, synth, ev):
               "frac": round(total_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         config=dict(B=B, Hq=Hq, Hkv=Hkv, T=T, d=d, n_atoms=N, K=K, klow=case.klow,
                     khigh=case.khigh, top="1/10", m=m, input_sets=nsets),
-        case=case)
+        int_softmax=int_res, case=case)
     return res
 
 
@@ -403,6 +422,7 @@ def main():
         + ", ".join(f"{k} {v * 1e3:.1f}" for k, v in dec["stage_ms"].items()))
     app = bench_append(args, torch, sd, synth, ev, dec)
     log(f"  decode-step append (16 vectors): {app['us_per_step']:.1f} us")
+    log(f"  integer-only softmax step: {dec['int_softmax']['us_per_step']:.1f} us")
     enc = None
     if not args.no_encode:
         log("encode benchmark (524,288 vectors)")
@@ -431,6 +451,7 @@ def main():
         "cpu_baseline": cpu,
     }
     line["append"] = app
+    line["int_softmax"] = dec["int_softmax"]
     if enc is not None:
         line["encode"] = {
             "metric": "KV vectors encoded/s", "value": round(enc["value"], 1),

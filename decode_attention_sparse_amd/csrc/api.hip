@@ -84,6 +84,8 @@ static sdkv_status check_attn(const sdkv_attn_args* a) {
   if (a->klow < 1 || a->klow > a->khigh || a->khigh > a->K) return SDKV_ERR_SHAPE;
   if (a->top_num < 1 || a->top_den < a->top_num || a->top_den > 0x7FFFFFFF) return SDKV_ERR_SHAPE;
   if (!isfinite(a->scale)) return SDKV_ERR_SHAPE;
+  if (a->softmax_mode != SDKV_SOFTMAX_FLOAT && a->softmax_mode != SDKV_SOFTMAX_INT)
+    return SDKV_ERR_SHAPE;
   if (a->q_dtype != SDKV_BF16) return SDKV_ERR_UNSUPPORTED;
   if (a->n_atoms > kMaxAtomsDecode) return SDKV_ERR_UNSUPPORTED;
   if ((int64_t)a->B * a->Hq > 0x7FFFFFFF / 64) return SDKV_ERR_UNSUPPORTED;

@@ -125,7 +125,66 @@ struct RowsArgs {
   uint32_t* err;
   uint32_t* ticket;         // [8] workgroup start-order counters, zeroed per call
   int xcd_map;              // per-XCD ticket classes (rows stay on one XCD)
+  int imode;                // integer-only softmax
+  int32_t* p_int_out;       // optional [rows, m] integer probabilities
+  uint32_t* ixchg;          // [rows, P, 4] integer-softmax exchange words
 };
+
+// --- integer-only softmax (review page, Summary and Strengths: token-wise
+// INT16 requantization of the Softmax input, an integer polynomial exp, shift
+// guards against INT32 overflow, fixed-point reciprocals). The polynomial is
+// I-BERT's fit exp(p) ~ a (p + b)^2 + c on (-ln2, 0], a = 0.3585, b = 1.353,
+// c = 0.344; the constants below are ln 2, b and c / a with 30 fractional
+// bits (floor).
+constexpr uint64_t kLN2_Q30 = 744261117ull;
+constexpr int64_t kB_Q30 = 1452772687ll;
+constexpr int64_t kCA_Q30 = 1030312935ll;
+
+struct IntSoftmax {
+  int k;      // requantization shift: q = rint(s 2^k), |q| <= 32767
+  int qmax;   // the row's largest q
+  int qb, g, qc;  // b 2^k; guard shift of the polynomial; (c/a) 2^(2(k-g))
+  int h;      // guard shift of the exponentials before the INT32 sum
+};
+
+__device__ __forceinline__ int requant16(float s, int k) {
+  return (int)fminf(fmaxf(rintf(ldexpf(s, k)), -32767.f), 32767.f);
+}
+
+// Row constants from the row's largest and smallest score and its size m.
+__device__ __forceinline__ IntSoftmax int_softmax_consts(float smax, float smin, int64_t m) {
+  IntSoftmax c;
+  const float A = fmaxf(fabsf(smax), fabsf(smin));
+  if (A == 0.f) {
+    c.k = 30;
+  } else {
+    int E;
+    frexpf(A, &E);  // A = f 2^E, f in [0.5, 1)
+    c.k = min(30, max(1, 15 - E));
+  }
+  c.qmax = requant16(smax, c.k);
+  c.qb = (int)(kB_Q30 >> (30 - c.k));
+  c.g = max(0, c.k - 14);
+  c.qc = (int)(kCA_Q30 >> (30 - 2 * (c.k - c.g)));
+  const uint32_t tb = (uint32_t)(c.qb >> c.g);
+  const uint32_t emax = tb * tb + (uint32_t)c.qc;
+  c.h = max(0, (64 - __clzll((unsigned long long)m)) + (32 - __clz(emax)) - 30);
+  return c;
+}
+
+// e' of one score: the range reduction x = -z ln2 + p at 30 fractional bits,
+// p truncated to k bits, 2^-z times the polynomial, then the rounding guard
+// shift by h.
+__device__ __forceinline__ uint32_t int_exp_guarded(float s, const IntSoftmax& c) {
+  const int qd = requant16(s, c.k) - c.qmax;  // <= 0
+  const uint64_t X = (uint64_t)(-qd) << (30 - c.k);
+  const uint64_t z = X / kLN2_Q30;
+  if (z >= 31) return 0u;
+  const int qp = -(int)((X - z * kLN2_Q30) >> (30 - c.k));
+  const int t = (qp + c.qb) >> c.g;
+  const uint32_t e = ((uint32_t)(t * t) + (uint32_t)c.qc) >> (int)z;
+  return c.h > 0 ? (e + (1u << (c.h - 1))) >> c.h : e;
+}
 
 static_assert(kRowThreads == SB && kMaxRowSPT == kMaxSPT, "planner and kernels disagree");
 
@@ -218,7 +277,9 @@ __device__ __forceinline__ void score_chunk(const RowsArgs& a, int row, const ui
   }
 }
 
-template <int SPT, bool FAST>
+// IM: the integer-only softmax (a separate build, so the fp32 kernel keeps
+// its registers).
+template <int SPT, bool FAST, bool IM>
 __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   __shared__ float s_u[kMaxAtomsDecode];
   __shared__ SelShared sh;
@@ -330,7 +391,7 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
     nbar = 1;
     if (sample_window_select<SPT>(key, skey, (uint32_t)ns, (uint32_t)a.m, (uint32_t)a.T, sh, grp,
                                   a.wtab + (int64_t)row * a.P * 2048, &tau, &sel, s_qcnt)) {
-      need_offset = a.sel_out != nullptr || a.s_high_out != nullptr;
+      need_offset = a.sel_out != nullptr || a.s_high_out != nullptr || a.p_int_out != nullptr;
     } else {
       sel = radix_select_coop<SPT>(key, (uint32_t)a.m, sh, grp, &offset, &count, &tau, s_qcnt, 1u);
       nbar = 3;
@@ -365,7 +426,7 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   // debug outputs need the row-global position of this workgroup's entries
   if (need_offset) {
     if (tid == 0) st_agent(&grp.xchg[2 * p + 1], nsel);
-    group_barrier(grp.bar, (uint32_t)a.P, nbar + 1u, grp.local, grp.err);
+    group_barrier(grp.bar, (uint32_t)a.P, ++nbar, grp.local, grp.err);
     if (tid == 0) {
       uint32_t off = 0;
       for (int q = 0; q < p; ++q) off += ld_agent(&grp.xchg[2 * q + 1]);
@@ -387,6 +448,7 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   const bool one_batch = cnt <= (int64_t)SB * kTokBatch;
   // (lmax, vb): running max of s_high and sum_t exp(s_t - lmax) sum_j |kappa^v_tj|
   float lmax = -INFINITY, vb = 0.f;
+  float lmin = INFINITY, vmax = 0.f;  // integer mode: score range, largest sum_j |kappa^v|
   uint32_t vw[kTokBatch][32];
   for (int64_t base = 0; base < cnt; base += (int64_t)SB * kTokBatch) {
     int64_t tt[kTokBatch];
@@ -421,6 +483,10 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
       if (i < cnt) {
         if (in_lds) s_ls[i] = s;
         else sh_g[i] = s;
+        if constexpr (IM) {
+          lmin = fminf(lmin, s);
+          vmax = fmaxf(vmax, va);
+        }
         if (s > lmax) {
           vb = vb * __expf(lmax - s) + va;
           lmax = s;
@@ -450,12 +516,78 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
     });
   }
 
+  // 5b. integer mode: the row's score range, every token's guarded integer
+  // exponential e' (stored over its score), the row's sum of e' and the
+  // 62-bit reciprocal. Two exchanges among the row's workgroups.
+  uint64_t rcp = 0;
+  if constexpr (IM) {
+    const float mn = -block_max<SNW>(-lmin, s_red);
+    float smax = M, smin = mn;
+    uint32_t* ix = a.ixchg + (int64_t)row * a.P * 4;
+    if (a.P > 1) {
+      if (tid == 0) {
+        st_agent(&ix[4 * p], __float_as_uint(M));
+        st_agent(&ix[4 * p + 1], __float_as_uint(mn));
+      }
+      group_barrier(grp.bar, (uint32_t)a.P, ++nbar, grp.local, grp.err);
+      if (tid == 0) {
+        for (int q = 0; q < a.P; ++q) {
+          smax = fmaxf(smax, __uint_as_float(ld_agent(&ix[4 * q])));
+          smin = fminf(smin, __uint_as_float(ld_agent(&ix[4 * q + 1])));
+        }
+        sh.bcast[0] = __float_as_uint(smax);
+        sh.bcast[1] = __float_as_uint(smin);
+      }
+      __syncthreads();
+      smax = __uint_as_float(sh.bcast[0]);
+      smin = __uint_as_float(sh.bcast[1]);
+    }
+    const IntSoftmax ic = int_softmax_consts(smax, smin, a.m);
+    uint32_t esum = 0;
+    for (int64_t i = tid; i < cnt; i += SB) {
+      float* slot = in_lds ? &s_ls[i] : &sh_g[i];
+      const uint32_t e = int_exp_guarded(*slot, ic);
+      *slot = __uint_as_float(e);
+      esum += e;
+    }
+    __threadfence_block();
+    uint32_t tot;
+    (void)block_excl_scan<SNW>(esum, sh.tmp, &tot);
+    if (a.P > 1) {
+      if (tid == 0) st_agent(&ix[4 * p + 2], tot);
+      group_barrier(grp.bar, (uint32_t)a.P, ++nbar, grp.local, grp.err);
+      if (tid == 0) {
+        uint32_t t = 0;
+        for (int q = 0; q < a.P; ++q) t += ld_agent(&ix[4 * q + 2]);
+        sh.bcast[2] = t;
+      }
+      __syncthreads();
+      tot = sh.bcast[2];
+    }
+    rcp = tot ? (1ull << 62) / tot : 0ull;
+    if (a.p_int_out) {
+      int32_t* pd = a.p_int_out + (int64_t)row * a.m;
+      ordered_ranks<SPT>(sel, sh, [&](int j, uint32_t r) {
+        const int64_t i = (int64_t)offset + r;
+        if (i < a.m) {
+          const uint32_t lp = lbase + (uint32_t)__popc(sel & ((1u << j) - 1u));
+          const uint32_t e = __float_as_uint(in_lds ? s_ls[lp] : sh_g[lp]);
+          pd[i] = (int32_t)(((uint64_t)e * rcp) >> 32);
+        }
+      });
+    }
+  }
+  // fixed-point scale bound: sum_t p_t sum_j |kappa^v_tj| <= the largest sum
+  // when the p_t sum to at most 1 (integer mode)
+  float vbound = vsum;
+  if constexpr (IM) vbound = block_max<SNW>(vmax, s_red) * 1.0001f;
+
   // 6. softmax weights and per-atom value weights. LDS integer atomics are
   // much faster than float ones on gfx950, so weights accumulate in int32
   // fixed point with a power-of-two scale S such that S * sum|p kappa| <=
   // 2^30: no bin can overflow, and each contribution is rounded to 2^-31
   // of the workgroup's total weight mass.
-  const int sexp = (vsum > 0.f) ? 30 - ilogbf(vsum) - 1 : 0;
+  const int sexp = (vbound > 0.f) ? 30 - ilogbf(vbound) - 1 : 0;
   const float S = ldexpf(1.f, min(sexp, 100));
   int32_t* s_w = (int32_t*)s_u;
   for (int i = tid; i < a.N; i += SB) s_w[i] = 0;
@@ -485,7 +617,8 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
     for (int r = 0; r < kTokBatch; ++r) {
       const int64_t i = base + (int64_t)r * SB + tid;
       if (i < cnt) {
-        const float pr = __expf(pt[r] - M);
+        const float pr = IM ? (float)(((uint64_t)__float_as_uint(pt[r]) * rcp) >> 32) * 0x1p-30f
+                            : __expf(pt[r] - M);
         lsum += pr;
         const float ps = pr * S;
         if (FAST) {
@@ -518,7 +651,10 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
     __builtin_nontemporal_store((float)v.w * invS, &dst[4 * i + 3]);
   }
   for (int i = (n4 << 2) + tid; i < a.N; i += SB) dst[i] = (float)s_w[i] * invS;
-  if (tid == 0) a.stats[(int64_t)row * a.P + p] = make_float2(cnt > 0 ? M : -INFINITY, lsum_all);
+  // (integer mode: the weights are already normalised; the merge adds them)
+  if (tid == 0)
+    a.stats[(int64_t)row * a.P + p] =
+        IM ? make_float2(0.f, 1.f) : make_float2(cnt > 0 ? M : -INFINITY, lsum_all);
 }
 
 // ---------------------------------------------------------------------------
@@ -531,6 +667,7 @@ struct WdvArgs {
   int N, d, P, rows, nrt, nsub, nchunks;
   float* opart;           // [nchunks, rows, d]
   float* w_out;           // optional [rows, N] normalised weights
+  int presum;             // partials already normalised (integer softmax): add them
 };
 
 constexpr int WSUB = 128;                 // atoms per MFMA sub-chunk
@@ -553,7 +690,7 @@ __device__ __forceinline__ void wdv_coefs(const WdvArgs& a, int r0, float* s_coe
     const float Mx = wave_max(Mq);
     const float c = (lq > 0.f) ? __expf(Mq - Mx) : 0.f;
     const float Lr = wave_sum(c * lq);
-    if (l < a.P) s_coef[r * kMaxRowP + l] = (Lr > 0.f) ? c / Lr : 0.f;
+    if (l < a.P) s_coef[r * kMaxRowP + l] = a.presum ? 1.f : (Lr > 0.f) ? c / Lr : 0.f;
   }
 }
 
@@ -658,7 +795,7 @@ __global__ __launch_bounds__(512) void k_wdv_bf16(WdvArgs a) {
       const float Mx = wave_max(Mq);
       const float c = (lq > 0.f) ? __expf(Mq - Mx) : 0.f;
       const float Lr = wave_sum(c * lq);
-      if (l < a.P) s_coef[(w + 8 * k) * kMaxRowP + l] = (Lr > 0.f) ? c / Lr : 0.f;
+      if (l < a.P) s_coef[(w + 8 * k) * kMaxRowP + l] = a.presum ? 1.f : (Lr > 0.f) ? c / Lr : 0.f;
     }
   }
   __syncthreads();
@@ -892,14 +1029,18 @@ sdkv_status plan_decode(const sdkv_attn_args* a, DecodePlan* p) {
   q.off_opart = off;  off = align_up(off + (size_t)q.nchunks * rows * a->d * 4, A);
   q.off_cand = off;   off = align_up(off + (q.P > 1 ? (size_t)rows * q.P * q.chunk * 4 : 0), A);
   q.off_wtab = off;   off = align_up(off + (q.P > 1 ? (size_t)rows * q.P * 2048 * 4 : 0), A);
+  q.off_ixchg = off;  off = align_up(off + (size_t)rows * q.P * 4 * 4, A);
   q.total = off;
   *p = q;
   return SDKV_OK;
 }
 
-static const void* pick_rows_kernel(int spt, bool fast) {
-#define SDKV_PICK(S) \
-  if (spt == S) return fast ? (const void*)&k_rows<S, true> : (const void*)&k_rows<S, false>;
+static const void* pick_rows_kernel(int spt, bool fast, bool im) {
+#define SDKV_PICK(S)                                                                        \
+  if (spt == S) {                                                                           \
+    if (im) return fast ? (const void*)&k_rows<S, true, true> : (const void*)&k_rows<S, false, true>; \
+    return fast ? (const void*)&k_rows<S, true, false> : (const void*)&k_rows<S, false, false>; \
+  }
   SDKV_PICK(4)
   SDKV_PICK(8)
   SDKV_PICK(16)
@@ -979,9 +1120,12 @@ sdkv_status launch_decode(const sdkv_attn_args* a, const DecodePlan& p, void* ws
   ra.xchg = xchg;
   ra.bar = bar;
   ra.err = err;
+  ra.imode = a->softmax_mode == SDKV_SOFTMAX_INT ? 1 : 0;
+  ra.p_int_out = ra.imode ? a->p_int : nullptr;
+  ra.ixchg = (uint32_t*)(base + p.off_ixchg);
   const bool aligned = (((uintptr_t)a->key_codes | (uintptr_t)a->val_codes) & 15u) == 0 &&
                        ra.rs % 4 == 0;
-  const void* kfn = pick_rows_kernel(p.spt, p.fast && aligned);
+  const void* kfn = pick_rows_kernel(p.spt, p.fast && aligned, ra.imode != 0);
   if (!kfn) return SDKV_ERR_UNSUPPORTED;
   ra.ticket = (uint32_t*)(base + p.off_ticket);
   // Per-XCD ticket classes need whole rows per class; with P > 1 every
@@ -1009,6 +1153,7 @@ sdkv_status launch_decode(const sdkv_attn_args* a, const DecodePlan& p, void* ws
   WdvArgs wa;
   wa.wpart = wpart;
   wa.stats = stats;
+  wa.presum = a->softmax_mode == SDKV_SOFTMAX_INT ? 1 : 0;
   wa.P = p.P;
   wa.w_out = a->w;
   wa.dv = a->dv;

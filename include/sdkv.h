@@ -48,7 +48,7 @@ extern "C" {
 #define SDKV_API
 #endif
 
-#define SDKV_ABI_VERSION 3
+#define SDKV_ABI_VERSION 4
 
 typedef int32_t sdkv_status;
 #define SDKV_OK 0
@@ -179,8 +179,32 @@ typedef struct sdkv_attn_args {
      1 score/select/rescore/softmax/value weights, 2 W.Dv contraction,
      3 output reduction. A failed event record returns SDKV_ERR_DEVICE.   */
   void* const* stage_events;
+  /* Softmax over the selected tokens (review page, Summary and Strengths:
+     the integer-only execution; Table 1 and Section 3.1.3 on token-wise
+     INT16 requantization at the Softmax input):
+       SDKV_SOFTMAX_FLOAT (0): fp32 exp, as above.
+       SDKV_SOFTMAX_INT   (1): integer-only. Per row (b, h), with A the
+         largest |s_high| over S, k = clamp(15 - E, 1, 30) where A = f 2^E,
+         f in [0.5, 1) (k = 30 when A = 0):
+           q_t  = clamp(rint(s_high_t 2^k), -32767, 32767) - max_S q
+           exp: X = -q_t 2^(30-k); z = floor(X / LN2); qp = -((X - z LN2)
+                >> (30-k)); t = (qp + (B >> (30-k))) >> g, g = max(0, k-14);
+                e_t = (t^2 + (CA >> (30 - 2(k-g)))) >> z, 0 once z >= 31;
+                LN2 = 744261117, B = 1452772687, CA = 1030312935 (ln 2,
+                1.353 and 0.344/0.3585 with 30 fractional bits, floor:
+                I-BERT's fit exp(p) ~ 0.3585 (p + 1.353)^2 + 0.344)
+           guard: h = max(0, bitlen(m) + bitlen(e_max) - 30), e_max the
+                value at q = 0; e'_t = (e_t + 2^(h-1)) >> h (h > 0)
+           p_t = (e'_t floor(2^62 / sum_S e')) >> 32   (30 fractional bits)
+         and w[a] = sum_t (p_t / 2^30) kappa^v ... as above.
+       Other values: SDKV_ERR_SHAPE.                                      */
+  int32_t softmax_mode;
+  int32_t* p_int;       /* OUT [B, Hq, m] integer p_t aligned with sel
+                           (SDKV_SOFTMAX_INT only), or NULL               */
 } sdkv_attn_args;
 #define SDKV_DECODE_STAGES 4
+#define SDKV_SOFTMAX_FLOAT 0
+#define SDKV_SOFTMAX_INT 1
 
 /* m = ceil(T * top_num / top_den), clamped to [1, T]; 0 on bad input. */
 SDKV_API int64_t sdkv_selected_count(int64_t T, int64_t top_num, int64_t top_den);

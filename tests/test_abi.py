@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) == 11, names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.sdkv_abi_version() == 3
+    assert lib.sdkv_abi_version() == 4
 
 
 def test_status_strings():
@@ -79,6 +79,7 @@ def test_decode_workspace_query():
     ("n_atoms", 40000, sd.SDKV_ERR_UNSUPPORTED),
     ("code_stride", 15, sd.SDKV_ERR_SHAPE), ("code_stride", -32, sd.SDKV_ERR_SHAPE),
     ("code_stride", 65537, sd.SDKV_ERR_SHAPE),
+    ("softmax_mode", 2, sd.SDKV_ERR_SHAPE), ("softmax_mode", -1, sd.SDKV_ERR_SHAPE),
 ])
 def test_decode_validation(field, value, status):
     a = good_attn(**{field: value})
