@@ -115,7 +115,7 @@ def select_topk(scores: np.ndarray, k: int) -> np.ndarray:
 
 def decode_attn(q, dk, dv, key_codes, val_codes, klow: int, khigh: int,
                 top_num: int, top_den: int, scale: float, sel=None, softmax: str = "float",
-                s_high_in=None):
+                s_high_in=None, select: str = "head"):
     """Hierarchical coded decode attention for one layer.
 
     Review page, Summary: every token is scored from its first Klow atoms
@@ -152,6 +152,16 @@ def decode_attn(q, dk, dv, key_codes, val_codes, klow: int, khigh: int,
     scores instead, so the integer steps can be checked bit for bit on
     another implementation's scores. The result then also holds p_int.
 
+    select="kv" shares one selection among the G query heads of a KV head
+    (grouped-query attention): the tokens are ranked by the group's summed
+    low score sum_{h in g} s_low_h = sum_{j<klow} kappa_tj U_g[i_tj] with
+    U_g = sum_h u_h, and every head of the group takes the same S; s_high,
+    p and w stay per head. Reading: the pages make the selection
+    query-aware and say nothing of GQA (review page, Summary); summing the
+    group's scores is the plainest shared ranking (the score of the
+    group's summed query). In this mode res["s_low"] holds that shared
+    ranking score for every head of the group.
+
     Returns a dict of float64 arrays: u [B,Hq,N], s_low [B,Hq,T],
     sel int64 [B,Hq,m] ascending, s_high [B,Hq,m], p [B,Hq,m],
     w [B,Hq,N], out [B,Hq,d], and m.
@@ -177,15 +187,21 @@ def decode_attn(q, dk, dv, key_codes, val_codes, klow: int, khigh: int,
         res["p_int"] = np.zeros((B, Hq, m), dtype=np.int64)
     elif softmax != "float":
         raise ValueError(softmax)
+    if select not in ("head", "kv"):
+        raise ValueError(select)
     for b in range(B):
         for g in range(Hkv):
             ki, kc = unpack_codes(key_codes[b, g])
             vi, vc = unpack_codes(val_codes[b, g])
+            if select == "kv":
+                u_g = sum(scale * (dk @ q[b, hh]) for hh in range(g * G, (g + 1) * G))
+                s_shared = (kc[:, :klow] * u_g[ki[:, :klow]]).sum(axis=1)
             for h in range(g * G, (g + 1) * G):
                 u = scale * (dk @ q[b, h])
                 s_low = (kc[:, :klow] * u[ki[:, :klow]]).sum(axis=1)
+                s_rank = s_shared if select == "kv" else s_low
                 if sel is None:
-                    order = np.argsort(-s_low, kind="stable")
+                    order = np.argsort(-s_rank, kind="stable")
                     S = np.sort(order[:m])
                 else:
                     S = np.sort(np.asarray(sel[b, h], dtype=np.int64))
@@ -202,7 +218,7 @@ def decode_attn(q, dk, dv, key_codes, val_codes, klow: int, khigh: int,
                 w = np.bincount(vi[S].ravel(), weights=(p[:, None] * vc[S]).ravel(),
                                 minlength=N)
                 res["u"][b, h] = u
-                res["s_low"][b, h] = s_low
+                res["s_low"][b, h] = s_rank
                 res["sel"][b, h] = S
                 res["s_high"][b, h] = s_high
                 res["p"][b, h] = p

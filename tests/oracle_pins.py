@@ -341,9 +341,48 @@ def check_gqa_mapping(decode, seed=25):
             np.testing.assert_array_equal(r["sel"][b, h], r1["sel"][0, 0])
 
 
+def check_kv_shared_selection(decode, seed=27):
+    """select="kv": (a) one query head per KV head reduces to per-head
+    selection; (b) identical queries within a group give the per-head
+    result; (c) queries q and -q in a group of two cancel exactly, every
+    shared score is 0 and the first m tokens are taken; (d) the shared score
+    is the sum of the group's per-head low scores, every head of a group
+    takes the same set, and that set is the top m of the sum under the
+    (-score, index) order."""
+    q, dk, dv, kc, vc = small_decode_inputs(seed, B=2, Hq=3, Hkv=3, T=33, K=4)
+    a = decode(q, dk, dv, kc, vc, 2, 4, 1, 4, 0.7)
+    k = decode(q, dk, dv, kc, vc, 2, 4, 1, 4, 0.7, select="kv")
+    for key in ("sel", "s_low", "out"):
+        np.testing.assert_array_equal(a[key], k[key])
+    q2, dk, dv, kc, vc = small_decode_inputs(seed + 1, B=1, Hq=4, Hkv=2, T=29, K=3)
+    q2[:, 1], q2[:, 3] = q2[:, 0], q2[:, 2]
+    a = decode(q2, dk, dv, kc, vc, 2, 3, 1, 3, 1.0)
+    k = decode(q2, dk, dv, kc, vc, 2, 3, 1, 3, 1.0, select="kv")
+    np.testing.assert_array_equal(a["sel"], k["sel"])
+    np.testing.assert_allclose(k["out"], a["out"], rtol=0, atol=1e-14)
+    q3 = q2.copy()
+    q3[:, 1], q3[:, 3] = -q3[:, 0], -q3[:, 2]
+    k = decode(q3, dk, dv, kc, vc, 2, 3, 1, 3, 1.0, select="kv")
+    assert np.all(k["s_low"] == 0.0)
+    for h in range(4):
+        assert list(k["sel"][0, h]) == list(range(k["m"]))
+    q4, dk, dv, kc, vc = small_decode_inputs(seed + 2, B=2, Hq=6, Hkv=2, T=41, K=4)
+    a = decode(q4, dk, dv, kc, vc, 3, 4, 2, 7, 0.8)
+    k = decode(q4, dk, dv, kc, vc, 3, 4, 2, 7, 0.8, select="kv")
+    m = k["m"]
+    for b in range(2):
+        for g in range(2):
+            hs = range(3 * g, 3 * g + 3)
+            tot = sum(a["s_low"][b, h] for h in hs)
+            want = sorted(sorted(range(41), key=lambda t: (-tot[t], t))[:m])
+            for h in hs:
+                np.testing.assert_allclose(k["s_low"][b, h], tot, rtol=0, atol=1e-12)
+                assert list(k["sel"][b, h]) == want
+
+
 DECODE_CHECKS = [check_golden_decode, check_dense_reduction,
                  check_score_identities, check_selection_rule,
-                 check_closed_forms, check_gqa_mapping]
+                 check_closed_forms, check_gqa_mapping, check_kv_shared_selection]
 
 
 def check_select_topk(select, seed=26):

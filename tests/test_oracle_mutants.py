@@ -31,8 +31,8 @@ DECODE_MUTANTS = {
                        "s_high = (kc[S, :klow] * u[ki[S, :klow]])"),
     "floor_count": ("return max(1, min(T, -(-T * top_num // top_den)))",
                     "return max(1, min(T, T * top_num // top_den))"),
-    "ties_to_higher": ('order = np.argsort(-s_low, kind="stable")',
-                       'order = (T - 1 - np.argsort(-s_low[::-1], kind="stable"))'),
+    "ties_to_higher": ('order = np.argsort(-s_rank, kind="stable")',
+                       'order = (T - 1 - np.argsort(-s_rank[::-1], kind="stable"))'),
     "softmax_all_tokens": ("p = e / e.sum()",
                            "p = e / (e.sum() + np.exp(np.delete(s_low, S) - s_high.max()).sum())"),
     "no_scale": ("u = scale * (dk @ q[b, h])", "u = (dk @ q[b, h])"),
@@ -41,6 +41,11 @@ DECODE_MUTANTS = {
                           "w = np.bincount(vi[S][:, :khigh].ravel(), weights=(p[:, None] * vc[S][:, :khigh]).ravel(),"),
     "unweighted_values": ("weights=(p[:, None] * vc[S]).ravel()", "weights=(vc[S] / len(S)).ravel()"),
     "value_dict_is_key_dict": ('res["out"][b, h] = dv.T @ w', 'res["out"][b, h] = dk.T @ w'),
+    "kv_first_head_only": ("u_g = sum(scale * (dk @ q[b, hh]) for hh in range(g * G, (g + 1) * G))",
+                           "u_g = scale * (dk @ q[b, g * G])"),
+    "kv_strided_group": ("u_g = sum(scale * (dk @ q[b, hh]) for hh in range(g * G, (g + 1) * G))",
+                         "u_g = sum(scale * (dk @ q[b, hh]) for hh in range(g, Hq, Hkv))"),
+    "kv_own_score": ('s_rank = s_shared if select == "kv" else s_low', "s_rank = s_low"),
 }
 
 
