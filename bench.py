@@ -187,24 +187,28 @@ def bench_decode(args, torch, sd, synth, ev):
     torch.cuda.synchronize()
     stage_ms = [float(np.mean([ev.ms(e[j], e[j + 1]) for e in evs])) for j in range(nstage - 1)]
 
-    # the same step with the integer-only softmax (a flag of the same call)
-    icalls = [sd.DecodeCall(s["q"], s["dk"], s["dv"], s["kv"], None, klow=case.klow,
-                            khigh=case.khigh, top_num=case.top_num, top_den=case.top_den,
-                            scale=case.scale, key_low=s["kl"], out=out, workspace=ws,
-                            softmax="int")
-              for s in sets]
-    for i in range(args.warmup):
-        icalls[i % nsets].launch()
-    torch.cuda.synchronize()
-    ev.record(t0, stream.cuda_stream)
-    for i in range(args.steps):
-        icalls[i % nsets].launch()
-    ev.record(t1, stream.cuda_stream)
-    torch.cuda.synchronize()
-    ims = ev.ms(t0, t1) / args.steps
-    int_res = {"metric": "decode step with the integer-only softmax",
-               "us_per_step": round(ims * 1e3, 2), "value": round(B * T / (ims * 1e-3), 1),
-               "unit": "context-tokens/s", "relative_to_fp32_softmax_step": round(ims / ms, 3)}
+    # the same step with each attention flag of the same call
+    def time_variant(**flags):
+        vcalls = [sd.DecodeCall(s["q"], s["dk"], s["dv"], s["kv"], None, klow=case.klow,
+                                khigh=case.khigh, top_num=case.top_num, top_den=case.top_den,
+                                scale=case.scale, key_low=s["kl"], out=out, workspace=ws,
+                                **flags)
+                  for s in sets]
+        for i in range(args.warmup):
+            vcalls[i % nsets].launch()
+        torch.cuda.synchronize()
+        ev.record(t0, stream.cuda_stream)
+        for i in range(args.steps):
+            vcalls[i % nsets].launch()
+        ev.record(t1, stream.cuda_stream)
+        torch.cuda.synchronize()
+        vms = ev.ms(t0, t1) / args.steps
+        return {"us_per_step": round(vms * 1e3, 2), "value": round(B * T / (vms * 1e-3), 1),
+                "unit": "context-tokens/s", "relative_to_default_step": round(vms / ms, 3)}
+
+    int_res = {"metric": "decode step with the integer-only softmax", **time_variant(softmax="int")}
+    kv_res = {"metric": "decode step with the selection shared by each KV head's query heads",
+              **time_variant(select="kv")}
 
     # algorithmic bytes (HBM): what the method must read per step
     low_b = B * Hkv * T * case.klow * 4
@@ -230,7 +234,7 @@ def bench_decode(args, torch, sd, synth, ev):
               "frac": round(total_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         config=dict(B=B, Hq=Hq, Hkv=Hkv, T=T, d=d, n_atoms=N, K=K, klow=case.klow,
                     khigh=case.khigh, top="1/10", m=m, input_sets=nsets),
-        int_softmax=int_res, case=case)
+        int_softmax=int_res, shared_select=kv_res, case=case)
     return res
 
 
@@ -423,6 +427,7 @@ def main():
     app = bench_append(args, torch, sd, synth, ev, dec)
     log(f"  decode-step append (16 vectors): {app['us_per_step']:.1f} us")
     log(f"  integer-only softmax step: {dec['int_softmax']['us_per_step']:.1f} us")
+    log(f"  shared-selection step: {dec['shared_select']['us_per_step']:.1f} us")
     enc = None
     if not args.no_encode:
         log("encode benchmark (524,288 vectors)")
@@ -452,6 +457,7 @@ def main():
     }
     line["append"] = app
     line["int_softmax"] = dec["int_softmax"]
+    line["shared_select"] = dec["shared_select"]
     if enc is not None:
         line["encode"] = {
             "metric": "KV vectors encoded/s", "value": round(enc["value"], 1),

@@ -29,6 +29,8 @@ SDKV_ERR_UNSUPPORTED, SDKV_ERR_WORKSPACE, SDKV_ERR_DEVICE = 4, 5, 6
 SDKV_BF16, SDKV_F32 = 0, 1
 SDKV_SOFTMAX_FLOAT, SDKV_SOFTMAX_INT = 0, 1
 _SOFTMAX = {"float": SDKV_SOFTMAX_FLOAT, "int": SDKV_SOFTMAX_INT}
+SDKV_SELECT_HEAD, SDKV_SELECT_KV = 0, 1
+_SELECT = {"head": SDKV_SELECT_HEAD, "kv": SDKV_SELECT_KV}
 
 c_void_p, c_int32, c_int64, c_float = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
 c_size_t = ctypes.c_size_t
@@ -53,7 +55,7 @@ class AttnArgs(ctypes.Structure):
                 ("scale", c_float), ("out", c_void_p), ("u", c_void_p),
                 ("s_low", c_void_p), ("sel", c_void_p), ("s_high", c_void_p),
                 ("w", c_void_p), ("stage_events", c_void_p), ("softmax_mode", c_int32),
-                ("p_int", c_void_p)]
+                ("p_int", c_void_p), ("select_mode", c_int32)]
 
 
 class SdkvError(RuntimeError):
@@ -231,7 +233,7 @@ def sdkv_encode(x, dictionary, K: int, *, codes=None, coef_f32=None, resid_norm=
 
 def attn_args(q, dk, dv, key_codes, val_codes, klow, khigh, top_num, top_den, scale, out,
               key_low=None, u=None, s_low=None, sel=None, s_high=None, w=None,
-              softmax: str = "float", p_int=None) -> AttnArgs:
+              softmax: str = "float", p_int=None, select: str = "head") -> AttnArgs:
     B, Hq, d = q.shape
     if val_codes is None:
         # one tensor [B, Hkv, T, 2, K]: each token's key record, then its value record
@@ -250,7 +252,8 @@ def attn_args(q, dk, dv, key_codes, val_codes, klow, khigh, top_num, top_den, sc
                     top_num=top_num, top_den=top_den, scale=scale, out=_dev(out, "out"),
                     u=_dev(u, "u"), s_low=_dev(s_low, "s_low"), sel=_dev(sel, "sel"),
                     s_high=_dev(s_high, "s_high"), w=_dev(w, "w"),
-                    softmax_mode=_SOFTMAX[softmax], p_int=_dev(p_int, "p_int"))
+                    softmax_mode=_SOFTMAX[softmax], p_int=_dev(p_int, "p_int"),
+                    select_mode=_SELECT[select])
 
 
 def decode_attn_workspace_bytes(args: AttnArgs) -> int:
@@ -263,12 +266,15 @@ def decode_attn_workspace_bytes(args: AttnArgs) -> int:
 def sdkv_decode_attn(q, dk, dv, key_codes, val_codes, *, klow: int, khigh: int,
                      top_num: int = 1, top_den: int = 10, scale: Optional[float] = None,
                      key_low=None, out=None, debug: bool = False, softmax: str = "float",
+                     select: str = "head",
                      workspace: Optional[Workspace] = None, stream=None, stage_events=None):
     """Hierarchical coded decode attention. q [B,Hq,d] bf16; dk, dv
     [n_atoms,d] bf16/fp32; key_codes, val_codes int32 [B,Hkv,T,K], or
     key_codes int32 [B,Hkv,T,2,K] (each token's key record, then its value
     record) with val_codes=None; optional key_low int32 [B,Hkv,T,klow].
-    softmax="int" takes the integer-only softmax (SDKV_SOFTMAX_INT).
+    softmax="int" takes the integer-only softmax (SDKV_SOFTMAX_INT);
+    select="kv" shares each KV head's selection among its query heads
+    (SDKV_SELECT_KV).
     Returns out fp32 [B,Hq,d], or with debug=True a dict that also holds u,
     s_low, sel, s_high and w (and p_int in integer mode)."""
     torch = _torch()
@@ -291,7 +297,7 @@ def sdkv_decode_attn(q, dk, dv, key_codes, val_codes, *, klow: int, khigh: int,
         if softmax == "int":
             dbg["p_int"] = torch.empty((B, Hq, m), dtype=torch.int32, device=dev)
     a = attn_args(q, dk, dv, key_codes, val_codes, klow, khigh, top_num, top_den, scale, out,
-                  key_low=key_low, softmax=softmax, **dbg)
+                  key_low=key_low, softmax=softmax, select=select, **dbg)
     ev_keep, a.stage_events = _events(stage_events)
     wp, wn = _ws(workspace, decode_attn_workspace_bytes(a))
     _check(_lib().sdkv_decode_attn(ctypes.byref(a), ctypes.c_void_p(wp), wn, _stream(stream)),
@@ -380,7 +386,7 @@ class DecodeCall:
 
     def __init__(self, q, dk, dv, key_codes, val_codes, *, klow: int, khigh: int,
                  top_num: int = 1, top_den: int = 10, scale: Optional[float] = None,
-                 key_low=None, out=None, softmax: str = "float",
+                 key_low=None, out=None, softmax: str = "float", select: str = "head",
                  workspace: Optional[Workspace] = None, stream=None):
         torch = _torch()
         B, Hq, d = q.shape
@@ -391,7 +397,7 @@ class DecodeCall:
         self.out = out
         self._keep = (q, dk, dv, key_codes, val_codes, key_low, out)
         self.args = attn_args(q, dk, dv, key_codes, val_codes, klow, khigh, top_num, top_den,
-                              scale, out, key_low=key_low, softmax=softmax)
+                              scale, out, key_low=key_low, softmax=softmax, select=select)
         self.ws = workspace if workspace is not None else Workspace()
         wp, wn = _ws(self.ws, decode_attn_workspace_bytes(self.args))
         self._wsp, self._wsn = ctypes.c_void_p(wp), wn
@@ -479,7 +485,7 @@ def sdkv_select_topk(scores, k: int, *, idx_out=None, thr_out=None,
 
 
 __all__ = ["sdkv_encode", "sdkv_decode_attn", "sdkv_select_topk", "selected_count",
-           "SDKV_SOFTMAX_FLOAT", "SDKV_SOFTMAX_INT",
+           "SDKV_SOFTMAX_FLOAT", "SDKV_SOFTMAX_INT", "SDKV_SELECT_HEAD", "SDKV_SELECT_KV",
            "Workspace", "SdkvError", "lib", "LIB_PATH", "HEADER", "EncodeArgs", "AttnArgs",
            "sdkv_append_tokens", "sdkv_encode_pair",
            "attn_args", "decode_attn_workspace_bytes", "DecodeCall", "EncodeCall"]

@@ -86,6 +86,8 @@ static sdkv_status check_attn(const sdkv_attn_args* a) {
   if (!isfinite(a->scale)) return SDKV_ERR_SHAPE;
   if (a->softmax_mode != SDKV_SOFTMAX_FLOAT && a->softmax_mode != SDKV_SOFTMAX_INT)
     return SDKV_ERR_SHAPE;
+  if (a->select_mode != SDKV_SELECT_HEAD && a->select_mode != SDKV_SELECT_KV)
+    return SDKV_ERR_SHAPE;
   if (a->q_dtype != SDKV_BF16) return SDKV_ERR_UNSUPPORTED;
   if (a->n_atoms > kMaxAtomsDecode) return SDKV_ERR_UNSUPPORTED;
   if ((int64_t)a->B * a->Hq > 0x7FFFFFFF / 64) return SDKV_ERR_UNSUPPORTED;

@@ -82,6 +82,18 @@ __global__ __launch_bounds__(256) void k_utable_bf16(UArgs a) {
   }
 }
 
+// Group sums of U for the shared selection: Ug[r][a] = sum_{j<G} U[r G + j][a]
+// (query rows are (b, h) with h = g G + j, so group r = b Hkv + g), in j order.
+__global__ __launch_bounds__(256) void k_usum(const float* U, float* Ug, int64_t n, int N, int G) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int64_t r = i / N, at = i % N;
+  const float* src = U + r * G * N + at;
+  float s = src[0];
+  for (int j = 1; j < G; ++j) s += src[(int64_t)j * N];
+  Ug[i] = s;
+}
+
 // fp32 dictionary (small configurations): one thread per (row, atom).
 __global__ __launch_bounds__(256) void k_utable_f32(UArgs a) {
   clear_region(a);
@@ -125,6 +137,8 @@ struct RowsArgs {
   uint32_t* err;
   uint32_t* ticket;         // [8] workgroup start-order counters, zeroed per call
   int xcd_map;              // per-XCD ticket classes (rows stay on one XCD)
+  const float* Ug;          // [B * Hkv, N] group-summed U rows (shared selection)
+  int shared;               // selection shared by the query heads of a KV head
   int imode;                // integer-only softmax
   int32_t* p_int_out;       // optional [rows, m] integer probabilities
   uint32_t* ixchg;          // [rows, P, 4] integer-softmax exchange words
@@ -212,9 +226,9 @@ __device__ __forceinline__ void load_record(const uint32_t* rec, int K, int nw, 
 
 // U row of `row` into LDS. All loads are issued before the first store
 // (stores go to clamped indices: a duplicate store writes the same value).
-__device__ __forceinline__ void stage_u(const RowsArgs& a, int row, float* s_u) {
+__device__ __forceinline__ void stage_u(const RowsArgs& a, const float* src, float* s_u) {
   const int tid = threadIdx.x;
-  const float4* src4 = (const float4*)(a.U + (int64_t)row * a.N);
+  const float4* src4 = (const float4*)src;
   const int n4 = a.N >> 2;
   constexpr int UPT = kMaxAtomsDecode / 4 / SB;
   if (n4 > 0) {
@@ -224,7 +238,7 @@ __device__ __forceinline__ void stage_u(const RowsArgs& a, int row, float* s_u) 
 #pragma unroll
     for (int k = 0; k < UPT; ++k) ((float4*)s_u)[min(tid + k * SB, n4 - 1)] = ub[k];
   }
-  for (int i = (n4 << 2) + tid; i < a.N; i += SB) s_u[i] = a.U[(int64_t)row * a.N + i];
+  for (int i = (n4 << 2) + tid; i < a.N; i += SB) s_u[i] = src[i];
 }
 
 // U row staging and low scores of a chunk for records of 16 words whose
@@ -233,7 +247,7 @@ __device__ __forceinline__ void stage_u(const RowsArgs& a, int row, float* s_u) 
 // next batch is requested before the current one is scored). LOW3: klow == 3,
 // each token's three words are one 12-byte load.
 template <int SPT, bool LOW3>
-__device__ __forceinline__ void score_chunk(const RowsArgs& a, int row, const uint32_t* lo,
+__device__ __forceinline__ void score_chunk(const RowsArgs& a, const float* usrc, const uint32_t* lo,
                                             int64_t t0, int64_t t1, float* s_u,
                                             uint32_t (&key)[SPT]) {
   const int tid = threadIdx.x;
@@ -258,7 +272,7 @@ __device__ __forceinline__ void score_chunk(const RowsArgs& a, int row, const ui
     }
   };
   load_batch(0, wb[0]);
-  stage_u(a, row, s_u);
+  stage_u(a, usrc, s_u);
   __syncthreads();
   const int nk = LOW3 ? 3 : a.klow;
 #pragma unroll
@@ -277,9 +291,9 @@ __device__ __forceinline__ void score_chunk(const RowsArgs& a, int row, const ui
   }
 }
 
-// IM: the integer-only softmax (a separate build, so the fp32 kernel keeps
-// its registers).
-template <int SPT, bool FAST, bool IM>
+// IM: the integer-only softmax; SH: the selection shared by a KV head's query
+// heads (separate builds, so the default kernel keeps its registers).
+template <int SPT, bool FAST, bool IM, bool SH>
 __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   __shared__ float s_u[kMaxAtomsDecode];
   __shared__ SelShared sh;
@@ -310,11 +324,13 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   const int lw = a.low_words;
   const bool low3 = FAST && a.klow == 3;
   uint32_t key[SPT];
+  // the ranking table: this head's U row, or its group's summed row
+  const float* usrc = SH ? a.Ug + kv * a.N : a.U + (int64_t)row * a.N;
   if (FAST) {
-    if (low3) score_chunk<SPT, true>(a, row, lo, t0, t1, s_u, key);
-    else score_chunk<SPT, false>(a, row, lo, t0, t1, s_u, key);
+    if (low3) score_chunk<SPT, true>(a, usrc, lo, t0, t1, s_u, key);
+    else score_chunk<SPT, false>(a, usrc, lo, t0, t1, s_u, key);
   } else {
-    stage_u(a, row, s_u);
+    stage_u(a, usrc, s_u);
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < SPT; ++j) {
@@ -438,6 +454,13 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   }
   int32_t* sel_dbg = a.sel_out ? a.sel_out + (int64_t)row * a.m : nullptr;
   float* sh_dbg = a.s_high_out ? a.s_high_out + (int64_t)row * a.m : nullptr;
+
+  // shared selection: the rescore needs this head's own U row
+  if constexpr (SH) {
+    __syncthreads();
+    stage_u(a, a.U + (int64_t)row * a.N, s_u);
+    __syncthreads();
+  }
 
   // 5. Khigh rescore, one thread per selected token (entries i = tid + k*SB;
   // the same thread handles the same entries in every later loop). Value
@@ -1030,16 +1053,23 @@ sdkv_status plan_decode(const sdkv_attn_args* a, DecodePlan* p) {
   q.off_cand = off;   off = align_up(off + (q.P > 1 ? (size_t)rows * q.P * q.chunk * 4 : 0), A);
   q.off_wtab = off;   off = align_up(off + (q.P > 1 ? (size_t)rows * q.P * 2048 * 4 : 0), A);
   q.off_ixchg = off;  off = align_up(off + (size_t)rows * q.P * 4 * 4, A);
+  q.off_ug = off;     off = align_up(off + (a->select_mode == SDKV_SELECT_KV
+                                            ? (size_t)a->B * a->Hkv * N * 4 : 0), A);
   q.total = off;
   *p = q;
   return SDKV_OK;
 }
 
-static const void* pick_rows_kernel(int spt, bool fast, bool im) {
-#define SDKV_PICK(S)                                                                        \
-  if (spt == S) {                                                                           \
-    if (im) return fast ? (const void*)&k_rows<S, true, true> : (const void*)&k_rows<S, false, true>; \
-    return fast ? (const void*)&k_rows<S, true, false> : (const void*)&k_rows<S, false, false>; \
+template <int S, bool IM, bool SH>
+static const void* rows_kernel(bool fast) {
+  return fast ? (const void*)&k_rows<S, true, IM, SH> : (const void*)&k_rows<S, false, IM, SH>;
+}
+
+static const void* pick_rows_kernel(int spt, bool fast, bool im, bool sh) {
+#define SDKV_PICK(S)                                         \
+  if (spt == S) {                                            \
+    if (im) return sh ? rows_kernel<S, true, true>(fast) : rows_kernel<S, true, false>(fast); \
+    return sh ? rows_kernel<S, false, true>(fast) : rows_kernel<S, false, false>(fast);       \
   }
   SDKV_PICK(4)
   SDKV_PICK(8)
@@ -1088,6 +1118,14 @@ sdkv_status launch_decode(const sdkv_attn_args* a, const DecodePlan& p, void* ws
   }
   if (hipGetLastError() != hipSuccess) return SDKV_ERR_DEVICE;
 
+  // shared selection: the group sums of U
+  if (a->select_mode == SDKV_SELECT_KV) {
+    const int64_t n = (int64_t)a->B * a->Hkv * a->n_atoms;
+    hipLaunchKernelGGL(k_usum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, U,
+                       (float*)(base + p.off_ug), n, a->n_atoms, a->Hq / a->Hkv);
+    if (hipGetLastError() != hipSuccess) return SDKV_ERR_DEVICE;
+  }
+
   // 2. row kernel, in row batches that fit co-resident when cooperative
   RowsArgs ra;
   ra.U = U;
@@ -1120,12 +1158,14 @@ sdkv_status launch_decode(const sdkv_attn_args* a, const DecodePlan& p, void* ws
   ra.xchg = xchg;
   ra.bar = bar;
   ra.err = err;
+  ra.shared = a->select_mode == SDKV_SELECT_KV ? 1 : 0;
+  ra.Ug = (const float*)(base + p.off_ug);
   ra.imode = a->softmax_mode == SDKV_SOFTMAX_INT ? 1 : 0;
   ra.p_int_out = ra.imode ? a->p_int : nullptr;
   ra.ixchg = (uint32_t*)(base + p.off_ixchg);
   const bool aligned = (((uintptr_t)a->key_codes | (uintptr_t)a->val_codes) & 15u) == 0 &&
                        ra.rs % 4 == 0;
-  const void* kfn = pick_rows_kernel(p.spt, p.fast && aligned, ra.imode != 0);
+  const void* kfn = pick_rows_kernel(p.spt, p.fast && aligned, ra.imode != 0, ra.shared != 0);
   if (!kfn) return SDKV_ERR_UNSUPPORTED;
   ra.ticket = (uint32_t*)(base + p.off_ticket);
   // Per-XCD ticket classes need whole rows per class; with P > 1 every

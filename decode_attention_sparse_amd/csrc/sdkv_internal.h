@@ -41,7 +41,7 @@ struct DecodePlan {
   size_t off_u = 0, off_sel = 0, off_shigh = 0, off_wpart = 0, off_stats = 0;
   size_t off_zero = 0, zero_bytes = 0;  // [ghist | xchg | bar | err], cleared per call
   size_t off_ghist = 0, off_xchg = 0, off_bar = 0, off_err = 0, off_opart = 0;
-  size_t off_cand = 0, off_ticket = 0, off_wtab = 0, off_ixchg = 0;
+  size_t off_cand = 0, off_ticket = 0, off_wtab = 0, off_ixchg = 0, off_ug = 0;
   size_t total = 0;
 };
 

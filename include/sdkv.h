@@ -48,7 +48,7 @@ extern "C" {
 #define SDKV_API
 #endif
 
-#define SDKV_ABI_VERSION 4
+#define SDKV_ABI_VERSION 5
 
 typedef int32_t sdkv_status;
 #define SDKV_OK 0
@@ -201,10 +201,23 @@ typedef struct sdkv_attn_args {
   int32_t softmax_mode;
   int32_t* p_int;       /* OUT [B, Hq, m] integer p_t aligned with sel
                            (SDKV_SOFTMAX_INT only), or NULL               */
+  /* Selection granularity under grouped-query attention (review page,
+     Summary: the selection is query-aware; the pages are silent on GQA):
+       SDKV_SELECT_HEAD (0): every query head ranks the tokens by its own
+         s_low, as above.
+       SDKV_SELECT_KV   (1): the G = Hq/Hkv query heads of a KV head share
+         one selection, ranked by their summed low score
+         sum_{j<klow} kappa_tj U_g[i_tj], U_g = sum_{h in g} u_h (fp32, h
+         ascending); s_high, the softmax and w stay per head. The s_low
+         debug output then holds that shared score for every head.
+       Other values: SDKV_ERR_SHAPE.                                      */
+  int32_t select_mode;
 } sdkv_attn_args;
 #define SDKV_DECODE_STAGES 4
 #define SDKV_SOFTMAX_FLOAT 0
 #define SDKV_SOFTMAX_INT 1
+#define SDKV_SELECT_HEAD 0
+#define SDKV_SELECT_KV 1
 
 /* m = ceil(T * top_num / top_den), clamped to [1, T]; 0 on bad input. */
 SDKV_API int64_t sdkv_selected_count(int64_t T, int64_t top_num, int64_t top_den);

@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) == 11, names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.sdkv_abi_version() == 4
+    assert lib.sdkv_abi_version() == 5
 
 
 def test_status_strings():
@@ -80,6 +80,7 @@ def test_decode_workspace_query():
     ("code_stride", 15, sd.SDKV_ERR_SHAPE), ("code_stride", -32, sd.SDKV_ERR_SHAPE),
     ("code_stride", 65537, sd.SDKV_ERR_SHAPE),
     ("softmax_mode", 2, sd.SDKV_ERR_SHAPE), ("softmax_mode", -1, sd.SDKV_ERR_SHAPE),
+    ("select_mode", 2, sd.SDKV_ERR_SHAPE), ("select_mode", -1, sd.SDKV_ERR_SHAPE),
 ])
 def test_decode_validation(field, value, status):
     a = good_attn(**{field: value})
@@ -215,3 +216,10 @@ def test_misaligned_pointers_rejected():
     at = good_attn()
     _, anb = ws_status(at)
     assert lib.sdkv_decode_attn(ctypes.byref(at), ctypes.c_void_p(FAKE + 4), anb, None) == sd.SDKV_ERR_UNSUPPORTED
+
+
+def test_decode_workspace_shared_selection():
+    # the shared selection adds the group-summed U rows: B * Hkv * n_atoms floats
+    st, nb = ws_status(good_attn())
+    st2, nb2 = ws_status(good_attn(select_mode=sd.SDKV_SELECT_KV))
+    assert st == st2 == 0 and nb2 - nb == 8 * 32768 * 4
