@@ -115,7 +115,7 @@ def select_topk(scores: np.ndarray, k: int) -> np.ndarray:
 
 def decode_attn(q, dk, dv, key_codes, val_codes, klow: int, khigh: int,
                 top_num: int, top_den: int, scale: float, sel=None, softmax: str = "float",
-                s_high_in=None, select: str = "head"):
+                s_high_in=None, select: str = "head", reading: str = "A"):
     """Hierarchical coded decode attention for one layer.
 
     Review page, Summary: every token is scored from its first Klow atoms
@@ -162,6 +162,17 @@ def decode_attn(q, dk, dv, key_codes, val_codes, klow: int, khigh: int,
     group's summed query). In this mode res["s_low"] holds that shared
     ranking score for every head of the group.
 
+    reading="B" lets every token into the softmax (the pages' other
+    reading of "scores all tokens at Klow=3 and refines the top 10%":
+    review page, Summary; FAQ): a selected token enters with s_high and all
+    K value pairs, every other token with its own head's s_low and its first
+    klow value pairs,
+        p = softmax over all T of (s_high on S, s_low elsewhere)
+        w[a] = sum_{t in S} p_t sum_{j<K} kappa^v_tj [i^v_tj == a]
+             + sum_{t not in S} p_t sum_{j<klow} kappa^v_tj [i^v_tj == a].
+    res["p"] keeps the selected tokens' probabilities. Reading B with the
+    integer softmax is not defined here (nor in the library).
+
     Returns a dict of float64 arrays: u [B,Hq,N], s_low [B,Hq,T],
     sel int64 [B,Hq,m] ascending, s_high [B,Hq,m], p [B,Hq,m],
     w [B,Hq,N], out [B,Hq,d], and m.
@@ -189,6 +200,8 @@ def decode_attn(q, dk, dv, key_codes, val_codes, klow: int, khigh: int,
         raise ValueError(softmax)
     if select not in ("head", "kv"):
         raise ValueError(select)
+    if reading not in ("A", "B") or (reading == "B" and softmax == "int"):
+        raise ValueError((reading, softmax))
     for b in range(B):
         for g in range(Hkv):
             ki, kc = unpack_codes(key_codes[b, g])
@@ -212,11 +225,22 @@ def decode_attn(q, dk, dv, key_codes, val_codes, klow: int, khigh: int,
                     pi = int_softmax(s32)
                     res["p_int"][b, h] = pi
                     p = pi.astype(np.float64) / 2.0 ** INT_SOFTMAX_P_BITS
+                elif reading == "B":
+                    rest = np.setdiff1d(np.arange(T), S)
+                    s_all = np.concatenate([s_high, s_low[rest]])
+                    e = np.exp(s_all - s_all.max())
+                    p_all = e / e.sum()
+                    p = p_all[:S.size]
+                    p_rest = p_all[S.size:]
                 else:
                     e = np.exp(s_high - s_high.max())
                     p = e / e.sum()
                 w = np.bincount(vi[S].ravel(), weights=(p[:, None] * vc[S]).ravel(),
                                 minlength=N)
+                if reading == "B":
+                    w = w + np.bincount(vi[rest, :klow].ravel(),
+                                        weights=(p_rest[:, None] * vc[rest, :klow]).ravel(),
+                                        minlength=N)
                 res["u"][b, h] = u
                 res["s_low"][b, h] = s_rank
                 res["sel"][b, h] = S

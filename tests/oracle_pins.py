@@ -380,9 +380,46 @@ def check_kv_shared_selection(decode, seed=27):
                 assert list(k["sel"][b, h]) == want
 
 
+def _textbook(q, Kt, Vt, scale):
+    logits = [scale * math.fsum(Kt[t] * q) for t in range(Kt.shape[0])]
+    mx = max(logits)
+    e = [math.exp(l - mx) for l in logits]
+    z = math.fsum(e)
+    return sum((e[t] / z) * Vt[t] for t in range(len(e)))
+
+
+def check_reading_b(decode, seed=28):
+    """reading="B" (every token in the softmax): (a) with the top fraction at
+    100% it equals reading A; (b) with Klow = Khigh = K it is textbook
+    attention over all T tokens' explicit reconstructions, whatever m is;
+    (c) in general it is textbook attention over per-token keys and values
+    built from K pairs for the selected tokens and Klow pairs for the rest
+    (reconstructed with plain loops)."""
+    q, dk, dv, kc, vc = small_decode_inputs(seed, Hq=2, Hkv=1, T=23, K=4)
+    a = decode(q, dk, dv, kc, vc, 2, 3, 1, 1, 0.6)
+    r = decode(q, dk, dv, kc, vc, 2, 3, 1, 1, 0.6, reading="B")
+    np.testing.assert_allclose(r["out"], a["out"], rtol=0, atol=1e-14)
+    K = kc.shape[-1]
+    r = decode(q, dk, dv, kc, vc, K, K, 1, 5, 0.6, reading="B")
+    for h in range(2):
+        o = _textbook(q[0, h], reconstruct(kc[0, 0], dk, K), reconstruct(vc[0, 0], dv, K), 0.6)
+        np.testing.assert_allclose(r["out"][0, h], o, rtol=1e-10, atol=1e-12)
+    klow, khigh = 2, 3
+    r = decode(q, dk, dv, kc, vc, klow, khigh, 2, 7, 0.6, reading="B")
+    for h in range(2):
+        S = set(int(t) for t in r["sel"][0, h])
+        Kl, Kh = reconstruct(kc[0, 0], dk, klow), reconstruct(kc[0, 0], dk, khigh)
+        Vl, Vf = reconstruct(vc[0, 0], dv, klow), reconstruct(vc[0, 0], dv, K)
+        Kt = np.array([Kh[t] if t in S else Kl[t] for t in range(23)])
+        Vt = np.array([Vf[t] if t in S else Vl[t] for t in range(23)])
+        np.testing.assert_allclose(r["out"][0, h], _textbook(q[0, h], Kt, Vt, 0.6),
+                                   rtol=1e-10, atol=1e-12)
+
+
 DECODE_CHECKS = [check_golden_decode, check_dense_reduction,
                  check_score_identities, check_selection_rule,
-                 check_closed_forms, check_gqa_mapping, check_kv_shared_selection]
+                 check_closed_forms, check_gqa_mapping, check_kv_shared_selection,
+                 check_reading_b]
 
 
 def check_select_topk(select, seed=26):

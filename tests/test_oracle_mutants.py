@@ -46,6 +46,11 @@ DECODE_MUTANTS = {
     "kv_strided_group": ("u_g = sum(scale * (dk @ q[b, hh]) for hh in range(g * G, (g + 1) * G))",
                          "u_g = sum(scale * (dk @ q[b, hh]) for hh in range(g, Hq, Hkv))"),
     "kv_own_score": ('s_rank = s_shared if select == "kv" else s_low', "s_rank = s_low"),
+    "b_rest_scored_high": ("s_all = np.concatenate([s_high, s_low[rest]])",
+                           "s_all = np.concatenate([s_high, (kc[rest, :khigh] * u[ki[rest, :khigh]]).sum(axis=1)])"),
+    "b_rest_full_values": ("w = w + np.bincount(vi[rest, :klow].ravel(),\n                                        weights=(p_rest[:, None] * vc[rest, :klow]).ravel(),",
+                           "w = w + np.bincount(vi[rest].ravel(),\n                                        weights=(p_rest[:, None] * vc[rest]).ravel(),"),
+    "b_rest_outside_normaliser": ("p_all = e / e.sum()", "p_all = e / e[:S.size].sum()"),
 }
 
 
