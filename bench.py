@@ -150,7 +150,9 @@ def bench_decode(args, torch, sd, synth, ev):
                 dv=torch.from_numpy(case.dv).to(dev).to(torch.bfloat16),
                 # each token's key record, then its value record: [B, Hkv, T, 2, K]
                 kv=up_words(np.stack([case.key_codes, case.val_codes], axis=3)),
-                kl=up_words(case.key_low))
+                kl=up_words(case.key_low),
+                # reading B's value low plane (first klow value words)
+                vl=up_words(np.ascontiguousarray(case.val_codes[..., :case.klow])))
     set_bytes = sum(t.numel() * t.element_size() for t in base.values())
     nsets = max(2, int(np.ceil(600e6 / set_bytes)))
     sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(nsets - 1)]
@@ -188,11 +190,11 @@ def bench_decode(args, torch, sd, synth, ev):
     stage_ms = [float(np.mean([ev.ms(e[j], e[j + 1]) for e in evs])) for j in range(nstage - 1)]
 
     # the same step with each attention flag of the same call
-    def time_variant(**flags):
+    def time_variant(per_set=lambda s: {}, **flags):
         vcalls = [sd.DecodeCall(s["q"], s["dk"], s["dv"], s["kv"], None, klow=case.klow,
                                 khigh=case.khigh, top_num=case.top_num, top_den=case.top_den,
                                 scale=case.scale, key_low=s["kl"], out=out, workspace=ws,
-                                **flags)
+                                **flags, **per_set(s))
                   for s in sets]
         for i in range(args.warmup):
             vcalls[i % nsets].launch()
@@ -209,6 +211,9 @@ def bench_decode(args, torch, sd, synth, ev):
     int_res = {"metric": "decode step with the integer-only softmax", **time_variant(softmax="int")}
     kv_res = {"metric": "decode step with the selection shared by each KV head's query heads",
               **time_variant(select="kv")}
+    b_res = {"metric": "decode step, reading B (every token in the softmax; Klow values "
+                       "outside the selection)",
+             **time_variant(per_set=lambda s: {"val_low": s["vl"]}, reading="B")}
 
     # algorithmic bytes (HBM): what the method must read per step
     low_b = B * Hkv * T * case.klow * 4
@@ -234,7 +239,7 @@ def bench_decode(args, torch, sd, synth, ev):
               "frac": round(total_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         config=dict(B=B, Hq=Hq, Hkv=Hkv, T=T, d=d, n_atoms=N, K=K, klow=case.klow,
                     khigh=case.khigh, top="1/10", m=m, input_sets=nsets),
-        int_softmax=int_res, shared_select=kv_res, case=case)
+        int_softmax=int_res, shared_select=kv_res, reading_b=b_res, case=case)
     return res
 
 
@@ -428,6 +433,7 @@ def main():
     log(f"  decode-step append (16 vectors): {app['us_per_step']:.1f} us")
     log(f"  integer-only softmax step: {dec['int_softmax']['us_per_step']:.1f} us")
     log(f"  shared-selection step: {dec['shared_select']['us_per_step']:.1f} us")
+    log(f"  reading-B step: {dec['reading_b']['us_per_step']:.1f} us")
     enc = None
     if not args.no_encode:
         log("encode benchmark (524,288 vectors)")
@@ -458,6 +464,7 @@ def main():
     line["append"] = app
     line["int_softmax"] = dec["int_softmax"]
     line["shared_select"] = dec["shared_select"]
+    line["reading_b"] = dec["reading_b"]
     if enc is not None:
         line["encode"] = {
             "metric": "KV vectors encoded/s", "value": round(enc["value"], 1),

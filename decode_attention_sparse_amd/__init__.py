@@ -31,6 +31,8 @@ SDKV_SOFTMAX_FLOAT, SDKV_SOFTMAX_INT = 0, 1
 _SOFTMAX = {"float": SDKV_SOFTMAX_FLOAT, "int": SDKV_SOFTMAX_INT}
 SDKV_SELECT_HEAD, SDKV_SELECT_KV = 0, 1
 _SELECT = {"head": SDKV_SELECT_HEAD, "kv": SDKV_SELECT_KV}
+SDKV_READING_A, SDKV_READING_B = 0, 1
+_READING = {"A": SDKV_READING_A, "B": SDKV_READING_B}
 
 c_void_p, c_int32, c_int64, c_float = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
 c_size_t = ctypes.c_size_t
@@ -55,7 +57,8 @@ class AttnArgs(ctypes.Structure):
                 ("scale", c_float), ("out", c_void_p), ("u", c_void_p),
                 ("s_low", c_void_p), ("sel", c_void_p), ("s_high", c_void_p),
                 ("w", c_void_p), ("stage_events", c_void_p), ("softmax_mode", c_int32),
-                ("p_int", c_void_p), ("select_mode", c_int32)]
+                ("p_int", c_void_p), ("select_mode", c_int32), ("reading", c_int32),
+                ("val_low", c_void_p)]
 
 
 class SdkvError(RuntimeError):
@@ -233,7 +236,8 @@ def sdkv_encode(x, dictionary, K: int, *, codes=None, coef_f32=None, resid_norm=
 
 def attn_args(q, dk, dv, key_codes, val_codes, klow, khigh, top_num, top_den, scale, out,
               key_low=None, u=None, s_low=None, sel=None, s_high=None, w=None,
-              softmax: str = "float", p_int=None, select: str = "head") -> AttnArgs:
+              softmax: str = "float", p_int=None, select: str = "head", reading: str = "A",
+              val_low=None) -> AttnArgs:
     B, Hq, d = q.shape
     if val_codes is None:
         # one tensor [B, Hkv, T, 2, K]: each token's key record, then its value record
@@ -253,7 +257,8 @@ def attn_args(q, dk, dv, key_codes, val_codes, klow, khigh, top_num, top_den, sc
                     u=_dev(u, "u"), s_low=_dev(s_low, "s_low"), sel=_dev(sel, "sel"),
                     s_high=_dev(s_high, "s_high"), w=_dev(w, "w"),
                     softmax_mode=_SOFTMAX[softmax], p_int=_dev(p_int, "p_int"),
-                    select_mode=_SELECT[select])
+                    select_mode=_SELECT[select], reading=_READING[reading],
+                    val_low=_dev(val_low, "val_low"))
 
 
 def decode_attn_workspace_bytes(args: AttnArgs) -> int:
@@ -266,7 +271,7 @@ def decode_attn_workspace_bytes(args: AttnArgs) -> int:
 def sdkv_decode_attn(q, dk, dv, key_codes, val_codes, *, klow: int, khigh: int,
                      top_num: int = 1, top_den: int = 10, scale: Optional[float] = None,
                      key_low=None, out=None, debug: bool = False, softmax: str = "float",
-                     select: str = "head",
+                     select: str = "head", reading: str = "A", val_low=None,
                      workspace: Optional[Workspace] = None, stream=None, stage_events=None):
     """Hierarchical coded decode attention. q [B,Hq,d] bf16; dk, dv
     [n_atoms,d] bf16/fp32; key_codes, val_codes int32 [B,Hkv,T,K], or
@@ -274,7 +279,9 @@ def sdkv_decode_attn(q, dk, dv, key_codes, val_codes, *, klow: int, khigh: int,
     record) with val_codes=None; optional key_low int32 [B,Hkv,T,klow].
     softmax="int" takes the integer-only softmax (SDKV_SOFTMAX_INT);
     select="kv" shares each KV head's selection among its query heads
-    (SDKV_SELECT_KV).
+    (SDKV_SELECT_KV); reading="B" lets every token into the softmax
+    (SDKV_READING_B), with val_low int32 [B,Hkv,T,klow] the first klow
+    value words (optional).
     Returns out fp32 [B,Hq,d], or with debug=True a dict that also holds u,
     s_low, sel, s_high and w (and p_int in integer mode)."""
     torch = _torch()
@@ -297,7 +304,8 @@ def sdkv_decode_attn(q, dk, dv, key_codes, val_codes, *, klow: int, khigh: int,
         if softmax == "int":
             dbg["p_int"] = torch.empty((B, Hq, m), dtype=torch.int32, device=dev)
     a = attn_args(q, dk, dv, key_codes, val_codes, klow, khigh, top_num, top_den, scale, out,
-                  key_low=key_low, softmax=softmax, select=select, **dbg)
+                  key_low=key_low, softmax=softmax, select=select, reading=reading,
+                  val_low=val_low, **dbg)
     ev_keep, a.stage_events = _events(stage_events)
     wp, wn = _ws(workspace, decode_attn_workspace_bytes(a))
     _check(_lib().sdkv_decode_attn(ctypes.byref(a), ctypes.c_void_p(wp), wn, _stream(stream)),
@@ -387,6 +395,7 @@ class DecodeCall:
     def __init__(self, q, dk, dv, key_codes, val_codes, *, klow: int, khigh: int,
                  top_num: int = 1, top_den: int = 10, scale: Optional[float] = None,
                  key_low=None, out=None, softmax: str = "float", select: str = "head",
+                 reading: str = "A", val_low=None,
                  workspace: Optional[Workspace] = None, stream=None):
         torch = _torch()
         B, Hq, d = q.shape
@@ -395,9 +404,10 @@ class DecodeCall:
         if out is None:
             out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
         self.out = out
-        self._keep = (q, dk, dv, key_codes, val_codes, key_low, out)
+        self._keep = (q, dk, dv, key_codes, val_codes, key_low, val_low, out)
         self.args = attn_args(q, dk, dv, key_codes, val_codes, klow, khigh, top_num, top_den,
-                              scale, out, key_low=key_low, softmax=softmax, select=select)
+                              scale, out, key_low=key_low, softmax=softmax, select=select,
+                              reading=reading, val_low=val_low)
         self.ws = workspace if workspace is not None else Workspace()
         wp, wn = _ws(self.ws, decode_attn_workspace_bytes(self.args))
         self._wsp, self._wsn = ctypes.c_void_p(wp), wn
@@ -486,6 +496,7 @@ def sdkv_select_topk(scores, k: int, *, idx_out=None, thr_out=None,
 
 __all__ = ["sdkv_encode", "sdkv_decode_attn", "sdkv_select_topk", "selected_count",
            "SDKV_SOFTMAX_FLOAT", "SDKV_SOFTMAX_INT", "SDKV_SELECT_HEAD", "SDKV_SELECT_KV",
+           "SDKV_READING_A", "SDKV_READING_B",
            "Workspace", "SdkvError", "lib", "LIB_PATH", "HEADER", "EncodeArgs", "AttnArgs",
            "sdkv_append_tokens", "sdkv_encode_pair",
            "attn_args", "decode_attn_workspace_bytes", "DecodeCall", "EncodeCall"]

@@ -88,10 +88,13 @@ static sdkv_status check_attn(const sdkv_attn_args* a) {
     return SDKV_ERR_SHAPE;
   if (a->select_mode != SDKV_SELECT_HEAD && a->select_mode != SDKV_SELECT_KV)
     return SDKV_ERR_SHAPE;
+  if (a->reading != SDKV_READING_A && a->reading != SDKV_READING_B) return SDKV_ERR_SHAPE;
   if (a->q_dtype != SDKV_BF16) return SDKV_ERR_UNSUPPORTED;
   if (a->n_atoms > kMaxAtomsDecode) return SDKV_ERR_UNSUPPORTED;
   if ((int64_t)a->B * a->Hq > 0x7FFFFFFF / 64) return SDKV_ERR_UNSUPPORTED;
   if (!aligned16(a->q) || !aligned16(a->dk) || !aligned16(a->dv)) return SDKV_ERR_UNSUPPORTED;
+  if (a->reading == SDKV_READING_B && a->softmax_mode != SDKV_SOFTMAX_FLOAT)
+    return SDKV_ERR_UNSUPPORTED;
   return SDKV_OK;
 }
 

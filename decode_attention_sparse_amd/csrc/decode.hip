@@ -139,6 +139,8 @@ struct RowsArgs {
   int xcd_map;              // per-XCD ticket classes (rows stay on one XCD)
   const float* Ug;          // [B * Hkv, N] group-summed U rows (shared selection)
   int shared;               // selection shared by the query heads of a KV head
+  int readb;                // reading B: every token enters the softmax
+  const uint32_t* vlow;     // optional [B, Hkv, T, klow] value low plane (reading B)
   int imode;                // integer-only softmax
   int32_t* p_int_out;       // optional [rows, m] integer probabilities
   uint32_t* ixchg;          // [rows, P, 4] integer-softmax exchange words
@@ -291,9 +293,10 @@ __device__ __forceinline__ void score_chunk(const RowsArgs& a, const float* usrc
   }
 }
 
-// IM: the integer-only softmax; SH: the selection shared by a KV head's query
-// heads (separate builds, so the default kernel keeps its registers).
-template <int SPT, bool FAST, bool IM, bool SH>
+// EXT: the build that takes the attention flags (integer-only softmax, the
+// selection shared by a KV head's query heads, reading B) from its arguments;
+// the default build has them all off at compile time and keeps its registers.
+template <int SPT, bool FAST, bool EXT>
 __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   __shared__ float s_u[kMaxAtomsDecode];
   __shared__ SelShared sh;
@@ -325,7 +328,8 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   const bool low3 = FAST && a.klow == 3;
   uint32_t key[SPT];
   // the ranking table: this head's U row, or its group's summed row
-  const float* usrc = SH ? a.Ug + kv * a.N : a.U + (int64_t)row * a.N;
+  const bool im = EXT && a.imode, sh_sel = EXT && a.shared, rb = EXT && a.readb;
+  const float* usrc = sh_sel ? a.Ug + kv * a.N : a.U + (int64_t)row * a.N;
   if (FAST) {
     if (low3) score_chunk<SPT, true>(a, usrc, lo, t0, t1, s_u, key);
     else score_chunk<SPT, false>(a, usrc, lo, t0, t1, s_u, key);
@@ -456,7 +460,7 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   float* sh_dbg = a.s_high_out ? a.s_high_out + (int64_t)row * a.m : nullptr;
 
   // shared selection: the rescore needs this head's own U row
-  if constexpr (SH) {
+  if (sh_sel) {
     __syncthreads();
     stage_u(a, a.U + (int64_t)row * a.N, s_u);
     __syncthreads();
@@ -506,10 +510,40 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
       if (i < cnt) {
         if (in_lds) s_ls[i] = s;
         else sh_g[i] = s;
-        if constexpr (IM) {
+        if (im) {
           lmin = fminf(lmin, s);
           vmax = fmaxf(vmax, va);
         }
+        if (s > lmax) {
+          vb = vb * __expf(lmax - s) + va;
+          lmax = s;
+        } else {
+          vb += __expf(s - lmax) * va;
+        }
+      }
+    }
+  }
+  // reading B: this workgroup's unselected tokens enter with their s_low and
+  // their first klow value words (value low plane, else the value records)
+  const uint32_t* vlo = a.vlow ? a.vlow + kv * a.T * a.klow : vbase;
+  const int64_t vlw = a.vlow ? a.klow : a.rs;
+  if (rb) {
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) {
+      const int64_t t = t0 + (int64_t)j * SB + tid;
+      if (t < t1 && !((sel >> j) & 1u)) {
+        float s = key_float(key[j]);
+        if (sh_sel) {
+          // the key holds the group's ranking score: this head's own s_low
+          // (U_h is staged again by now), kept in the key for the weights
+          const uint32_t* wp = lo + t * lw;
+          s = 0.f;
+          for (int c = 0; c < a.klow; ++c) s = fmaf(code_coef(wp[c]), s_u[code_idx(wp[c]) & AMASK], s);
+          key[j] = float_key(s);
+        }
+        const uint32_t* vp = vlo + t * vlw;
+        float va = 0.f;
+        for (int c = 0; c < a.klow; ++c) va += fabsf(code_coef(vp[c]));
         if (s > lmax) {
           vb = vb * __expf(lmax - s) + va;
           lmax = s;
@@ -543,7 +577,7 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   // exponential e' (stored over its score), the row's sum of e' and the
   // 62-bit reciprocal. Two exchanges among the row's workgroups.
   uint64_t rcp = 0;
-  if constexpr (IM) {
+  if (im) {
     const float mn = -block_max<SNW>(-lmin, s_red);
     float smax = M, smin = mn;
     uint32_t* ix = a.ixchg + (int64_t)row * a.P * 4;
@@ -603,7 +637,7 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   // fixed-point scale bound: sum_t p_t sum_j |kappa^v_tj| <= the largest sum
   // when the p_t sum to at most 1 (integer mode)
   float vbound = vsum;
-  if constexpr (IM) vbound = block_max<SNW>(vmax, s_red) * 1.0001f;
+  if (im) vbound = block_max<SNW>(vmax, s_red) * 1.0001f;
 
   // 6. softmax weights and per-atom value weights. LDS integer atomics are
   // much faster than float ones on gfx950, so weights accumulate in int32
@@ -640,7 +674,7 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
     for (int r = 0; r < kTokBatch; ++r) {
       const int64_t i = base + (int64_t)r * SB + tid;
       if (i < cnt) {
-        const float pr = IM ? (float)(((uint64_t)__float_as_uint(pt[r]) * rcp) >> 32) * 0x1p-30f
+        const float pr = im ? (float)(((uint64_t)__float_as_uint(pt[r]) * rcp) >> 32) * 0x1p-30f
                             : __expf(pt[r] - M);
         lsum += pr;
         const float ps = pr * S;
@@ -654,6 +688,22 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
             atomicAdd((uint32_t*)&s_w[code_idx(vw[r][q]) & AMASK],
                       (uint32_t)(int32_t)rintf(ps * code_coef(vw[r][q])));
         }
+      }
+    }
+  }
+  if (rb) {
+    // reading B: the unselected tokens' weights with their first klow value words
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) {
+      const int64_t t = t0 + (int64_t)j * SB + tid;
+      if (t < t1 && !((sel >> j) & 1u)) {
+        const float pr = __expf(key_float(key[j]) - M);
+        lsum += pr;
+        const float ps = pr * S;
+        const uint32_t* vp = vlo + t * vlw;
+        for (int c = 0; c < a.klow; ++c)
+          atomicAdd((uint32_t*)&s_w[code_idx(vp[c]) & AMASK],
+                    (uint32_t)(int32_t)rintf(ps * code_coef(vp[c])));
       }
     }
   }
@@ -677,7 +727,7 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   // (integer mode: the weights are already normalised; the merge adds them)
   if (tid == 0)
     a.stats[(int64_t)row * a.P + p] =
-        IM ? make_float2(0.f, 1.f) : make_float2(cnt > 0 ? M : -INFINITY, lsum_all);
+        im ? make_float2(0.f, 1.f) : make_float2(M, lsum_all);
 }
 
 // ---------------------------------------------------------------------------
@@ -1060,17 +1110,14 @@ sdkv_status plan_decode(const sdkv_attn_args* a, DecodePlan* p) {
   return SDKV_OK;
 }
 
-template <int S, bool IM, bool SH>
+template <int S, bool EXT>
 static const void* rows_kernel(bool fast) {
-  return fast ? (const void*)&k_rows<S, true, IM, SH> : (const void*)&k_rows<S, false, IM, SH>;
+  return fast ? (const void*)&k_rows<S, true, EXT> : (const void*)&k_rows<S, false, EXT>;
 }
 
-static const void* pick_rows_kernel(int spt, bool fast, bool im, bool sh) {
-#define SDKV_PICK(S)                                         \
-  if (spt == S) {                                            \
-    if (im) return sh ? rows_kernel<S, true, true>(fast) : rows_kernel<S, true, false>(fast); \
-    return sh ? rows_kernel<S, false, true>(fast) : rows_kernel<S, false, false>(fast);       \
-  }
+static const void* pick_rows_kernel(int spt, bool fast, bool ext) {
+#define SDKV_PICK(S) \
+  if (spt == S) return ext ? rows_kernel<S, true>(fast) : rows_kernel<S, false>(fast);
   SDKV_PICK(4)
   SDKV_PICK(8)
   SDKV_PICK(16)
@@ -1159,13 +1206,16 @@ sdkv_status launch_decode(const sdkv_attn_args* a, const DecodePlan& p, void* ws
   ra.bar = bar;
   ra.err = err;
   ra.shared = a->select_mode == SDKV_SELECT_KV ? 1 : 0;
+  ra.readb = a->reading == SDKV_READING_B ? 1 : 0;
+  ra.vlow = a->val_low;
   ra.Ug = (const float*)(base + p.off_ug);
   ra.imode = a->softmax_mode == SDKV_SOFTMAX_INT ? 1 : 0;
   ra.p_int_out = ra.imode ? a->p_int : nullptr;
   ra.ixchg = (uint32_t*)(base + p.off_ixchg);
   const bool aligned = (((uintptr_t)a->key_codes | (uintptr_t)a->val_codes) & 15u) == 0 &&
                        ra.rs % 4 == 0;
-  const void* kfn = pick_rows_kernel(p.spt, p.fast && aligned, ra.imode != 0, ra.shared != 0);
+  const void* kfn = pick_rows_kernel(p.spt, p.fast && aligned,
+                                     ra.imode != 0 || ra.shared != 0 || ra.readb != 0);
   if (!kfn) return SDKV_ERR_UNSUPPORTED;
   ra.ticket = (uint32_t*)(base + p.off_ticket);
   // Per-XCD ticket classes need whole rows per class; with P > 1 every

@@ -48,7 +48,7 @@ extern "C" {
 #define SDKV_API
 #endif
 
-#define SDKV_ABI_VERSION 5
+#define SDKV_ABI_VERSION 6
 
 typedef int32_t sdkv_status;
 #define SDKV_OK 0
@@ -212,12 +212,28 @@ typedef struct sdkv_attn_args {
          debug output then holds that shared score for every head.
        Other values: SDKV_ERR_SHAPE.                                      */
   int32_t select_mode;
+  /* Which tokens enter the softmax (review page, Summary: every token is
+     scored with Klow atoms and the best tenth refined with Khigh; the pages
+     do not say whether the rest then drop out):
+       SDKV_READING_A (0): only S, as above.
+       SDKV_READING_B (1): every token; t in S with s_high_t and its K value
+         pairs, t not in S with its own head's s_low_t and its first klow
+         value pairs:  p = softmax over all T,
+           w[a] = sum_{t in S} p_t sum_{j<K} kappa^v_tj [i^v_tj == a]
+                + sum_{t not in S} p_t sum_{j<klow} kappa^v_tj [i^v_tj == a].
+         Requires SDKV_SOFTMAX_FLOAT (else SDKV_ERR_UNSUPPORTED).
+       Other values: SDKV_ERR_SHAPE.                                      */
+  int32_t reading;
+  const uint32_t* val_low; /* [B, Hkv, T, klow] first klow value words, or
+                              NULL to read them from val_codes (reading B) */
 } sdkv_attn_args;
 #define SDKV_DECODE_STAGES 4
 #define SDKV_SOFTMAX_FLOAT 0
 #define SDKV_SOFTMAX_INT 1
 #define SDKV_SELECT_HEAD 0
 #define SDKV_SELECT_KV 1
+#define SDKV_READING_A 0
+#define SDKV_READING_B 1
 
 /* m = ceil(T * top_num / top_den), clamped to [1, T]; 0 on bad input. */
 SDKV_API int64_t sdkv_selected_count(int64_t T, int64_t top_num, int64_t top_den);

@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) == 11, names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.sdkv_abi_version() == 5
+    assert lib.sdkv_abi_version() == 6
 
 
 def test_status_strings():
@@ -81,6 +81,7 @@ def test_decode_workspace_query():
     ("code_stride", 65537, sd.SDKV_ERR_SHAPE),
     ("softmax_mode", 2, sd.SDKV_ERR_SHAPE), ("softmax_mode", -1, sd.SDKV_ERR_SHAPE),
     ("select_mode", 2, sd.SDKV_ERR_SHAPE), ("select_mode", -1, sd.SDKV_ERR_SHAPE),
+    ("reading", 2, sd.SDKV_ERR_SHAPE), ("reading", -1, sd.SDKV_ERR_SHAPE),
 ])
 def test_decode_validation(field, value, status):
     a = good_attn(**{field: value})
@@ -223,3 +224,9 @@ def test_decode_workspace_shared_selection():
     st, nb = ws_status(good_attn())
     st2, nb2 = ws_status(good_attn(select_mode=sd.SDKV_SELECT_KV))
     assert st == st2 == 0 and nb2 - nb == 8 * 32768 * 4
+
+
+def test_reading_b_needs_float_softmax():
+    assert ws_status(good_attn(reading=sd.SDKV_READING_B))[0] == sd.SDKV_OK
+    a = good_attn(reading=sd.SDKV_READING_B, softmax_mode=sd.SDKV_SOFTMAX_INT)
+    assert ws_status(a)[0] == sd.SDKV_ERR_UNSUPPORTED
