@@ -26,7 +26,7 @@ fixtures); none is "parity unpinned". The readings taken where the pages are
 silent are listed in each docstring.
 """
 from .sdkv_oracle import (  # noqa: F401
-    unpack_codes, pack_codes, mp_encode, decode_attn, select_topk,
+    unpack_codes, pack_codes, mp_encode, omp_encode, decode_attn, select_topk,
     selected_count,
 )
 from .integer_softmax import int_softmax, int_exp_consts, INT_SOFTMAX_P_BITS  # noqa: F401

@@ -9,7 +9,7 @@ import numpy as np
 
 from oracle.integer_softmax import INT_SOFTMAX_P_BITS, int_softmax
 
-__all__ = ["unpack_codes", "pack_codes", "mp_encode", "decode_attn",
+__all__ = ["unpack_codes", "pack_codes", "mp_encode", "omp_encode", "decode_attn",
            "select_topk", "selected_count"]
 
 
@@ -94,6 +94,59 @@ def mp_encode(X: np.ndarray, D: np.ndarray, K: int, *, trace: bool = False,
 
 # ---------------------------------------------------------------------------
 # Decode: two-level (Klow then Khigh) scoring over coded keys and values
+def omp_encode(X: np.ndarray, D: np.ndarray, K: int, *, trace: bool = False):
+    """Orthogonal matching pursuit: the comparison encoder that the pages'
+    greedy pursuit replaces (review page, Summary and Strengths: the
+    projection pursuit avoids OMP's least-squares refits). Per vector x:
+        S = (), r_0 = x
+        for k = 0 .. K-1:
+            c_a  = <r_k, d_a>                 for every atom a
+            a_k  = smallest a with |c_a| maximal
+            S    = S + (a_k,)
+            g    = argmin_g |x - sum_{j<=k} g_j d_{S_j}|^2   (least squares)
+            r_k+1 = x - sum_{j<=k} g_j d_{S_j}
+    The codes are the atoms in selection order with the final refit
+    coefficients. Readings: the same tie rule as the pursuit; the least
+    squares is solved from the normal equations with numpy.linalg.solve
+    (the support's Gram matrix is nonsingular while its atoms are linearly
+    independent, which the refit guarantees for k < d: a new atom with
+    nonzero correlation to a residual orthogonal to the support lies outside
+    its span).
+
+    Returns (idx int64 [n,K], gamma float64 [n,K] final coefficients,
+    resid_norm float64 [n]); with trace=True also the residual norms before
+    each step [n, K+1].
+    """
+    X = np.asarray(X, dtype=np.float64)
+    D = np.asarray(D, dtype=np.float64)
+    n = X.shape[0]
+    idx = np.zeros((n, K), dtype=np.int64)
+    gam = np.zeros((n, K), dtype=np.float64)
+    rn = np.zeros(n, dtype=np.float64)
+    tr = np.zeros((n, K + 1), dtype=np.float64) if trace else None
+    for v in range(n):
+        x = X[v]
+        r = x.copy()
+        S = []
+        g = np.zeros(0)
+        for k in range(K):
+            if trace:
+                tr[v, k] = np.linalg.norm(r)
+            c = D @ r
+            S.append(int(np.argmax(np.abs(c))))
+            DS = D[S]
+            g = np.linalg.solve(DS @ DS.T, DS @ x)
+            r = x - DS.T @ g
+        idx[v] = S
+        gam[v] = g
+        rn[v] = np.linalg.norm(r)
+        if trace:
+            tr[v, K] = rn[v]
+    if trace:
+        return idx, gam, rn, tr
+    return idx, gam, rn
+
+
 # ---------------------------------------------------------------------------
 def selected_count(T: int, top_num: int, top_den: int) -> int:
     """m = ceil(T * num / den) in integer arithmetic, clamped to [1, T].

@@ -212,6 +212,117 @@ ENCODE_CHECKS = [check_golden_mp, check_exact_recovery_orthonormal,
 # ---------------------------------------------------------------------------
 # Decode pins
 # ---------------------------------------------------------------------------
+# --- OMP (the comparison encoder) ---------------------------------------------
+def check_omp_equals_mp_on_orthonormal(omp, mp, seed=40):
+    """On an orthonormal dictionary the least-squares refit returns the
+    projection coefficients, so OMP and the pursuit agree: same atoms,
+    coefficients within 1e-12. K = 1 agrees on any dictionary."""
+    rng = np.random.default_rng(seed)
+    D = orthonormal_dictionary(rng, 24)
+    X = rng.standard_normal((6, 24))
+    i1, g1, r1 = omp(X, D, 7)
+    i2, g2, r2 = mp(X, D, 7)
+    assert np.array_equal(i1, i2)
+    np.testing.assert_allclose(g1, g2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(r1, r2, rtol=0, atol=1e-12)
+    D2 = rng.standard_normal((40, 12))
+    D2 /= np.linalg.norm(D2, axis=1, keepdims=True)
+    i1, g1, _ = omp(X[:, :12], D2, 1)
+    i2, g2, _ = mp(X[:, :12], D2, 1)
+    assert np.array_equal(i1, i2)
+    np.testing.assert_allclose(g1, g2, rtol=0, atol=1e-12)
+
+
+def check_omp_refit_properties(omp, seed=41):
+    """The final residual is orthogonal to every selected atom, equals x
+    minus the coded reconstruction, and the residual norm never grows from
+    one step to the next (least squares over a larger support)."""
+    rng = np.random.default_rng(seed)
+    D = rng.standard_normal((300, 32))
+    D /= np.linalg.norm(D, axis=1, keepdims=True)
+    X = rng.standard_normal((5, 32))
+    idx, gam, rn, tr = omp(X, D, 10, trace=True)
+    for v in range(5):
+        r = X[v] - gam[v] @ D[idx[v]]
+        assert abs(np.linalg.norm(r) - rn[v]) < 1e-12
+        assert np.abs(D[idx[v]] @ r).max() < 1e-12
+        assert np.all(np.diff(tr[v]) <= 1e-12)
+        assert len(set(idx[v].tolist())) == 10
+
+
+def check_omp_exact_recovery_coherent_support(omp, mp, seed=42):
+    """A 3-atom support with pairwise inner products of 0.3 and every other
+    atom satisfying Tropp's exact-recovery condition for OMP,
+    |pinv(D_S) d_a|_1 < 1: OMP picks exactly the support, returns the true
+    coefficients and a zero residual in 3 steps. The pursuit, without the
+    refit, leaves a nonzero residual on the same input."""
+    rng = np.random.default_rng(seed)
+    d, K, N = 48, 3, 200
+    G = np.full((K, K), 0.3) + 0.7 * np.eye(K)
+    L = np.linalg.cholesky(G)
+    Q, _ = np.linalg.qr(rng.standard_normal((d, K)))
+    supp = (Q @ L.T).T  # rows with Gram matrix G
+    rest = rng.standard_normal((N - K, d))
+    rest /= np.linalg.norm(rest, axis=1, keepdims=True)
+    pinv = np.linalg.pinv(supp.T)
+    while True:
+        bad = np.abs(rest @ pinv.T).sum(axis=1) >= 0.9
+        if not bad.any():
+            break
+        r = rng.standard_normal((int(bad.sum()), d))
+        rest[bad] = r / np.linalg.norm(r, axis=1, keepdims=True)
+    D = np.concatenate([supp, rest])
+    for _ in range(8):
+        c = rng.uniform(0.5, 2.0, K) * rng.choice([-1.0, 1.0], K)
+        x = c @ supp
+        idx, gam, rn = omp(x[None], D, K)
+        assert sorted(idx[0].tolist()) == [0, 1, 2]
+        np.testing.assert_allclose(gam[0], c[idx[0]], rtol=0, atol=1e-12)
+        assert rn[0] < 1e-12
+        assert mp(x[None], D, K)[2][0] > 1e-3
+
+
+def check_omp_bruteforce_rational(omp, seed=43):
+    """Tiny integer inputs in exact rational arithmetic: first atom of
+    largest |<r, d_a>| (ties to the lower index), then the exact
+    least-squares coefficients from the normal equations by Gaussian
+    elimination over the rationals."""
+    from fractions import Fraction as F
+    rng = np.random.default_rng(seed)
+    for _ in range(6):
+        d, N, K = 4, 7, 3
+        Dn = rng.integers(-3, 4, (N, d)).astype(np.float64)
+        Dn[np.all(Dn == 0, axis=1)] = 1.0
+        x = rng.integers(-5, 6, d).astype(np.float64)
+        Dq = [[F(int(v)) for v in row] for row in Dn]
+        xq = [F(int(v)) for v in x]
+        r = list(xq)
+        S, g = [], []
+        for _k in range(K):
+            c = [sum(a * b for a, b in zip(Dq[i], r)) for i in range(N)]
+            best = max(abs(ci) for ci in c)
+            S.append(next(i for i in range(N) if abs(c[i]) == best))
+            M = [[sum(a * b for a, b in zip(Dq[i], Dq[j])) for j in S] + [sum(a * b for a, b in zip(Dq[i], xq))]
+                 for i in S]
+            k = len(S)
+            for col in range(k):  # Gauss-Jordan over the rationals
+                piv = next(rw for rw in range(col, k) if M[rw][col] != 0)
+                M[col], M[piv] = M[piv], M[col]
+                M[col] = [v / M[col][col] for v in M[col]]
+                for rw in range(k):
+                    if rw != col and M[rw][col] != 0:
+                        f = M[rw][col]
+                        M[rw] = [a - f * b for a, b in zip(M[rw], M[col])]
+            g = [M[i][k] for i in range(k)]
+            r = [xq[t] - sum(g[i] * Dq[S[i]][t] for i in range(k)) for t in range(d)]
+        idx, gam, _ = omp(x[None], Dn, K)
+        assert list(idx[0]) == S, (list(idx[0]), S)
+        np.testing.assert_allclose(gam[0], [float(v) for v in g], rtol=1e-12, atol=1e-12)
+
+
+OMP_CHECKS = [check_omp_refit_properties, check_omp_bruteforce_rational]
+
+
 def reconstruct(words, D, n_slots):
     """Explicit vectors sum_{j<n_slots} coef_j * D[idx_j] built with plain
     loops (independent of the oracle's table lookups)."""

@@ -171,3 +171,33 @@ def test_int_softmax_mutant_is_caught(name):
 
 def test_unmutated_int_softmax_passes():
     assert not _int_fails(_build_isx(("import math", "import math")))
+
+
+# --- the OMP comparison encoder -------------------------------------------------
+OMP_MUTANTS = {
+    "omp_no_refit": ("g = np.linalg.solve(DS @ DS.T, DS @ x)\n            r = x - DS.T @ g",
+                     "g = np.append(g, c[S[-1]])\n            r = r - g[-1] * D[S[-1]]"),
+    "omp_refit_on_residual": ("g = np.linalg.solve(DS @ DS.T, DS @ x)",
+                              "g = np.linalg.solve(DS @ DS.T, DS @ r)"),
+    "omp_ties_to_last": ("S.append(int(np.argmax(np.abs(c))))",
+                         "S.append(int(len(c) - 1 - np.argmax(np.abs(c)[::-1])))"),
+    "omp_drops_first_atom": ("DS = D[S]", "DS = D[S[1:] if len(S) > 1 else S]"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(OMP_MUTANTS))
+def test_omp_mutant_is_caught(name):
+    m = build(OMP_MUTANTS[name])
+    caught = False
+    for chk in pins.OMP_CHECKS:
+        try:
+            chk(m.omp_encode)
+        except Exception:
+            caught = True
+            break
+    if not caught:
+        try:
+            pins.check_omp_exact_recovery_coherent_support(m.omp_encode, m.mp_encode)
+        except Exception:
+            caught = True
+    assert caught, f"no pin catches OMP mutant {name}"
