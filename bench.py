@@ -281,13 +281,35 @@ def bench_append(args, torch, sd, synth, ev, dec):
     torch.cuda.synchronize()
     ms = ev.ms(t0, t1) / n
     dict_bytes = 2 * K * case.n_atoms * d * 2  # each pursuit step reads its dictionary once
+    # the OMP comparison encoder against the pursuit on the same 16 vectors
+    # (16-atom combinations of the key dictionary plus noise): time per encode
+    # and mean final residual norm
+    xs16 = synth.make_sparse_vectors(rng, case.dk, 2 * B * Hkv, 16, 0.05, "absdesc")[0]
+    x16 = torch.from_numpy(synth.bf16_round(xs16)).to(dev).to(torch.bfloat16)
+    cmp = {}
+    for alg in ("pursuit", "omp"):
+        wsa = sd.Workspace()
+        r = sd.sdkv_encode(x16, dk, K, resid_norm=True, algorithm=alg, workspace=wsa)
+        torch.cuda.synchronize()
+        rn = float(r["resid_norm"].mean())
+        t0, t1 = ev.create(2)
+        ev.record(t0, stream.cuda_stream)
+        for _ in range(n):
+            sd.sdkv_encode(x16, dk, K, codes=r["codes"], resid_norm=r["resid_norm"],
+                           algorithm=alg, workspace=wsa)
+        ev.record(t1, stream.cuda_stream)
+        torch.cuda.synchronize()
+        cmp[alg] = {"us_per_encode": round(ev.ms(t0, t1) / n * 1e3, 2), "mean_resid_norm": round(rn, 5)}
+    cmp["mean_x_norm"] = round(float(np.linalg.norm(xs16, axis=1).mean()), 5)
+    cmp["vectors"] = 2 * B * Hkv
     return {"metric": "decode-step append encode", "us_per_step": round(ms * 1e3, 2),
             "vectors": 2 * B * Hkv, "value": round(2 * B * Hkv / (ms * 1e-3), 1),
             "unit": "vectors/s", "launches": K + 1,
             "dictionary_bytes_per_step": dict_bytes,
             "dictionary_GBs": round(dict_bytes / (ms * 1e-3) / 1e9, 1),
             "config": {"B": B, "Hkv": Hkv, "d": d, "K": K, "n_atoms": case.n_atoms,
-                       "path": "small-batch exact pursuit (n <= 64), key and value encodes sharing launches"}}
+                       "path": "small-batch exact pursuit (n <= 64), key and value encodes sharing launches"},
+            "omp_comparison": cmp}
 
 
 def bench_encode(args, torch, sd, synth, ev):
@@ -431,6 +453,10 @@ def main():
         + ", ".join(f"{k} {v * 1e3:.1f}" for k, v in dec["stage_ms"].items()))
     app = bench_append(args, torch, sd, synth, ev, dec)
     log(f"  decode-step append (16 vectors): {app['us_per_step']:.1f} us")
+    oc = app["omp_comparison"]
+    log(f"  16-vector encode: pursuit {oc['pursuit']['us_per_encode']:.1f} us, |r| "
+        f"{oc['pursuit']['mean_resid_norm']:.4f}; OMP {oc['omp']['us_per_encode']:.1f} us, |r| "
+        f"{oc['omp']['mean_resid_norm']:.4f} (|x| {oc['mean_x_norm']:.4f})")
     log(f"  integer-only softmax step: {dec['int_softmax']['us_per_step']:.1f} us")
     log(f"  shared-selection step: {dec['shared_select']['us_per_step']:.1f} us")
     log(f"  reading-B step: {dec['reading_b']['us_per_step']:.1f} us")

@@ -32,6 +32,8 @@ _SOFTMAX = {"float": SDKV_SOFTMAX_FLOAT, "int": SDKV_SOFTMAX_INT}
 SDKV_SELECT_HEAD, SDKV_SELECT_KV = 0, 1
 _SELECT = {"head": SDKV_SELECT_HEAD, "kv": SDKV_SELECT_KV}
 SDKV_READING_A, SDKV_READING_B = 0, 1
+SDKV_ENCODE_PURSUIT, SDKV_ENCODE_OMP = 0, 1
+_ALGORITHM = {"pursuit": SDKV_ENCODE_PURSUIT, "omp": SDKV_ENCODE_OMP}
 _READING = {"A": SDKV_READING_A, "B": SDKV_READING_B}
 
 c_void_p, c_int32, c_int64, c_float = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
@@ -44,7 +46,7 @@ class EncodeArgs(ctypes.Structure):
                 ("n_atoms", c_int32), ("K", c_int32), ("codes", c_void_p),
                 ("codes_ld", c_int64), ("coef_f32", c_void_p), ("resid_norm", c_void_p),
                 ("low_plane", c_void_p), ("low_ld", c_int64), ("klow", c_int32),
-                ("stage_events", c_void_p)]
+                ("stage_events", c_void_p), ("algorithm", c_int32)]
 
 
 class AttnArgs(ctypes.Structure):
@@ -195,11 +197,12 @@ def _events(stage_events):
 
 def sdkv_encode(x, dictionary, K: int, *, codes=None, coef_f32=None, resid_norm=None,
                 low_plane=None, klow: int = 0, workspace: Optional[Workspace] = None,
-                stream=None, stage_events=None):
+                stream=None, stage_events=None, algorithm: str = "pursuit"):
     """Greedy-pursuit codes of the rows of x [n, d] over `dictionary`
     [n_atoms, d] (bf16 or fp32 GPU tensors). Output tensors are allocated
     when not given: codes int32 [n, K]; pass coef_f32=True / resid_norm=True /
-    low_plane=True (with klow) to request the optional outputs."""
+    low_plane=True (with klow) to request the optional outputs.
+    algorithm="omp" takes the OMP comparison encoder (SDKV_ENCODE_OMP)."""
     torch = _torch()
     n, d = x.shape
     dev = x.device
@@ -217,7 +220,7 @@ def sdkv_encode(x, dictionary, K: int, *, codes=None, coef_f32=None, resid_norm=
                    coef_f32=_dev(coef_f32 if coef_f32 is not False else None, "coef_f32"),
                    resid_norm=_dev(resid_norm if resid_norm is not False else None, "resid_norm"),
                    low_plane=_dev(low_plane if low_plane is not False else None, "low_plane"),
-                   klow=klow)
+                   klow=klow, algorithm=_ALGORITHM[algorithm])
     ev_keep, a.stage_events = _events(stage_events)
     nb = c_size_t(0)
     _check(_lib().sdkv_encode_workspace(ctypes.byref(a), ctypes.byref(nb)), "sdkv_encode_workspace")
@@ -496,7 +499,7 @@ def sdkv_select_topk(scores, k: int, *, idx_out=None, thr_out=None,
 
 __all__ = ["sdkv_encode", "sdkv_decode_attn", "sdkv_select_topk", "selected_count",
            "SDKV_SOFTMAX_FLOAT", "SDKV_SOFTMAX_INT", "SDKV_SELECT_HEAD", "SDKV_SELECT_KV",
-           "SDKV_READING_A", "SDKV_READING_B",
+           "SDKV_READING_A", "SDKV_READING_B", "SDKV_ENCODE_PURSUIT", "SDKV_ENCODE_OMP",
            "Workspace", "SdkvError", "lib", "LIB_PATH", "HEADER", "EncodeArgs", "AttnArgs",
            "sdkv_append_tokens", "sdkv_encode_pair",
            "attn_args", "decode_attn_workspace_bytes", "DecodeCall", "EncodeCall"]

@@ -68,6 +68,9 @@ static sdkv_status check_encode(const sdkv_encode_args* a) {
     return SDKV_ERR_SHAPE;
   if (a->n > ((int64_t)1 << 40)) return SDKV_ERR_UNSUPPORTED;
   if (!aligned16(a->x) || !aligned16(a->dict)) return SDKV_ERR_UNSUPPORTED;
+  if (a->algorithm != SDKV_ENCODE_PURSUIT && a->algorithm != SDKV_ENCODE_OMP) return SDKV_ERR_SHAPE;
+  if (a->algorithm == SDKV_ENCODE_OMP && (a->n > 64 || a->dict_dtype != SDKV_BF16))
+    return SDKV_ERR_UNSUPPORTED;
   return SDKV_OK;
 }
 
@@ -159,7 +162,7 @@ static sdkv_status plan_pair(const sdkv_encode_args* a0, const sdkv_encode_args*
   s = check_encode(a1);
   if (s != SDKV_OK) return s;
   if (a0->n != a1->n || a0->d != a1->d || a0->n_atoms != a1->n_atoms || a0->K != a1->K ||
-      a0->dict_dtype != a1->dict_dtype)
+      a0->dict_dtype != a1->dict_dtype || a0->algorithm != a1->algorithm)
     return SDKV_ERR_SHAPE;
   if ((s = plan_encode(a0, p0)) != SDKV_OK || (s = plan_encode(a1, p1)) != SDKV_OK) return s;
   if (!p0->small || !p1->small) return SDKV_ERR_UNSUPPORTED;

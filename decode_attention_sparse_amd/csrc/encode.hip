@@ -337,6 +337,7 @@ constexpr int kSmallN = 64;        // vectors per call on this path
 constexpr int ECHS = 128;          // atoms per workgroup
 constexpr int ESB = 256;           // threads per workgroup
 constexpr int kSmallMaxG = 512;    // workgroups at 65,536 atoms
+constexpr int kMaxK = 32;          // code length limit
 
 struct SmallArgs {                 // one encode problem
   const void* x;
@@ -351,6 +352,11 @@ struct SmallArgs {                 // one encode problem
   int64_t low_ld;
   int x_f32;
   int klow;
+  // OMP (comparison encoder) state, written by workgroup 0:
+  float* Q;                        // [n][K][D] orthonormal directions of the support
+  float* Rm;                       // [n][K][K] R of the support (R[i][k], i <= k)
+  float* zq;                       // [n][K] coordinates <x, q_k>
+  int* sup;                        // [n][K] support atoms in selection order
 };
 
 struct SmallLaunch {               // up to two problems of one shape
@@ -396,7 +402,46 @@ __device__ __forceinline__ void split3_bf16x4(float4 v, uint2& hi, uint2& mid, u
   lo = make_uint2(o[0], o[1]);
 }
 
-template <int D, bool F32D, int NV, int PPL>
+// Sum over the D/4 consecutive lanes that hold one vector (xor butterfly:
+// every lane gets the same bits).
+template <int D>
+__device__ __forceinline__ float vec_sum(float x) {
+#pragma unroll
+  for (int o = D / 8; o > 0; o >>= 1) x += __shfl_xor(x, o, D / 4);
+  return x;
+}
+
+// OMP, the last launch (step K + 1, one workgroup per vector): the
+// coefficients of vector v from R g = z by back substitution, one lane per
+// support slot, then the code words, fp32 coefficients and low plane.
+template <int D>
+__device__ __forceinline__ void omp_finish_one(const SmallArgs& a, const SmallLaunch& L, int v,
+                                               int l, int K) {
+  float rrow[kMaxK];
+  const float* Rv = a.Rm + (int64_t)v * K * K;
+  const int j = min(l, K - 1);
+#pragma unroll
+  for (int k = 0; k < kMaxK; ++k) rrow[k] = (k < K) ? Rv[(int64_t)j * K + k] : 0.f;
+  const float z = a.zq[(int64_t)v * K + j];
+  float acc = 0.f, g = 0.f;
+#pragma unroll
+  for (int k = kMaxK - 1; k >= 0; --k) {
+    if (k < K) {
+      if (l == k) g = (z - acc) / rrow[k];
+      const float gk = __shfl(g, k, 64);
+      if (l < k) acc = fmaf(rrow[k], gk, acc);
+    }
+  }
+  if (l < K) {
+    const uint32_t word = (uint32_t)a.sup[(int64_t)v * K + l] | (f32_to_f16_bits(g) << 16);
+    a.codes[(int64_t)v * a.codes_ld + l] = word;
+    if (a.coef_f32) a.coef_f32[(int64_t)v * K + l] = g;
+    if (a.low_plane && l < a.klow) a.low_plane[(int64_t)v * a.low_ld + l] = word;
+  }
+}
+
+
+template <int D, bool F32D, int NV, int PPL, bool OMP>
 __global__ __launch_bounds__(ESB) void k_small(SmallLaunch L, int step) {
   static_assert(ECHS * 2 == ESB && ECHS == 32 * (ESB / 64), "atom tiles per wave");
   static_assert(NV <= kSmallN && NV % 16 == 0 && 64 * PPL <= kSmallMaxG, "launch limits");
@@ -413,6 +458,12 @@ __global__ __launch_bounds__(ESB) void k_small(SmallLaunch L, int step) {
   __shared__ float s_g[NV];
   __shared__ int s_a[NV];
   const SmallArgs a = blockIdx.y ? L.p[1] : L.p[0];
+  if constexpr (OMP) {
+    if (step == L.K + 1) {
+      if (blockIdx.x < L.n && threadIdx.x < 64) omp_finish_one<D>(a, L, blockIdx.x, lane_id(), L.K);
+      return;
+    }
+  }
   const int tid = threadIdx.x, w = wave_id(), l = lane_id();
   const int n = L.n, G = L.G, wg = blockIdx.x, nq = n * D / 4;
   const bool corr = step < L.K;
@@ -475,8 +526,73 @@ __global__ __launch_bounds__(ESB) void k_small(SmallLaunch L, int step) {
   }
   __syncthreads();
 
+  // --- OMP: the new atom joins the support. Its direction is orthogonalised
+  // against the previous ones (modified Gram-Schmidt, coefficients R[i][k]),
+  // normalised (R[k][k]; a direction in the support's span, possible only
+  // when the residual is numerically zero, is dropped with R[k][k] = 1), and
+  // r_step = r_{step-1} - z q_k with z = <r_{step-1}, q_k> = <x, q_k>: the
+  // residual of the least-squares fit on the support. The coefficients come
+  // from R g = z at the end. A vector's D/4 float4 groups sit in D/4
+  // consecutive lanes.
+  if constexpr (OMP) {
+    if (step > 0) {
+      const int k = step - 1;
+      float4 q[NQ];
+#pragma unroll
+      for (int j = 0; j < NQ; ++j) {
+        const int i = 4 * min(tid + j * ESB, nq - 1);
+        const uint2 u = *(const uint2*)((const uint16_t*)a.dict + (int64_t)s_a[i / D] * D + i % D);
+        q[j] = make_float4(bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y));
+      }
+      for (int i0 = 0; i0 < k; ++i0) {
+        float4 qi[NQ];
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+          const int e = 4 * min(tid + j * ESB, nq - 1);
+          qi[j] = *(const float4*)(a.Q + ((int64_t)(e / D) * L.K + i0) * D + e % D);
+        }
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+          float dot = q[j].x * qi[j].x;
+          dot = fmaf(q[j].y, qi[j].y, dot); dot = fmaf(q[j].z, qi[j].z, dot); dot = fmaf(q[j].w, qi[j].w, dot);
+          dot = vec_sum<D>(dot);
+          q[j].x = fmaf(-dot, qi[j].x, q[j].x); q[j].y = fmaf(-dot, qi[j].y, q[j].y);
+          q[j].z = fmaf(-dot, qi[j].z, q[j].z); q[j].w = fmaf(-dot, qi[j].w, q[j].w);
+          const int gq = tid + j * ESB;
+          if (wg == 0 && gq < nq && (4 * gq) % D == 0)
+            a.Rm[((int64_t)(4 * gq / D) * L.K + i0) * L.K + k] = dot;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < NQ; ++j) {
+        float nn = q[j].x * q[j].x;
+        nn = fmaf(q[j].y, q[j].y, nn); nn = fmaf(q[j].z, q[j].z, nn); nn = fmaf(q[j].w, q[j].w, nn);
+        nn = vec_sum<D>(nn);
+        const float rkk = sqrtf(nn);
+        const bool ok = rkk > 1e-20f;
+        const float inv = ok ? 1.f / rkk : 0.f;
+        q[j].x *= inv; q[j].y *= inv; q[j].z *= inv; q[j].w *= inv;
+        float z = rr[j].x * q[j].x;
+        z = fmaf(rr[j].y, q[j].y, z); z = fmaf(rr[j].z, q[j].z, z); z = fmaf(rr[j].w, q[j].w, z);
+        z = vec_sum<D>(z);
+        rr[j].x = fmaf(-z, q[j].x, rr[j].x); rr[j].y = fmaf(-z, q[j].y, rr[j].y);
+        rr[j].z = fmaf(-z, q[j].z, rr[j].z); rr[j].w = fmaf(-z, q[j].w, rr[j].w);
+        const int gq = tid + j * ESB;
+        if (wg == 0 && gq < nq) {
+          const int v = 4 * gq / D, e = (4 * gq) % D;
+          *(float4*)(a.Q + ((int64_t)v * L.K + k) * D + e) = q[j];
+          if (e == 0) {
+            a.Rm[((int64_t)v * L.K + k) * L.K + k] = ok ? rkk : 1.f;
+            a.zq[(int64_t)v * L.K + k] = z;
+            a.sup[(int64_t)v * L.K + k] = s_a[v];
+          }
+        }
+      }
+    }
+  }
+
   // --- r_step = r_{step-1} - g d_a, one fmaf per element ---------------------
-  if (step > 0) {
+  if (!OMP && step > 0) {
     float4 dk[NQ];
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
@@ -618,8 +734,8 @@ __global__ __launch_bounds__(ESB) void k_small(SmallLaunch L, int step) {
       }
     }
     // words of steps before K - 1 come from earlier launches; the last one
-    // from this workgroup's own reduction
-    if (a.low_plane)
+    // from this workgroup's own reduction (OMP: written by the last launch)
+    if (!OMP && a.low_plane)
       for (int i = tid; i < n * a.klow; i += ESB) {
         const int v = i / a.klow, j = i % a.klow;
         a.low_plane[(int64_t)v * a.low_ld + j] =
@@ -638,6 +754,10 @@ sdkv_status plan_encode(const sdkv_encode_args* a, EncodePlan* p) {
     size_t off = 0;
     q.off_r = off;     off = align_up(off + (size_t)2 * a->n * a->d * 4, 256);
     q.off_part = off;  off = align_up(off + (size_t)2 * q.G * a->n * 8, 256);
+    if (a->algorithm == SDKV_ENCODE_OMP) {
+      const size_t nK = (size_t)a->n * a->K;
+      q.off_omp = off;  off = align_up(off + nK * a->d * 4 + nK * a->K * 4 + nK * 4 + nK * 4, 256);
+    }
     q.total = off;
     *p = q;
     return SDKV_OK;
@@ -667,16 +787,21 @@ static SmallArgs small_args(const sdkv_encode_args* a, const EncodePlan& p, char
   s.low_ld = a->low_ld ? a->low_ld : a->klow;
   s.x_f32 = a->x_dtype == SDKV_F32;
   s.klow = a->low_plane ? a->klow : 0;
+  const size_t nK = (size_t)a->n * a->K;
+  s.Q = (float*)(base + p.off_omp);
+  s.Rm = s.Q + nK * a->d;
+  s.zq = s.Rm + nK * a->K;
+  s.sup = (int*)(s.zq + nK);
   return s;
 }
 
-template <int D, bool F32D>
+template <int D, bool F32D, bool OMP = false>
 static void launch_small_kernel(bool few, bool narrow, dim3 grid, hipStream_t stream,
                                 const SmallLaunch& L, int step) {
-  if (few && narrow)  hipLaunchKernelGGL((k_small<D, F32D, 16, 4>), grid, dim3(ESB), 0, stream, L, step);
-  else if (few)       hipLaunchKernelGGL((k_small<D, F32D, 16, 8>), grid, dim3(ESB), 0, stream, L, step);
-  else if (narrow)    hipLaunchKernelGGL((k_small<D, F32D, kSmallN, 4>), grid, dim3(ESB), 0, stream, L, step);
-  else                hipLaunchKernelGGL((k_small<D, F32D, kSmallN, 8>), grid, dim3(ESB), 0, stream, L, step);
+  if (few && narrow)  hipLaunchKernelGGL((k_small<D, F32D, 16, 4, OMP>), grid, dim3(ESB), 0, stream, L, step);
+  else if (few)       hipLaunchKernelGGL((k_small<D, F32D, 16, 8, OMP>), grid, dim3(ESB), 0, stream, L, step);
+  else if (narrow)    hipLaunchKernelGGL((k_small<D, F32D, kSmallN, 4, OMP>), grid, dim3(ESB), 0, stream, L, step);
+  else                hipLaunchKernelGGL((k_small<D, F32D, kSmallN, 8, OMP>), grid, dim3(ESB), 0, stream, L, step);
 }
 
 // The K + 1 launches of the small path for `count` (1 or 2) problems of one
@@ -692,6 +817,17 @@ static sdkv_status launch_small(const sdkv_encode_args* const* a, const EncodePl
   const bool f32d = a[0]->dict_dtype == SDKV_F32;
   const dim3 grid((unsigned)L.G, (unsigned)count);
   const bool few = L.n <= 16, narrow = L.G <= 256;
+  if (a[0]->algorithm == SDKV_ENCODE_OMP) {
+    // (bf16 dictionaries only, checked by the caller) K + 2 launches
+    for (int step = 0; step <= L.K + 1; ++step) {
+      // the last launch finishes one vector per workgroup
+      const dim3 g = step <= L.K ? grid : dim3((unsigned)L.n, (unsigned)count);
+      if (a[0]->d == 128) launch_small_kernel<128, false, true>(few, narrow, g, stream, L, step);
+      else                launch_small_kernel<64, false, true>(few, narrow, g, stream, L, step);
+      if (hipGetLastError() != hipSuccess) return SDKV_ERR_DEVICE;
+    }
+    return SDKV_OK;
+  }
   for (int step = 0; step <= L.K; ++step) {
     if (a[0]->d == 128) {
       if (f32d) launch_small_kernel<128, true>(few, narrow, grid, stream, L, step);

@@ -71,6 +71,7 @@ struct EncodePlan {
   int small = 0;         // n <= 64: exact pursuit spread over the device
   int G = 0;             // small path: workgroups (atom slices)
   size_t off_part = 0;   // small path: per-workgroup winners [2][G][n]
+  size_t off_omp = 0;    // small path, OMP: Q, R, z and support
   size_t total = 0;
 };
 sdkv_status plan_encode(const sdkv_encode_args* a, EncodePlan* p);

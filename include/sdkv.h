@@ -48,7 +48,7 @@ extern "C" {
 #define SDKV_API
 #endif
 
-#define SDKV_ABI_VERSION 6
+#define SDKV_ABI_VERSION 7
 
 typedef int32_t sdkv_status;
 #define SDKV_OK 0
@@ -103,7 +103,19 @@ typedef struct sdkv_encode_args {
      stage i and the last one after the final stage. Stages: 0 fp16 screen
      copy of the dictionary, 1 pursuit.                                   */
   void* const* stage_events;
+  /* SDKV_ENCODE_PURSUIT (0): the greedy pursuit above. SDKV_ENCODE_OMP (1):
+     orthogonal matching pursuit, the comparison encoder the pursuit
+     replaces (review page, Summary and Strengths: the projection pursuit
+     avoids OMP's least-squares refits): the same atom choice on the current
+     residual, then every selected atom's coefficient refit by least squares
+     and r = x - sum_j g_j d_{a_j}; the codes hold the final coefficients.
+     Built as a comparison on the small path only: n <= 64 and bf16
+     dictionaries, else SDKV_ERR_UNSUPPORTED; K + 2 launches. Other values:
+     SDKV_ERR_SHAPE.                                                      */
+  int32_t algorithm;
 } sdkv_encode_args;
+#define SDKV_ENCODE_PURSUIT 0
+#define SDKV_ENCODE_OMP 1
 #define SDKV_ENCODE_STAGES 2
 
 /* Bytes of device workspace sdkv_encode needs for these arguments. */
@@ -111,15 +123,16 @@ SDKV_API sdkv_status sdkv_encode_workspace(const sdkv_encode_args* args, size_t*
 SDKV_API sdkv_status sdkv_encode(const sdkv_encode_args* args, void* ws, size_t ws_bytes,
                         void* stream);
 
-/* Two small encodes in one sequence of K + 1 launches: a decode step's new
- * key vectors over the key dictionary and its value vectors over the value
- * dictionary (review page, Strengths, on write endurance: a new token is
- * appended as codes). Each side gets the codes, coefficients, norms and low
- * plane that sdkv_encode gives it alone, bit for bit. Both must take the
- * small path (n <= 64) and agree in n, d, n_atoms, K and dict_dtype, else
- * SDKV_ERR_UNSUPPORTED (n > 64) or SDKV_ERR_SHAPE; stage_events are not
- * recorded. The workspace holds both sides' scratch; outputs must not
- * overlap the inputs or each other. */
+/* Two small encodes in one sequence of launches (K + 1; OMP: K + 2): a
+ * decode step's new key vectors over the key dictionary and its value
+ * vectors over the value dictionary (review page, Strengths, on write
+ * endurance: a new token is appended as codes). Each side gets the codes,
+ * coefficients, norms and low plane that sdkv_encode gives it alone, bit
+ * for bit. Both must take the small path (n <= 64), else
+ * SDKV_ERR_UNSUPPORTED, and agree in n, d, n_atoms, K, dict_dtype and
+ * algorithm, else SDKV_ERR_SHAPE; stage_events are not recorded. The
+ * workspace holds both sides' scratch; outputs must not overlap the inputs
+ * or each other. */
 SDKV_API sdkv_status sdkv_encode_pair_workspace(const sdkv_encode_args* key,
                                                 const sdkv_encode_args* val, size_t* bytes);
 SDKV_API sdkv_status sdkv_encode_pair(const sdkv_encode_args* key, const sdkv_encode_args* val,

@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) == 11, names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.sdkv_abi_version() == 6
+    assert lib.sdkv_abi_version() == 7
 
 
 def test_status_strings():
@@ -230,3 +230,24 @@ def test_reading_b_needs_float_softmax():
     assert ws_status(good_attn(reading=sd.SDKV_READING_B))[0] == sd.SDKV_OK
     a = good_attn(reading=sd.SDKV_READING_B, softmax_mode=sd.SDKV_SOFTMAX_INT)
     assert ws_status(a)[0] == sd.SDKV_ERR_UNSUPPORTED
+
+
+def test_omp_encoder_limits():
+    nb = ctypes.c_size_t(0)
+    lib = sd.lib()
+    a = good_enc(n=16, algorithm=sd.SDKV_ENCODE_OMP)
+    assert lib.sdkv_encode_workspace(ctypes.byref(a), ctypes.byref(nb)) == 0
+    base = ctypes.c_size_t(0)
+    b = good_enc(n=16)
+    assert lib.sdkv_encode_workspace(ctypes.byref(b), ctypes.byref(base)) == 0
+    # Q [n][K][d], R [n][K][K], z and the support [n][K]
+    extra = 16 * 16 * (128 + 16 + 2) * 4
+    assert nb.value == base.value + -(-extra // 256) * 256
+    for field, value, status in (("n", 65, sd.SDKV_ERR_UNSUPPORTED),
+                                 ("dict_dtype", sd.SDKV_F32, sd.SDKV_ERR_UNSUPPORTED),
+                                 ("algorithm", 2, sd.SDKV_ERR_SHAPE)):
+        c = good_enc(n=16, algorithm=sd.SDKV_ENCODE_OMP)
+        setattr(c, field, value)
+        assert lib.sdkv_encode_workspace(ctypes.byref(c), ctypes.byref(nb)) == status
+    k, v = good_enc(n=8), good_enc(n=8, algorithm=sd.SDKV_ENCODE_OMP)
+    assert lib.sdkv_encode_pair_workspace(ctypes.byref(k), ctypes.byref(v), ctypes.byref(nb)) == sd.SDKV_ERR_SHAPE
