@@ -208,12 +208,15 @@ def bench_decode(args, torch, sd, synth, ev):
         return {"us_per_step": round(vms * 1e3, 2), "value": round(B * T / (vms * 1e-3), 1),
                 "unit": "context-tokens/s", "relative_to_default_step": round(vms / ms, 3)}
 
-    int_res = {"metric": "decode step with the integer-only softmax", **time_variant(softmax="int")}
-    kv_res = {"metric": "decode step with the selection shared by each KV head's query heads",
-              **time_variant(select="kv")}
-    b_res = {"metric": "decode step, reading B (every token in the softmax; Klow values "
-                       "outside the selection)",
-             **time_variant(per_set=lambda s: {"val_low": s["vl"]}, reading="B")}
+    int_res = kv_res = b_res = None
+    if not args.no_variants:
+        int_res = {"metric": "decode step with the integer-only softmax",
+                   **time_variant(softmax="int")}
+        kv_res = {"metric": "decode step with the selection shared by each KV head's query heads",
+                  **time_variant(select="kv")}
+        b_res = {"metric": "decode step, reading B (every token in the softmax; Klow values "
+                           "outside the selection)",
+                 **time_variant(per_set=lambda s: {"val_low": s["vl"]}, reading="B")}
 
     # algorithmic bytes (HBM): what the method must read per step
     low_b = B * Hkv * T * case.klow * 4
@@ -416,6 +419,8 @@ def main():
     ap.add_argument("--enc-warmup", type=int, default=1)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-encode", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the attention-flag steps, the append and the OMP comparison")
     ap.add_argument("--no-decode", action="store_true",
                     help="encode only (profiling runs); prints no benchmark line")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -451,15 +456,17 @@ def main():
     dec = bench_decode(args, torch, sd, synth, ev)
     log(f"  {dec['ms'] * 1e3:.1f} us/step, stages (us): "
         + ", ".join(f"{k} {v * 1e3:.1f}" for k, v in dec["stage_ms"].items()))
-    app = bench_append(args, torch, sd, synth, ev, dec)
-    log(f"  decode-step append (16 vectors): {app['us_per_step']:.1f} us")
-    oc = app["omp_comparison"]
-    log(f"  16-vector encode: pursuit {oc['pursuit']['us_per_encode']:.1f} us, |r| "
-        f"{oc['pursuit']['mean_resid_norm']:.4f}; OMP {oc['omp']['us_per_encode']:.1f} us, |r| "
-        f"{oc['omp']['mean_resid_norm']:.4f} (|x| {oc['mean_x_norm']:.4f})")
-    log(f"  integer-only softmax step: {dec['int_softmax']['us_per_step']:.1f} us")
-    log(f"  shared-selection step: {dec['shared_select']['us_per_step']:.1f} us")
-    log(f"  reading-B step: {dec['reading_b']['us_per_step']:.1f} us")
+    app = None
+    if not args.no_variants:
+        app = bench_append(args, torch, sd, synth, ev, dec)
+        log(f"  decode-step append (16 vectors): {app['us_per_step']:.1f} us")
+        oc = app["omp_comparison"]
+        log(f"  16-vector encode: pursuit {oc['pursuit']['us_per_encode']:.1f} us, |r| "
+            f"{oc['pursuit']['mean_resid_norm']:.4f}; OMP {oc['omp']['us_per_encode']:.1f} us, |r| "
+            f"{oc['omp']['mean_resid_norm']:.4f} (|x| {oc['mean_x_norm']:.4f})")
+        log(f"  integer-only softmax step: {dec['int_softmax']['us_per_step']:.1f} us")
+        log(f"  shared-selection step: {dec['shared_select']['us_per_step']:.1f} us")
+        log(f"  reading-B step: {dec['reading_b']['us_per_step']:.1f} us")
     enc = None
     if not args.no_encode:
         log("encode benchmark (524,288 vectors)")
@@ -487,10 +494,11 @@ def main():
         "stage_us": {k: round(v * 1e3, 2) for k, v in dec["stage_ms"].items()},
         "cpu_baseline": cpu,
     }
-    line["append"] = app
-    line["int_softmax"] = dec["int_softmax"]
-    line["shared_select"] = dec["shared_select"]
-    line["reading_b"] = dec["reading_b"]
+    if app is not None:
+        line["append"] = app
+        line["int_softmax"] = dec["int_softmax"]
+        line["shared_select"] = dec["shared_select"]
+        line["reading_b"] = dec["reading_b"]
     if enc is not None:
         line["encode"] = {
             "metric": "KV vectors encoded/s", "value": round(enc["value"], 1),
