@@ -190,7 +190,7 @@ def bench_decode(args, torch, sd, synth, ev):
     stage_ms = [float(np.mean([ev.ms(e[j], e[j + 1]) for e in evs])) for j in range(nstage - 1)]
 
     # the same step with each attention flag of the same call
-    def time_variant(per_set=lambda s: {}, **flags):
+    def time_variant(per_set=lambda s: {}, extra_bytes=0, **flags):
         vcalls = [sd.DecodeCall(s["q"], s["dk"], s["dv"], s["kv"], None, klow=case.klow,
                                 khigh=case.khigh, top_num=case.top_num, top_den=case.top_den,
                                 scale=case.scale, key_low=s["kl"], out=out, workspace=ws,
@@ -205,18 +205,12 @@ def bench_decode(args, torch, sd, synth, ev):
         ev.record(t1, stream.cuda_stream)
         torch.cuda.synchronize()
         vms = ev.ms(t0, t1) / args.steps
+        path_b = total_b + extra_bytes
         return {"us_per_step": round(vms * 1e3, 2), "value": round(B * T / (vms * 1e-3), 1),
-                "unit": "context-tokens/s", "relative_to_default_step": round(vms / ms, 3)}
-
-    int_res = kv_res = b_res = None
-    if not args.no_variants:
-        int_res = {"metric": "decode step with the integer-only softmax",
-                   **time_variant(softmax="int")}
-        kv_res = {"metric": "decode step with the selection shared by each KV head's query heads",
-                  **time_variant(select="kv")}
-        b_res = {"metric": "decode step, reading B (every token in the softmax; Klow values "
-                           "outside the selection)",
-                 **time_variant(per_set=lambda s: {"val_low": s["vl"]}, reading="B")}
+                "unit": "context-tokens/s", "relative_to_default_step": round(vms / ms, 3),
+                "path_roofline": {"bound": "hbm", "algorithmic_bytes_per_step": path_b,
+                                  "achieved_GBs": round(path_b / (vms * 1e-3) / 1e9, 1),
+                                  "frac": round(path_b / (vms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
 
     # algorithmic bytes (HBM): what the method must read per step
     low_b = B * Hkv * T * case.klow * 4
@@ -226,6 +220,18 @@ def bench_decode(args, torch, sd, synth, ev):
     qo_b = B * Hq * d * (2 + 4)
     stage_bytes = [dict_b + B * Hq * d * 2, low_b + refine_b + value_b, dict_b, B * Hq * d * 4]
     total_b = sum(stage_bytes)
+    int_res = kv_res = b_res = None
+    if not args.no_variants:
+        int_res = {"metric": "decode step with the integer-only softmax",
+                   **time_variant(softmax="int")}
+        kv_res = {"metric": "decode step with the selection shared by each KV head's query heads",
+                  **time_variant(select="kv")}
+        b_res = {"metric": "decode step, reading B (every token in the softmax; Klow values "
+                           "outside the selection)",
+                 **time_variant(per_set=lambda s: {"val_low": s["vl"]}, reading="B",
+                                # every query head reads its KV head's value low plane
+                                extra_bytes=B * Hq * T * case.klow * 4)}
+
     dom = int(np.argmax(stage_ms))
     names = ["k_utable_bf16", "k_rows", "k_wdv_bf16", "k_reduce_out"]
     achieved = stage_bytes[dom] / (stage_ms[dom] * 1e-3) / 1e9
@@ -310,6 +316,10 @@ def bench_append(args, torch, sd, synth, ev, dec):
             "unit": "vectors/s", "launches": K + 1,
             "dictionary_bytes_per_step": dict_bytes,
             "dictionary_GBs": round(dict_bytes / (ms * 1e-3) / 1e9, 1),
+            "roofline": {"bound": "hbm", "achieved": round(dict_bytes / (ms * 1e-3) / 1e9, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(dict_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "note": "each pursuit step reads both dictionaries once"},
             "config": {"B": B, "Hkv": Hkv, "d": d, "K": K, "n_atoms": case.n_atoms,
                        "path": "small-batch exact pursuit (n <= 64), key and value encodes sharing launches"},
             "omp_comparison": cmp}
