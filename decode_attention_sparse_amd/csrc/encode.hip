@@ -544,23 +544,33 @@ __global__ __launch_bounds__(ESB) void k_small(SmallLaunch L, int step) {
         const uint2 u = *(const uint2*)((const uint16_t*)a.dict + (int64_t)s_a[i / D] * D + i % D);
         q[j] = make_float4(bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y));
       }
-      for (int i0 = 0; i0 < k; ++i0) {
-        float4 qi[NQ];
+      // previous directions QB at a time: their loads are issued together
+      constexpr int QB = NQ <= 2 ? 4 : 1;
+      for (int i0 = 0; i0 < k; i0 += QB) {
+        float4 qi[QB][NQ];
 #pragma unroll
-        for (int j = 0; j < NQ; ++j) {
-          const int e = 4 * min(tid + j * ESB, nq - 1);
-          qi[j] = *(const float4*)(a.Q + ((int64_t)(e / D) * L.K + i0) * D + e % D);
-        }
+        for (int u = 0; u < QB; ++u)
 #pragma unroll
-        for (int j = 0; j < NQ; ++j) {
-          float dot = q[j].x * qi[j].x;
-          dot = fmaf(q[j].y, qi[j].y, dot); dot = fmaf(q[j].z, qi[j].z, dot); dot = fmaf(q[j].w, qi[j].w, dot);
-          dot = vec_sum<D>(dot);
-          q[j].x = fmaf(-dot, qi[j].x, q[j].x); q[j].y = fmaf(-dot, qi[j].y, q[j].y);
-          q[j].z = fmaf(-dot, qi[j].z, q[j].z); q[j].w = fmaf(-dot, qi[j].w, q[j].w);
-          const int gq = tid + j * ESB;
-          if (wg == 0 && gq < nq && (4 * gq) % D == 0)
-            a.Rm[((int64_t)(4 * gq / D) * L.K + i0) * L.K + k] = dot;
+          for (int j = 0; j < NQ; ++j) {
+            const int e = 4 * min(tid + j * ESB, nq - 1);
+            qi[u][j] = *(const float4*)(a.Q + ((int64_t)(e / D) * L.K + min(i0 + u, k - 1)) * D + e % D);
+          }
+#pragma unroll
+        for (int u = 0; u < QB; ++u) {
+          if (i0 + u < k) {
+#pragma unroll
+            for (int j = 0; j < NQ; ++j) {
+              float dot = q[j].x * qi[u][j].x;
+              dot = fmaf(q[j].y, qi[u][j].y, dot); dot = fmaf(q[j].z, qi[u][j].z, dot);
+              dot = fmaf(q[j].w, qi[u][j].w, dot);
+              dot = vec_sum<D>(dot);
+              q[j].x = fmaf(-dot, qi[u][j].x, q[j].x); q[j].y = fmaf(-dot, qi[u][j].y, q[j].y);
+              q[j].z = fmaf(-dot, qi[u][j].z, q[j].z); q[j].w = fmaf(-dot, qi[u][j].w, q[j].w);
+              const int gq = tid + j * ESB;
+              if (wg == 0 && gq < nq && (4 * gq) % D == 0)
+                a.Rm[((int64_t)(4 * gq / D) * L.K + i0 + u) * L.K + k] = dot;
+            }
+          }
         }
       }
 #pragma unroll
