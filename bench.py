@@ -321,7 +321,7 @@ def bench_append(args, torch, sd, synth, ev, dec):
                          "frac": round(dict_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                          "note": "each pursuit step reads both dictionaries once"},
             "config": {"B": B, "Hkv": Hkv, "d": d, "K": K, "n_atoms": case.n_atoms,
-                       "path": "small-batch exact pursuit (n <= 64), key and value encodes sharing launches"},
+                       "path": "small-batch fp32-accurate pursuit (n <= 64), key and value encodes sharing launches"},
             "omp_comparison": cmp}
 
 

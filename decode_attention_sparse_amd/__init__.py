@@ -356,7 +356,7 @@ def sdkv_append_tokens(xk, xv, dk, dv, key_codes, val_codes, t: int, *, key_low=
     val_codes int32 [B, Hkv, T, K], or key_codes [B, Hkv, T, 2, K] with
     val_codes=None (records side by side); key_low int32 [B, Hkv, T, klow]
     receives the key's first klow words. With n = B*Hkv <= 64 both sides
-    take the exact small-batch path together, in one sequence of K + 1
+    take the fp32-accurate small-batch path together, in one sequence of K + 1
     launches (sdkv_encode_pair); larger batches make two sdkv_encode calls."""
     B, Hkv, d = xk.shape
     if val_codes is None:

@@ -68,7 +68,7 @@ struct EncodePlan {
   int rows_per_wg = 0;
   int64_t nwg = 0;
   size_t off_dh = 0, off_r = 0, off_rh = 0, off_scale = 0;
-  int small = 0;         // n <= 64: exact pursuit spread over the device
+  int small = 0;         // n <= 64: fp32-accurate pursuit over the device
   int G = 0;             // small path: workgroups (atom slices)
   size_t off_part = 0;   // small path: per-workgroup winners [2][G][n]
   size_t off_omp = 0;    // small path, OMP: Q, R, z and support

@@ -74,8 +74,11 @@ typedef int32_t sdkv_status;
  * found with an fp16 matrix-core screen of all atoms followed by an exact
  * fp32 re-check of the best candidates. For n <= 64 (a decode step's new
  * tokens, which the cache appends as codes: review page, Strengths, on
- * write endurance) every correlation is computed exactly in fp32, with the
- * atoms spread over the whole device; that path takes K + 1 launches.
+ * write endurance) every correlation is computed to fp32 accuracy with the
+ * atoms spread over the whole device (bf16 dictionaries: the residual split
+ * exactly into three bf16 parts on the matrix cores, products exact, fp32
+ * accumulation; fp32 dictionaries: fp32 dot products); that path takes
+ * K + 1 launches.
  * ---------------------------------------------------------------------- */
 typedef struct sdkv_encode_args {
   const void* x;        /* [n, d] vectors, dtype x_dtype (SDKV_BF16/F32)  */
@@ -92,7 +95,8 @@ typedef struct sdkv_encode_args {
                            else >= K. Pointing `codes` at slot t of a
                            [rows, T, stride] cache with codes_ld = T *
                            stride appends one token per row in place.     */
-  float* coef_f32;      /* OUT [n, K] unrounded g_k, or NULL              */
+  float* coef_f32;      /* OUT [n, K] unrounded g_k (OMP: the final
+                           least-squares coefficients), or NULL           */
   float* resid_norm;    /* OUT [n] |r_K|_2, or NULL                       */
   uint32_t* low_plane;  /* OUT first klow code words of vector i at
                            low_plane[i * low_ld + j], or NULL             */

@@ -1,5 +1,5 @@
 """GPU parity of the decode-step append: the small-batch encode path
-(n <= 64 vectors, exact fp32 correlations spread over the device) against
+(n <= 64 vectors, fp32-accurate correlations spread over the device) against
 the fp64 oracle, against the batch path, and written into a cache slot."""
 import numpy as np
 import pytest
