@@ -110,6 +110,17 @@ def test_many_workgroups_per_row_and_batches():
     compare(case, run_gpu(case))
 
 
+def test_cooperative_rows_with_the_selection_list_in_the_workspace():
+    """128 rows of 20,000 tokens keeping the top half: each row is split over
+    two workgroups of 16 keys per thread, and each workgroup selects ~5,000
+    tokens, more than its LDS list holds, so the list and the rescored
+    scores live in the workspace."""
+    H.log("decode B=16 Hq=8 Hkv=2 T=20000 top 1/2")
+    case = synth.decode_case(B=16, Hq=8, Hkv=2, T=20000, seed=15, n_atoms=1024, top_num=1,
+                             top_den=2)
+    compare(case, run_gpu(case))
+
+
 def test_low_plane_from_key_codes():
     H.log("decode without a separate low plane")
     case = synth.decode_case(B=1, Hq=4, Hkv=1, T=3000, seed=8, n_atoms=1024)

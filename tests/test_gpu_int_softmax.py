@@ -84,6 +84,15 @@ def test_int_softmax_rows_over_many_workgroups():
     check(case, run_int(case, interleaved=True), "T=40000")
 
 
+def test_int_softmax_selection_list_in_the_workspace():
+    # ~5,000 selected tokens per workgroup: the integer exponentials are
+    # stored over the scores in the workspace list
+    H.log("integer softmax: B=16 Hq=8 Hkv=2 T=20000 top 1/2")
+    case = synth.decode_case(B=16, Hq=8, Hkv=2, T=20000, seed=19, n_atoms=1024, top_num=1,
+                             top_den=2)
+    check(case, run_int(case), "top 1/2")
+
+
 def test_int_softmax_zero_query_uniform():
     """q = 0: every score is 0 (k = 30), so within each row every selected
     token gets the same integer probability."""

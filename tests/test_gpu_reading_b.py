@@ -89,6 +89,13 @@ def test_reading_b_with_shared_selection():
     check(case, run(case, select="kv"), "B + shared", select="kv")
 
 
+def test_reading_b_selection_list_in_the_workspace():
+    H.log("reading B: B=16 Hq=8 Hkv=2 T=20000 top 1/2 (selection list in the workspace)")
+    case = synth.decode_case(B=16, Hq=8, Hkv=2, T=20000, seed=41, n_atoms=1024, top_num=1,
+                             top_den=2)
+    check(case, run(case, val_low=False), "top 1/2")
+
+
 def test_reading_b_at_full_selection_equals_reading_a():
     H.log("reading B with every token selected")
     case = synth.decode_case(B=1, Hq=4, Hkv=2, T=3000, seed=39, n_atoms=2048)

@@ -82,6 +82,13 @@ def test_shared_select_rows_over_many_workgroups():
     check(case, run(case, interleaved=True), "T=40000")
 
 
+def test_shared_select_selection_list_in_the_workspace():
+    H.log("shared selection: B=16 Hq=8 Hkv=2 T=20000 top 1/2 (selection list in the workspace)")
+    case = synth.decode_case(B=16, Hq=8, Hkv=2, T=20000, seed=30, n_atoms=1024, top_num=1,
+                             top_den=2)
+    check(case, run(case), "top 1/2")
+
+
 def test_shared_select_with_integer_softmax():
     H.log("shared selection + integer softmax: B=1 Hq=8 Hkv=2 T=20000")
     case = synth.decode_case(B=1, Hq=8, Hkv=2, T=20000, seed=28, n_atoms=4096)
