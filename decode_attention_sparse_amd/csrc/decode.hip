@@ -245,14 +245,13 @@ __device__ __forceinline__ void stage_u(const RowsArgs& a, const float* src, flo
 
 // U row staging and low scores of a chunk for records of 16 words whose
 // first min(klow, 4) words score the token (klow <= 4). The U loads are
-// issued with the first token batch (and whatever loads `pre` issues);
-// token batches are double-buffered (the next batch is requested before the
-// current one is scored). LOW3: klow == 3, each token's three words are one
-// 12-byte load.
-template <int SPT, bool LOW3, typename Pre>
+// issued with the first token batch; token batches are double-buffered (the
+// next batch is requested before the current one is scored). LOW3: klow == 3,
+// each token's three words are one 12-byte load.
+template <int SPT, bool LOW3>
 __device__ __forceinline__ void score_chunk(const RowsArgs& a, const float* usrc, const uint32_t* lo,
                                             int64_t t0, int64_t t1, float* s_u,
-                                            uint32_t (&key)[SPT], Pre&& pre) {
+                                            uint32_t (&key)[SPT]) {
   const int tid = threadIdx.x;
   const int lw = a.low_words;
   constexpr int AMASK = kMaxAtomsDecode - 1;
@@ -275,7 +274,6 @@ __device__ __forceinline__ void score_chunk(const RowsArgs& a, const float* usrc
     }
   };
   load_batch(0, wb[0]);
-  pre();
   stage_u(a, usrc, s_u);
   __syncthreads();
   const int nk = LOW3 ? 3 : a.klow;
@@ -332,32 +330,9 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   // the ranking table: this head's U row, or its group's summed row
   const bool im = EXT && a.imode, sh_sel = EXT && a.shared, rb = EXT && a.readb;
   const float* usrc = sh_sel ? a.Ug + kv * a.N : a.U + (int64_t)row * a.N;
-  // rows split over P > 1 workgroups rank a shared sample first (step 3):
-  // its element t_i is i if T <= kSampleN, else, with R = kSampleN / 16 runs
-  // of 16 consecutive tokens, run g = i / 16 starting at floor(g T / R)
-  // (inside the row: T > kSampleN = 16 R, so (R - 1) T / R + 15 < T). With
-  // records of up to four scoring words (FAST) their loads go out with the
-  // chunk's first batch.
-  const bool coop = !(SPT > kMaxCoopSPT || a.P == 1);
-  const int64_t ns = min((int64_t)kSampleN, a.T);
-  const bool all = a.T <= kSampleN;
-  auto sample_token = [&](int j) -> int64_t {
-    const int64_t i = min((int64_t)(tid + j * SB), ns - 1);
-    return all ? i : ((i >> 4) * a.T) / kSampleRuns + (i & 15);
-  };
-  uint32_t swd[kSamplePT][4];
-  auto load_sample = [&]() {
-    if (!coop) return;
-#pragma unroll
-    for (int j = 0; j < kSamplePT; ++j) {
-      const uint32_t* wp = lo + sample_token(j) * lw;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) swd[j][c] = wp[min(c, a.klow - 1)];
-    }
-  };
   if (FAST) {
-    if (low3) score_chunk<SPT, true>(a, usrc, lo, t0, t1, s_u, key, load_sample);
-    else score_chunk<SPT, false>(a, usrc, lo, t0, t1, s_u, key, load_sample);
+    if (low3) score_chunk<SPT, true>(a, usrc, lo, t0, t1, s_u, key);
+    else score_chunk<SPT, false>(a, usrc, lo, t0, t1, s_u, key);
   } else {
     stage_u(a, usrc, s_u);
     __syncthreads();
@@ -399,25 +374,37 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   uint32_t offset = 0, count = 0, tau = 0, nbar = 0;
   bool need_offset = false;
   Mask sel = 0;
-  if (!coop) {
+  if (SPT > kMaxCoopSPT || a.P == 1) {
     // single-workgroup rows (the only ones the host plans at SPT > kMaxCoopSPT)
     sel = radix_select_local<SPT>(key, (uint32_t)a.m, sh, &offset, &count, &tau);
   } else {
-    // s_low of the shared sample (the same in every workgroup of the row)
+    // s_low of a fixed sample of the row's tokens (the same in every
+    // workgroup of the row): all tokens if T <= kSampleN, else R = kSampleN /
+    // 16 runs of 16 consecutive tokens, run g starting at floor(g T / R)
+    // (inside the row: T > kSampleN = 16 R, so (R - 1) T / R + 15 < T)
+    const int64_t ns = min((int64_t)kSampleN, a.T);
+    const bool all = a.T <= kSampleN;
     uint32_t skey[kSamplePT];
     {
-      if (!FAST) load_sample();
+      uint32_t wd[kSamplePT][4];
+      const uint32_t* wps[kSamplePT];
 #pragma unroll
       for (int j = 0; j < kSamplePT; ++j) {
+        const int64_t i = min((int64_t)(tid + j * SB), ns - 1);
+        const int64_t t = all ? i : ((i >> 4) * a.T) / kSampleRuns + (i & 15);
+        wps[j] = lo + t * lw;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) wd[j][c] = wps[j][min(c, a.klow - 1)];
+      }
+#pragma unroll
+      for (int j = 0; j < kSamplePT; ++j) {
+        const uint32_t* wp = wps[j];
         float s = 0.f;
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-          if (c < a.klow) s = fmaf(code_coef(swd[j][c]), s_u[code_idx(swd[j][c]) & AMASK], s);
-        if (!FAST) {
-          const uint32_t* wp = lo + sample_token(j) * lw;
-          for (int c = 4; c < a.klow; ++c)
-            s = fmaf(code_coef(wp[c]), s_u[code_idx(wp[c]) & AMASK], s);
-        }
+          if (c < a.klow) s = fmaf(code_coef(wd[j][c]), s_u[code_idx(wd[j][c]) & AMASK], s);
+        for (int c = 4; c < a.klow; ++c)
+          s = fmaf(code_coef(wp[c]), s_u[code_idx(wp[c]) & AMASK], s);
         skey[j] = (tid + j * SB < ns) ? float_key(s) : 0u;
       }
     }
