@@ -420,6 +420,40 @@ def cpu_baseline_encode(ecase, budget_s):
             "sample": f"{n_sample} seeded vectors of the key stream, {el:.1f} s, fp64 NumPy"}
 
 
+def achievable(torch, reps: int = 5):
+    """What the device reaches on plain library work, as context for the
+    roofline fractions (the fractions themselves use the published peaks):
+    a 1 GiB device-to-device copy (bytes read + written) and an 8192^3 bf16
+    matrix product (torch.matmul on contiguous 2-D operands). Medians of
+    `reps` timed runs after one warm-up, timed with events on torch's stream."""
+    def med(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return sorted(ts)[len(ts) // 2]
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    t_copy = med(lambda: dst.copy_(src))
+    del src, dst
+    g = 8192
+    a = torch.randn(g, g, device="cuda").to(torch.bfloat16)
+    b = torch.randn(g, g, device="cuda").to(torch.bfloat16)
+    t_mm = med(lambda: torch.matmul(a, b))
+    del a, b
+    torch.cuda.empty_cache()
+    return {"copy_GBs": round(2 * n * 4 / t_copy / 1e9, 1),
+            "bf16_gemm_TFLOPs": round(2 * g ** 3 / t_mm / 1e12, 1),
+            "what": "1 GiB device copy (read + write bytes); 8192^3 bf16 torch.matmul"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -427,7 +461,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--enc-steps", type=int, default=3)
     ap.add_argument("--enc-warmup", type=int, default=1)
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-cpu", action="store_true",
+                    help="skip the CPU oracle baseline and the achievable-rate measurements")
     ap.add_argument("--no-encode", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the attention-flag steps, the append and the OMP comparison")
@@ -483,8 +518,11 @@ def main():
         enc = bench_encode(args, torch, sd, synth, ev)
         log(f"  {enc['ms']:.2f} ms/step, kernel {enc['kernel_ms']:.2f} ms, "
             f"{enc['value'] / 1e6:.2f} M vectors/s, {enc['roofline']['achieved']} TFLOP/s")
-    cpu = None
+    ach = cpu = None
     if not args.no_cpu:
+        ach = achievable(torch)
+        log(f"achievable: device copy {ach['copy_GBs']} GB/s, bf16 GEMM "
+            f"{ach['bf16_gemm_TFLOPs']} TFLOP/s")
         log("cpu baseline (fp64 oracle on host cores)")
         cpu = cpu_baseline_decode(dec["case"], args.cpu_budget)
         if enc is not None:
@@ -503,6 +541,7 @@ def main():
         "path_roofline": dec["path"],
         "stage_us": {k: round(v * 1e3, 2) for k, v in dec["stage_ms"].items()},
         "cpu_baseline": cpu,
+        "achievable": ach,
     }
     if app is not None:
         line["append"] = app
