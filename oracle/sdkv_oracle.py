@@ -111,7 +111,10 @@ def omp_encode(X: np.ndarray, D: np.ndarray, K: int, *, trace: bool = False):
     (the support's Gram matrix is nonsingular while its atoms are linearly
     independent, which the refit guarantees for k < d: a new atom with
     nonzero correlation to a residual orthogonal to the support lies outside
-    its span).
+    its span). The pages leave the exact-fit case open; reading: once the
+    residual is exactly zero every correlation is zero, the tie rule picks
+    atom 0, and the fit is already exact, so that atom joins with
+    coefficient 0 and no refit is made.
 
     Returns (idx int64 [n,K], gamma float64 [n,K] final coefficients,
     resid_norm float64 [n]); with trace=True also the residual norms before
@@ -134,6 +137,9 @@ def omp_encode(X: np.ndarray, D: np.ndarray, K: int, *, trace: bool = False):
                 tr[v, k] = np.linalg.norm(r)
             c = D @ r
             S.append(int(np.argmax(np.abs(c))))
+            if not np.any(c):
+                g = np.append(g, 0.0)
+                continue
             DS = D[S]
             g = np.linalg.solve(DS @ DS.T, DS @ x)
             r = x - DS.T @ g

@@ -320,7 +320,25 @@ def check_omp_bruteforce_rational(omp, seed=43):
         np.testing.assert_allclose(gam[0], [float(v) for v in g], rtol=1e-12, atol=1e-12)
 
 
-OMP_CHECKS = [check_omp_refit_properties, check_omp_bruteforce_rational]
+def check_omp_exact_fit(omp, seed=44):
+    """Once the residual is exactly zero (the exact-fit reading): a zero
+    vector gives atom 0 with coefficient 0 in every slot; x = 3 e_2 over the
+    standard basis of R^8 is fitted by atom 2 with coefficient 3, after which
+    atom 0 fills the remaining slots with coefficient 0 (worked by hand)."""
+    rng = np.random.default_rng(seed)
+    D = rng.standard_normal((40, 16))
+    D /= np.linalg.norm(D, axis=1, keepdims=True)
+    idx, gam, rn = omp(np.zeros((1, 16)), D, 4)
+    assert idx.tolist() == [[0, 0, 0, 0]] and np.all(gam == 0) and rn[0] == 0
+    x = np.zeros((1, 8))
+    x[0, 2] = 3.0
+    idx, gam, rn = omp(x, np.eye(8), 4)
+    assert idx.tolist() == [[2, 0, 0, 0]], idx
+    assert gam.tolist() == [[3.0, 0.0, 0.0, 0.0]], gam
+    assert rn[0] == 0
+
+
+OMP_CHECKS = [check_omp_refit_properties, check_omp_bruteforce_rational, check_omp_exact_fit]
 
 
 def reconstruct(words, D, n_slots):

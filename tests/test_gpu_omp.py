@@ -134,3 +134,27 @@ def test_omp_residual_against_the_pursuit():
     H.log(f"  mean |r_16|: OMP {go['resid_norm'].mean():.4f} (oracle {rn_o.mean():.4f}), "
           f"pursuit {gp['resid_norm'].mean():.4f} (oracle {rn_p.mean():.4f}), "
           f"|x| {np.linalg.norm(x, axis=1).mean():.4f}")
+
+
+@pytest.mark.parametrize("n,algorithm", [(6, "omp"), (6, "pursuit"), (100, "pursuit")])
+def test_zero_vectors(n, algorithm):
+    """Zero vectors (every correlation zero): atom 0 with coefficient 0 in
+    every slot and a zero residual norm, on the small path (n <= 64) for both
+    encoders and on the batch path for the pursuit; the batch's other
+    vectors as the oracle encodes them."""
+    H.log(f"zero vectors: n={n} {algorithm}")
+    rng = np.random.default_rng(47 + n)
+    D = synth.make_dictionary(rng, 2048, 128, "bf16")
+    x = synth.bf16_round(synth.make_sparse_vectors(rng, D, n, 16, 0.05, "absdesc")[0])
+    z = [1, n - 2]
+    x[z] = 0.0
+    g = run(x, D, 8, algorithm=algorithm)
+    gi, gc = H.unpack_words(g["codes"])
+    assert np.all(gi[z] == 0) and np.all(gc[z] == 0)
+    assert np.all(g["coef_f32"][z] == 0) and np.all(g["resid_norm"][z] == 0)
+    if algorithm == "omp":
+        compare_omp(x, D, 8, g, "omp with zero vectors")
+    else:
+        ri, _, rn = oracle.mp_encode(x, D, 8)
+        assert H.code_agreement(gi, ri) >= H.IDX_AGREE
+        assert np.abs(g["resid_norm"].astype(np.float64) - rn).max() <= 1e-4 * max(1.0, rn.max())

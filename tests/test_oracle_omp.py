@@ -1,8 +1,9 @@
 """Pins of the oracle's OMP comparison encoder (oracle.omp_encode): agreement
 with the pursuit where the refit changes nothing (orthonormal dictionary,
 K = 1), the defining properties of the least-squares refit, exact recovery
-of a coherent support that the pursuit alone cannot finish, and exact
-rational brute force on tiny integer inputs."""
+of a coherent support that the pursuit alone cannot finish, exact
+rational brute force on tiny integer inputs, and the exact-fit case (a
+residual that reaches zero)."""
 import oracle
 from tests import oracle_pins as pins
 
@@ -21,3 +22,7 @@ def test_omp_exact_recovery_of_a_coherent_support():
 
 def test_omp_rational_bruteforce():
     pins.check_omp_bruteforce_rational(oracle.omp_encode)
+
+
+def test_omp_exact_fit():
+    pins.check_omp_exact_fit(oracle.omp_encode)
