@@ -113,7 +113,9 @@ typedef struct sdkv_encode_args {
      avoids OMP's least-squares refits): the same atom choice on the current
      residual, then every selected atom's coefficient refit by least squares
      and r = x - sum_j g_j d_{a_j}; the codes hold the final coefficients.
-     Built as a comparison on the small path only: n <= 64 and bf16
+     Once the residual is exactly zero (a zero vector) every correlation is
+     zero: the remaining slots take atom 0 with coefficient 0, as in the
+     pursuit. Built as a comparison on the small path only: n <= 64 and bf16
      dictionaries, else SDKV_ERR_UNSUPPORTED; K + 2 launches. Other values:
      SDKV_ERR_SHAPE.                                                      */
   int32_t algorithm;
