@@ -25,7 +25,8 @@ LIB_PATH = os.path.join(HERE, "libsdkv.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "sdkv.h")
 
 SDKV_OK, SDKV_ERR_NULL, SDKV_ERR_SHAPE, SDKV_ERR_DTYPE = 0, 1, 2, 3
-SDKV_ERR_UNSUPPORTED, SDKV_ERR_WORKSPACE, SDKV_ERR_DEVICE = 4, 5, 6
+SDKV_ERR_UNSUPPORTED, SDKV_ERR_WORKSPACE, SDKV_ERR_DEVICE, SDKV_ERR_WAIT = 4, 5, 6, 7
+ABI_VERSION = 8
 SDKV_BF16, SDKV_F32 = 0, 1
 SDKV_SOFTMAX_FLOAT, SDKV_SOFTMAX_INT = 0, 1
 _SOFTMAX = {"float": SDKV_SOFTMAX_FLOAT, "int": SDKV_SOFTMAX_INT}
@@ -91,6 +92,11 @@ def _lib():
         lib = ctypes.CDLL(LIB_PATH)
         P = ctypes.POINTER
         lib.sdkv_abi_version.restype = c_int32
+        if lib.sdkv_abi_version() != ABI_VERSION:
+            raise ImportError(f"{LIB_PATH} has ABI {lib.sdkv_abi_version()}, the binding "
+                              f"expects {ABI_VERSION}: rebuild it")
+        lib.sdkv_test_set_wait.restype = None
+        lib.sdkv_test_set_wait.argtypes = [ctypes.c_uint32, ctypes.c_uint32]
         lib.sdkv_status_str.restype = ctypes.c_char_p
         lib.sdkv_status_str.argtypes = [c_int32]
         lib.sdkv_selected_count.restype = c_int64
@@ -118,6 +124,13 @@ def _lib():
 
 def lib():
     return _lib()
+
+
+def set_test_wait(polls: int = 0, extra: int = 0):
+    """Test hook (sdkv_test_set_wait): later calls' cross-workgroup waits give
+    up after `polls` polls and wait for `extra` arrivals that never come;
+    set_test_wait() restores the normal bounds."""
+    _lib().sdkv_test_set_wait(polls, extra)
 
 
 def _check(status: int, where: str):
@@ -159,7 +172,11 @@ def _stream(stream):
 
 
 class Workspace:
-    """A reusable device workspace (a uint8 torch tensor that grows on demand)."""
+    """A reusable device workspace (a uint8 torch tensor that grows on demand).
+
+    Word 0 of a decode-attention or top-k workspace is the call's status word
+    (include/sdkv.h): status() reads it (synchronising) and check() raises
+    SdkvError(SDKV_ERR_WAIT) when a cross-workgroup wait gave up."""
 
     def __init__(self, device=None):
         self.buf = None
@@ -172,12 +189,33 @@ class Workspace:
             self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device or "cuda")
         return self.buf
 
+    def status(self) -> int:
+        """The status word (uint32 at byte 0) after the last call's work has
+        completed (a device-to-host copy, which waits for it)."""
+        if self.buf is None:
+            return 0
+        b = self.buf[:4].cpu().tolist()
+        return b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24)
 
-def _ws(workspace, nbytes):
-    if workspace is None:
+    def check(self, where: str = "status word"):
+        if self.status() != 0:
+            raise SdkvError(SDKV_ERR_WAIT, where)
+
+
+def _ws(workspace, nbytes, stream=None):
+    """(workspace, pointer, size). The caller keeps the returned Workspace
+    referenced until the call has been enqueued; a workspace made here for
+    one call is also tied to the launch stream, so the caching allocator
+    does not hand its memory out again before that stream's work is done."""
+    own = workspace is None
+    if own:
         workspace = Workspace()
     buf = workspace.get(nbytes)
-    return buf.data_ptr(), buf.numel()
+    if own and stream is not None:
+        torch = _torch()
+        if stream != torch.cuda.current_stream():
+            buf.record_stream(stream)
+    return workspace, buf.data_ptr(), buf.numel()
 
 
 # ---------------------------------------------------------------------------
@@ -224,9 +262,10 @@ def sdkv_encode(x, dictionary, K: int, *, codes=None, coef_f32=None, resid_norm=
     ev_keep, a.stage_events = _events(stage_events)
     nb = c_size_t(0)
     _check(_lib().sdkv_encode_workspace(ctypes.byref(a), ctypes.byref(nb)), "sdkv_encode_workspace")
-    wp, wn = _ws(workspace, nb.value)
+    ws, wp, wn = _ws(workspace, nb.value, stream)
     _check(_lib().sdkv_encode(ctypes.byref(a), ctypes.c_void_p(wp), wn, _stream(stream)),
            "sdkv_encode")
+    del ws
     res = {"codes": codes}
     if coef_f32 is not None and coef_f32 is not False:
         res["coef_f32"] = coef_f32
@@ -275,7 +314,8 @@ def sdkv_decode_attn(q, dk, dv, key_codes, val_codes, *, klow: int, khigh: int,
                      top_num: int = 1, top_den: int = 10, scale: Optional[float] = None,
                      key_low=None, out=None, debug: bool = False, softmax: str = "float",
                      select: str = "head", reading: str = "A", val_low=None,
-                     workspace: Optional[Workspace] = None, stream=None, stage_events=None):
+                     workspace: Optional[Workspace] = None, stream=None, stage_events=None,
+                     check: bool = True):
     """Hierarchical coded decode attention. q [B,Hq,d] bf16; dk, dv
     [n_atoms,d] bf16/fp32; key_codes, val_codes int32 [B,Hkv,T,K], or
     key_codes int32 [B,Hkv,T,2,K] (each token's key record, then its value
@@ -284,7 +324,10 @@ def sdkv_decode_attn(q, dk, dv, key_codes, val_codes, *, klow: int, khigh: int,
     select="kv" shares each KV head's selection among its query heads
     (SDKV_SELECT_KV); reading="B" lets every token into the softmax
     (SDKV_READING_B), with val_low int32 [B,Hkv,T,klow] the first klow
-    value words (optional).
+    value words (optional). q may be bf16 or fp32.
+    With check=True (the default) the call waits for its work and raises
+    SdkvError(SDKV_ERR_WAIT) if the workspace's status word reports that a
+    cross-workgroup wait gave up.
     Returns out fp32 [B,Hq,d], or with debug=True a dict that also holds u,
     s_low, sel, s_high and w (and p_int in integer mode)."""
     torch = _torch()
@@ -310,9 +353,11 @@ def sdkv_decode_attn(q, dk, dv, key_codes, val_codes, *, klow: int, khigh: int,
                   key_low=key_low, softmax=softmax, select=select, reading=reading,
                   val_low=val_low, **dbg)
     ev_keep, a.stage_events = _events(stage_events)
-    wp, wn = _ws(workspace, decode_attn_workspace_bytes(a))
+    ws, wp, wn = _ws(workspace, decode_attn_workspace_bytes(a), stream)
     _check(_lib().sdkv_decode_attn(ctypes.byref(a), ctypes.c_void_p(wp), wn, _stream(stream)),
            "sdkv_decode_attn")
+    if check:
+        ws.check("sdkv_decode_attn")
     if debug:
         dbg["out"] = out
         return dbg
@@ -332,9 +377,10 @@ def _encode_rows_args(x, dictionary, K, codes_ptr, codes_ld, low_ptr, low_ld, kl
 def _encode_into(a, workspace, stream):
     nb = c_size_t(0)
     _check(_lib().sdkv_encode_workspace(ctypes.byref(a), ctypes.byref(nb)), "sdkv_encode_workspace")
-    wp, wn = _ws(workspace, nb.value)
+    ws, wp, wn = _ws(workspace, nb.value, stream)
     _check(_lib().sdkv_encode(ctypes.byref(a), ctypes.c_void_p(wp), wn, _stream(stream)),
            "sdkv_encode")
+    del ws
 
 
 def sdkv_encode_pair(ak: "EncodeArgs", av: "EncodeArgs", workspace: Optional[Workspace] = None,
@@ -344,9 +390,10 @@ def sdkv_encode_pair(ak: "EncodeArgs", av: "EncodeArgs", workspace: Optional[Wor
     nb = c_size_t(0)
     _check(_lib().sdkv_encode_pair_workspace(ctypes.byref(ak), ctypes.byref(av), ctypes.byref(nb)),
            "sdkv_encode_pair_workspace")
-    wp, wn = _ws(workspace if workspace is not None else Workspace(), nb.value)
+    ws, wp, wn = _ws(workspace, nb.value, stream)
     _check(_lib().sdkv_encode_pair(ctypes.byref(ak), ctypes.byref(av), ctypes.c_void_p(wp), wn,
                                    _stream(stream)), "sdkv_encode_pair")
+    del ws
 
 
 def sdkv_append_tokens(xk, xv, dk, dv, key_codes, val_codes, t: int, *, key_low=None,
@@ -412,7 +459,7 @@ class DecodeCall:
                               scale, out, key_low=key_low, softmax=softmax, select=select,
                               reading=reading, val_low=val_low)
         self.ws = workspace if workspace is not None else Workspace()
-        wp, wn = _ws(self.ws, decode_attn_workspace_bytes(self.args))
+        _, wp, wn = _ws(self.ws, decode_attn_workspace_bytes(self.args))
         self._wsp, self._wsn = ctypes.c_void_p(wp), wn
         self._stream = _stream(stream)
         self._argp = ctypes.byref(self.args)
@@ -428,6 +475,11 @@ class DecodeCall:
         if st != SDKV_OK:
             raise SdkvError(st, "sdkv_decode_attn")
         return self.out
+
+    def check(self):
+        """Raise SdkvError(SDKV_ERR_WAIT) if the last launch's status word
+        reports a wait that gave up (waits for the launch to complete)."""
+        self.ws.check("sdkv_decode_attn")
 
 
 class EncodeCall:
@@ -451,7 +503,7 @@ class EncodeCall:
         _check(_lib().sdkv_encode_workspace(ctypes.byref(self.args), ctypes.byref(nb)),
                "sdkv_encode_workspace")
         self.ws = workspace if workspace is not None else Workspace()
-        wp, wn = _ws(self.ws, nb.value)
+        _, wp, wn = _ws(self.ws, nb.value)
         self._wsp, self._wsn = ctypes.c_void_p(wp), wn
         self._stream = _stream(stream)
         self._argp = ctypes.byref(self.args)
@@ -470,10 +522,12 @@ class EncodeCall:
 
 
 def sdkv_select_topk(scores, k: int, *, idx_out=None, thr_out=None,
-                     workspace: Optional[Workspace] = None, stream=None):
+                     workspace: Optional[Workspace] = None, stream=None, check: bool = True):
     """Indices (int32, ascending) of the k largest entries of each row of the
     fp32 GPU tensor `scores` [rows, n] (rows may be strided: row stride =
-    scores.stride(0)); ties to the lower index. Returns (idx, thr)."""
+    scores.stride(0)); ties to the lower index. Returns (idx, thr). With
+    check=True the call waits for its work and raises on a status word that
+    reports a wait that gave up (see sdkv_decode_attn)."""
     torch = _torch()
     if scores.dim() == 1:
         scores = scores[None]
@@ -488,12 +542,14 @@ def sdkv_select_topk(scores, k: int, *, idx_out=None, thr_out=None,
     nb = c_size_t(0)
     _check(_lib().sdkv_select_topk_workspace(rows, n, k, ctypes.byref(nb)),
            "sdkv_select_topk_workspace")
-    wp, wn = _ws(workspace, nb.value)
+    ws, wp, wn = _ws(workspace, nb.value, stream)
     thr_ptr = thr_out.data_ptr() if thr_out is not None and thr_out is not False else None
     _check(_lib().sdkv_select_topk(ctypes.c_void_p(scores.data_ptr()), rows, n, ld, k,
                                    ctypes.c_void_p(_dev(idx_out, "idx_out")),
                                    ctypes.c_void_p(thr_ptr), ctypes.c_void_p(wp), wn,
                                    _stream(stream)), "sdkv_select_topk")
+    if check:
+        ws.check("sdkv_select_topk")
     return idx_out, (thr_out if thr_ptr else None)
 
 
@@ -501,5 +557,6 @@ __all__ = ["sdkv_encode", "sdkv_decode_attn", "sdkv_select_topk", "selected_coun
            "SDKV_SOFTMAX_FLOAT", "SDKV_SOFTMAX_INT", "SDKV_SELECT_HEAD", "SDKV_SELECT_KV",
            "SDKV_READING_A", "SDKV_READING_B", "SDKV_ENCODE_PURSUIT", "SDKV_ENCODE_OMP",
            "Workspace", "SdkvError", "lib", "LIB_PATH", "HEADER", "EncodeArgs", "AttnArgs",
+           "SDKV_ERR_WAIT", "set_test_wait",
            "sdkv_append_tokens", "sdkv_encode_pair",
            "attn_args", "decode_attn_workspace_bytes", "DecodeCall", "EncodeCall"]

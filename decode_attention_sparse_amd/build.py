@@ -1,22 +1,25 @@
 """Build libsdkv.so (HIP, gfx950) in-tree with hipcc.
 
 Usage: python -m decode_attention_sparse_amd.build  (or build() from Python).
-Every call recompiles. The library lands next to this file.
+Every call recompiles: each source to an object (in parallel), then one link.
+The library lands next to this file; objects go to _build/ beside it.
 """
 from __future__ import annotations
 
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
+OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsdkv.so")
 SOURCES = ["api.hip", "decode.hip", "topk.hip", "encode.hip"]
 ARCH = "gfx950"
 
 FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Wall", "-Wno-unused-result",
     # no packed fp32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -31,10 +34,7 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, "-I", os.path.join(HERE, "..", "include"), *srcs, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -45,6 +45,19 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(lines))
     if lines and verbose:
         print("\n".join(lines))
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OBJ, exist_ok=True)
+    inc = ["-I", os.path.join(HERE, "..", "include")]
+    srcs = list(SOURCES)
+    objs = [os.path.join(OBJ, os.path.splitext(s)[0] + ".o") for s in srcs]
+    cmds = [[hipcc(), *FLAGS, *inc, "-c", os.path.join(CSRC, s), "-o", o]
+            for s, o in zip(srcs, objs)]
+    with ThreadPoolExecutor(max_workers=min(len(cmds), 8)) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
+    tmp = LIB + ".tmp"
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -5,6 +5,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -15,8 +16,9 @@ using namespace sdkv;
 namespace sdkv {
 
 // The co-residency capacity of a (kernel, block size, device) never changes,
-// so it is computed once and cached. This small mutex-guarded cache is the
-// library's only process-wide state.
+// so it is computed once and cached. This small mutex-guarded cache and the
+// wait bounds below (changed only by the test hook) are the library's only
+// process-wide state.
 namespace {
 struct CapEntry {
   const void* kernel;
@@ -25,6 +27,24 @@ struct CapEntry {
 std::mutex g_cap_mu;
 std::vector<CapEntry> g_cap;
 }  // namespace
+
+// Bounds of the cross-workgroup waits. Normal: 2^24 polls (each after an
+// s_sleep of 64 clocks, ~0.5 s), nothing added to the arrival targets.
+// sdkv_test_set_wait replaces both, so that tests can make every wait give
+// up on purpose while every kernel still exits normally.
+namespace {
+constexpr uint32_t kWaitPolls = 1u << 24;
+std::atomic<uint32_t> g_wait_polls{kWaitPolls};
+std::atomic<uint32_t> g_wait_extra{0};
+}  // namespace
+
+WaitCtl wait_ctl(uint32_t* err) {
+  WaitCtl w;
+  w.err = err;
+  w.limit = g_wait_polls.load(std::memory_order_relaxed);
+  w.extra = g_wait_extra.load(std::memory_order_relaxed);
+  return w;
+}
 
 sdkv_status coresident_blocks(const void* kernel, int threads, size_t dyn_lds, int* out) {
   int dev = 0;
@@ -92,7 +112,6 @@ static sdkv_status check_attn(const sdkv_attn_args* a) {
   if (a->select_mode != SDKV_SELECT_HEAD && a->select_mode != SDKV_SELECT_KV)
     return SDKV_ERR_SHAPE;
   if (a->reading != SDKV_READING_A && a->reading != SDKV_READING_B) return SDKV_ERR_SHAPE;
-  if (a->q_dtype != SDKV_BF16) return SDKV_ERR_UNSUPPORTED;
   if (a->n_atoms > kMaxAtomsDecode) return SDKV_ERR_UNSUPPORTED;
   if ((int64_t)a->B * a->Hq > 0x7FFFFFFF / 64) return SDKV_ERR_UNSUPPORTED;
   if (!aligned16(a->q) || !aligned16(a->dk) || !aligned16(a->dv)) return SDKV_ERR_UNSUPPORTED;
@@ -101,9 +120,32 @@ static sdkv_status check_attn(const sdkv_attn_args* a) {
   return SDKV_OK;
 }
 
+namespace sdkv {
+sdkv_status plan_pair(const sdkv_encode_args* a0, const sdkv_encode_args* a1,
+                      EncodePlan* p0, EncodePlan* p1, size_t* off1, size_t* total) {
+  sdkv_status s = check_encode(a0);
+  if (s != SDKV_OK) return s;
+  s = check_encode(a1);
+  if (s != SDKV_OK) return s;
+  if (a0->n != a1->n || a0->d != a1->d || a0->n_atoms != a1->n_atoms || a0->K != a1->K ||
+      a0->dict_dtype != a1->dict_dtype || a0->algorithm != a1->algorithm)
+    return SDKV_ERR_SHAPE;
+  if ((s = plan_encode(a0, p0)) != SDKV_OK || (s = plan_encode(a1, p1)) != SDKV_OK) return s;
+  if (!p0->small || !p1->small) return SDKV_ERR_UNSUPPORTED;
+  *off1 = align_up(p0->total, 256);
+  *total = *off1 + p1->total;
+  return SDKV_OK;
+}
+}  // namespace sdkv
+
 extern "C" {
 
 int32_t sdkv_abi_version(void) { return SDKV_ABI_VERSION; }
+
+void sdkv_test_set_wait(uint32_t polls, uint32_t extra) {
+  g_wait_polls.store(polls ? polls : kWaitPolls, std::memory_order_relaxed);
+  g_wait_extra.store(extra, std::memory_order_relaxed);
+}
 
 const char* sdkv_status_str(sdkv_status s) {
   switch (s) {
@@ -114,6 +156,7 @@ const char* sdkv_status_str(sdkv_status s) {
     case SDKV_ERR_UNSUPPORTED: return "valid arguments outside the supported range";
     case SDKV_ERR_WORKSPACE: return "workspace too small";
     case SDKV_ERR_DEVICE: return "HIP runtime or launch error";
+    case SDKV_ERR_WAIT: return "a cross-workgroup wait gave up (workgroups not co-resident)";
     default: return "unknown status";
   }
 }
@@ -153,22 +196,6 @@ sdkv_status sdkv_encode(const sdkv_encode_args* args, void* ws, size_t ws_bytes,
   } catch (...) {
     return SDKV_ERR_DEVICE;
   }
-}
-
-static sdkv_status plan_pair(const sdkv_encode_args* a0, const sdkv_encode_args* a1,
-                             EncodePlan* p0, EncodePlan* p1, size_t* off1, size_t* total) {
-  sdkv_status s = check_encode(a0);
-  if (s != SDKV_OK) return s;
-  s = check_encode(a1);
-  if (s != SDKV_OK) return s;
-  if (a0->n != a1->n || a0->d != a1->d || a0->n_atoms != a1->n_atoms || a0->K != a1->K ||
-      a0->dict_dtype != a1->dict_dtype || a0->algorithm != a1->algorithm)
-    return SDKV_ERR_SHAPE;
-  if ((s = plan_encode(a0, p0)) != SDKV_OK || (s = plan_encode(a1, p1)) != SDKV_OK) return s;
-  if (!p0->small || !p1->small) return SDKV_ERR_UNSUPPORTED;
-  *off1 = align_up(p0->total, 256);
-  *total = *off1 + p1->total;
-  return SDKV_OK;
 }
 
 sdkv_status sdkv_encode_pair_workspace(const sdkv_encode_args* a0, const sdkv_encode_args* a1,

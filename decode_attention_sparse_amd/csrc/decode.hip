@@ -27,7 +27,8 @@ namespace sdkv {
 // U table
 // ---------------------------------------------------------------------------
 struct UArgs {
-  const uint16_t* q;   // [rows, d] bf16
+  const void* q;       // [rows, d] bf16, or fp32 when q_f32
+  int q_f32;
   const void* dk;      // [N, d]
   int rows, N, d;
   float scale;
@@ -62,12 +63,37 @@ __global__ __launch_bounds__(256) void k_utable_bf16(UArgs a) {
   for (int r0 = 0; r0 < a.rows; r0 += 16) {
     const int row = r0 + (l & 15);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (a.q_f32) {
+      // fp32 queries: three exact bf16 parts, each product exact on the
+      // matrix cores, fp32 accumulation
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      if (s < ks) {
-        u32x4 af = u32x4{0u, 0u, 0u, 0u};
-        if (row < a.rows) af = *(const u32x4*)(a.q + (int64_t)row * a.d + 32 * s + 8 * (l >> 4));
-        acc = mfma_bf16(af, bf[s], acc);
+      for (int s = 0; s < 4; ++s) {
+        if (s < ks) {
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = 0.f;
+          if (row < a.rows) {
+            const float4* qp = (const float4*)((const float*)a.q + (int64_t)row * a.d + 32 * s + 8 * (l >> 4));
+            const float4 x0 = qp[0], x1 = qp[1];
+            v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
+            v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+          }
+          u32x4 hi, mid, lo;
+          split3_bf16(v, hi, mid, lo);
+          acc = mfma_bf16(hi, bf[s], acc);
+          acc = mfma_bf16(mid, bf[s], acc);
+          acc = mfma_bf16(lo, bf[s], acc);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        if (s < ks) {
+          u32x4 af = u32x4{0u, 0u, 0u, 0u};
+          if (row < a.rows)
+            af = *(const u32x4*)((const uint16_t*)a.q + (int64_t)row * a.d + 32 * s + 8 * (l >> 4));
+          acc = mfma_bf16(af, bf[s], acc);
+        }
       }
     }
 #pragma unroll
@@ -101,9 +127,14 @@ __global__ __launch_bounds__(256) void k_utable_f32(UArgs a) {
   if (i >= (int64_t)a.rows * a.N) return;
   const int r = (int)(i / a.N), atom = (int)(i % a.N);
   const float* dk = (const float*)a.dk + (int64_t)atom * a.d;
-  const uint16_t* q = a.q + (int64_t)r * a.d;
   float s = 0.f;
-  for (int k = 0; k < a.d; ++k) s = fmaf(bf16_to_f32(q[k]), dk[k], s);
+  if (a.q_f32) {
+    const float* q = (const float*)a.q + (int64_t)r * a.d;
+    for (int k = 0; k < a.d; ++k) s = fmaf(q[k], dk[k], s);
+  } else {
+    const uint16_t* q = (const uint16_t*)a.q + (int64_t)r * a.d;
+    for (int k = 0; k < a.d; ++k) s = fmaf(bf16_to_f32(q[k]), dk[k], s);
+  }
   const float v = s * a.scale;
   a.U[i] = v;
   if (a.u_dbg) a.u_dbg[i] = v;
@@ -134,7 +165,7 @@ struct RowsArgs {
   uint32_t* cand;           // [rows, P, chunk] threshold-bin candidates
   uint32_t* xchg;           // [rows, P, 2]
   uint32_t* bar;            // [rows, 2] barrier counters
-  uint32_t* err;
+  WaitCtl wait;             // status word (workspace word 0) and wait bounds
   uint32_t* ticket;         // [8] workgroup start-order counters, zeroed per call
   int xcd_map;              // per-XCD ticket classes (rows stay on one XCD)
   const float* Ug;          // [B * Hkv, N] group-summed U rows (shared selection)
@@ -365,7 +396,7 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   grp.xchg = a.xchg + (int64_t)row * a.P * 2;
   grp.bar = a.bar + 2 * (int64_t)row;
   grp.local = a.xcd_map != 0;
-  grp.err = a.err;
+  grp.wait = a.wait;
   grp.cand = a.cand + (int64_t)row * a.P * a.chunk;
   grp.cap = a.chunk;
   // offset: this workgroup's first position in the row's selection (token
@@ -446,10 +477,10 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   // debug outputs need the row-global position of this workgroup's entries
   if (need_offset) {
     if (tid == 0) st_agent(&grp.xchg[2 * p + 1], nsel);
-    group_barrier(grp.bar, (uint32_t)a.P, ++nbar, grp.local, grp.err);
+    const bool ok = group_barrier(grp.bar, (uint32_t)a.P, ++nbar, grp.local, grp.wait);
     if (tid == 0) {
       uint32_t off = 0;
-      for (int q = 0; q < p; ++q) off += ld_agent(&grp.xchg[2 * q + 1]);
+      for (int q = 0; q < p && ok; ++q) off += ld_agent(&grp.xchg[2 * q + 1]);
       sh.bcast[6] = off;
     }
     __syncthreads();
@@ -586,9 +617,9 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
         st_agent(&ix[4 * p], __float_as_uint(M));
         st_agent(&ix[4 * p + 1], __float_as_uint(mn));
       }
-      group_barrier(grp.bar, (uint32_t)a.P, ++nbar, grp.local, grp.err);
+      const bool ok = group_barrier(grp.bar, (uint32_t)a.P, ++nbar, grp.local, grp.wait);
       if (tid == 0) {
-        for (int q = 0; q < a.P; ++q) {
+        for (int q = 0; q < a.P && ok; ++q) {
           smax = fmaxf(smax, __uint_as_float(ld_agent(&ix[4 * q])));
           smin = fminf(smin, __uint_as_float(ld_agent(&ix[4 * q + 1])));
         }
@@ -612,10 +643,10 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
     (void)block_excl_scan<SNW>(esum, sh.tmp, &tot);
     if (a.P > 1) {
       if (tid == 0) st_agent(&ix[4 * p + 2], tot);
-      group_barrier(grp.bar, (uint32_t)a.P, ++nbar, grp.local, grp.err);
+      const bool ok = group_barrier(grp.bar, (uint32_t)a.P, ++nbar, grp.local, grp.wait);
       if (tid == 0) {
-        uint32_t t = 0;
-        for (int q = 0; q < a.P; ++q) t += ld_agent(&ix[4 * q + 2]);
+        uint32_t t = ok ? 0u : tot;
+        for (int q = 0; q < a.P && ok; ++q) t += ld_agent(&ix[4 * q + 2]);
         sh.bcast[2] = t;
       }
       __syncthreads();
@@ -1085,20 +1116,22 @@ sdkv_status plan_decode(const sdkv_attn_args* a, DecodePlan* p) {
   const size_t A = 256;
   const int64_t N = a->n_atoms, rows = q.rows;
   size_t off = 0;
+  // cleared per call (by the U-table kernel): the status word first (word 0
+  // of the workspace), tickets, barrier counters, exchange words, histograms
+  q.off_zero = 0;
+  q.off_err = off;    off += 4;
+  q.off_ticket = off; off += 8 * 4;
+  q.off_bar = off;    off += (size_t)rows * 2 * 4;
+  q.off_xchg = off;   off += (size_t)rows * q.P * 2 * 4;
+  q.off_ghist = off;  off += (q.P > 1) ? (size_t)rows * 2048 * 4 : 0;
+  off = align_up(off, A);
+  q.zero_bytes = off - q.off_zero;
   q.off_u = off;      off = align_up(off + (size_t)rows * N * 4, A);
   const size_t list = (size_t)rows * q.P * q.chunk * 4;  // per-workgroup regions
   q.off_sel = off;    off = align_up(off + list, A);
   q.off_shigh = off;  off = align_up(off + list, A);
   q.off_wpart = off;  off = align_up(off + (size_t)rows * q.P * N * 4, A);
   q.off_stats = off;  off = align_up(off + (size_t)rows * q.P * 8, A);
-  q.off_zero = off;
-  q.off_ghist = off;  off += (q.P > 1) ? (size_t)rows * 2048 * 4 : 0;
-  q.off_xchg = off;   off += (size_t)rows * q.P * 2 * 4;
-  q.off_bar = off;    off += (size_t)rows * 2 * 4;
-  q.off_err = off;    off += 4;
-  q.off_ticket = off; off += 8 * 4;
-  off = align_up(off, A);
-  q.zero_bytes = off - q.off_zero;
   q.off_opart = off;  off = align_up(off + (size_t)q.nchunks * rows * a->d * 4, A);
   q.off_cand = off;   off = align_up(off + (q.P > 1 ? (size_t)rows * q.P * q.chunk * 4 : 0), A);
   q.off_wtab = off;   off = align_up(off + (q.P > 1 ? (size_t)rows * q.P * 2048 * 4 : 0), A);
@@ -1144,7 +1177,8 @@ sdkv_status launch_decode(const sdkv_attn_args* a, const DecodePlan& p, void* ws
 
   // 1. U table (+ clear the barrier / histogram region)
   UArgs ua;
-  ua.q = (const uint16_t*)a->q;
+  ua.q = a->q;
+  ua.q_f32 = a->q_dtype == SDKV_F32 ? 1 : 0;
   ua.dk = a->dk;
   ua.rows = (int)rows;
   ua.N = a->n_atoms;
@@ -1204,7 +1238,7 @@ sdkv_status launch_decode(const sdkv_attn_args* a, const DecodePlan& p, void* ws
   ra.cand = (uint32_t*)(base + p.off_cand);
   ra.xchg = xchg;
   ra.bar = bar;
-  ra.err = err;
+  ra.wait = wait_ctl(err);
   ra.shared = a->select_mode == SDKV_SELECT_KV ? 1 : 0;
   ra.readb = a->reading == SDKV_READING_B ? 1 : 0;
   ra.vlow = a->val_low;

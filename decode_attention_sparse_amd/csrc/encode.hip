@@ -10,17 +10,22 @@
 //   * screen: every step correlates the workgroup's residuals with all atoms
 //     on the matrix cores (v_mfma_f32_16x16x32_f16). The residual rows are
 //     scaled by a power of two and rounded to fp16; the dictionary is an fp16
-//     copy (exact for bf16 atoms of unit-norm size). Each lane keeps, per
-//     output row it owns, the largest |c| seen in its atom column and that
-//     atom's tile, packed in one word: |c| with its low 12 mantissa bits
-//     replaced by the complement of the tile index, so a single unsigned
-//     max keeps the larger value and, among equal truncated values, the
-//     lower tile. (The truncation, at most 2^-11 of |c|, is well inside the
-//     recheck window below.)
-//   * exact pick: per vector, the 16 column winners whose screened |c| lie
-//     within a window of the best are recomputed in fp32 from the original
-//     dictionary; the largest exact |c| wins, lowest atom index on ties.
-//     The window (2^-7 |r|) is 4x the worst-case screen error bound.
+//     copy (exact for bf16 atoms of unit-norm size). Each lane owns one atom
+//     column (atoms = c mod 16) for the rows it holds and keeps the two
+//     largest screened |c| of that column, each packed in one word: |c| with
+//     its low 12 mantissa bits replaced by the complement of the 16-atom tile
+//     index (and bit 31 marking a filled slot), so unsigned max / median
+//     operations keep the larger values and, among equal truncated values,
+//     the lower tile.
+//   * exact pick: E bounds |exact - screened| for every atom (fp16 rounding
+//     of the residual and, for fp32 dictionaries, of the atoms, plus the
+//     truncation; derived below). Every kept value within 2E of the best is
+//     recomputed in fp32 from the original dictionary; the largest exact |c|
+//     wins, lowest atom index on ties. A column whose second value lies
+//     within E of that winner may hide a third candidate: its atoms are then
+//     all recomputed exactly by the whole wave (rare). Every atom that is not
+//     recomputed is therefore exactly below the winner, so the pick is the
+//     exact fp32 argmax.
 //   * update: g = exact <r, d_a> (fp32), r -= g d_a in fp32.
 #include "sdkv_device.h"
 #include "sdkv_internal.h"
@@ -31,7 +36,7 @@ constexpr int EB = 512;            // threads per workgroup
 constexpr int ENW = EB / 64;       // waves
 constexpr int EROWS = ENW * 64;    // vectors per workgroup (64 per wave)
 constexpr int ECH = 64;            // atoms per LDS chunk
-constexpr int EWIN_SHIFT = 7;      // recheck window = |r| * 2^-7
+constexpr int kPrepBlocks = 256;   // workgroups of the dictionary prep kernel
 
 struct EncArgs {
   const void* x;
@@ -39,6 +44,7 @@ struct EncArgs {
   const void* dict;
   int dict_f32;
   const uint16_t* dh;   // [npad, D] fp16 screen copy
+  const float* dnorm;   // [kPrepBlocks] largest atom norm seen by each prep workgroup
   float* r;             // [n, D] residuals (workspace)
   int64_t n;
   int N, npad, K, klow;
@@ -50,18 +56,59 @@ struct EncArgs {
   int64_t low_ld;
 };
 
-// fp16 screen copy of the dictionary, zero rows past N.
+// fp16 screen copy of the dictionary (zero rows past N) and the largest atom
+// norm: 8 consecutive elements per thread (one 16-byte store), the row's
+// threads reduce its squared norm with lane shuffles, and each workgroup
+// writes the largest norm it saw to dnorm[blockIdx.x].
 __global__ __launch_bounds__(256) void k_prep_dict(const void* dict, int dict_f32, int N,
-                                                   int npad, int D, uint16_t* dh) {
-  const int64_t total = (int64_t)npad * D;
+                                                   int npad, int D, uint16_t* dh, float* dnorm) {
+  __shared__ float s_m[4];
+  const int64_t groups = (int64_t)npad * D / 8;  // D / 8 groups per row (8 or 16 lanes)
+  const int gpr = D / 8;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
-    const int a = (int)(i / D);
-    float v = 0.f;
-    if (a < N)
-      v = dict_f32 ? ((const float*)dict)[i] : bf16_to_f32(((const uint16_t*)dict)[i]);
-    dh[i] = (uint16_t)f32_to_f16_bits(v);
+  float mx = 0.f;
+  // the trip count is the same for every lane of a row's lanes (rows never
+  // straddle a stride: stride and gpr are powers of two with gpr | stride)
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < groups; g += stride) {
+    const int a = (int)(g / gpr);
+    float v[8];
+    if (a < N) {
+      if (dict_f32) {
+        const float4* p = (const float4*)((const float*)dict + g * 8);
+        const float4 x0 = p[0], x1 = p[1];
+        v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
+        v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+      } else {
+        const u32x4 u = *(const u32x4*)((const uint16_t*)dict + g * 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { v[2 * e] = bf16_lo(u[e]); v[2 * e + 1] = bf16_hi(u[e]); }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = 0.f;
+    }
+    u32x4 o;
+    float s2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      o[e] = f32_to_f16_bits(v[2 * e]) | (f32_to_f16_bits(v[2 * e + 1]) << 16);
+      s2 = fmaf(v[2 * e], v[2 * e], s2);
+      s2 = fmaf(v[2 * e + 1], v[2 * e + 1], s2);
+    }
+    *(u32x4*)(dh + g * 8) = o;
+    for (int off = gpr / 2; off > 0; off >>= 1) s2 += __shfl_xor(s2, off, 64);
+    mx = fmaxf(mx, sqrtf(s2));
   }
+  mx = wave_max(mx);
+  if (lane_id() == 0) s_m[wave_id()] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    dnorm[blockIdx.x] = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+}
+
+// median of three (v_med3_u32)
+__device__ __forceinline__ uint32_t med3_u32(uint32_t a, uint32_t b, uint32_t c) {
+  return max(min(a, b), min(max(a, b), c));
 }
 
 template <int D>
@@ -97,13 +144,23 @@ __global__ __launch_bounds__(EB) void k_encode(EncArgs a) {
   constexpr int KS = D / 32;           // MFMA k-steps per 16x16 tile
   constexpr int BP = D + 8;            // LDS row pitch (fp16 elements)
   __shared__ __attribute__((aligned(16))) uint16_t s_b[2][ECH * BP];
-  __shared__ float s_wv[EROWS * 16];
-  __shared__ int32_t s_wi[EROWS * 16];
+  __shared__ uint32_t s_k1[EROWS * 16];  // per row and column: best screened key
+  __shared__ uint32_t s_k2[EROWS * 16];  // and the second best (0: none)
   __shared__ float s_scale[EROWS];
   __shared__ float s_rnorm[EROWS];
+  __shared__ float s_snorm[EROWS];       // |r * scale| from the fp32 residual
+  __shared__ float s_dmax;
 
   const int tid = threadIdx.x, w = wave_id(), l = lane_id();
   const int64_t row0 = (int64_t)blockIdx.x * EROWS;
+
+  // largest atom norm (from the prep kernel's per-workgroup maxima)
+  if (w == 0) {
+    float dm = 0.f;
+    for (int i = l; i < kPrepBlocks; i += 64) dm = fmaxf(dm, a.dnorm[i]);
+    dm = wave_max(dm);
+    if (l == 0) s_dmax = dm;
+  }
 
   // --- init: r = x, |r| ---------------------------------------------------------
   {
@@ -151,7 +208,18 @@ __global__ __launch_bounds__(EB) void k_encode(EncArgs a) {
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       // power-of-two scale putting the row's largest |r| in [1, 2)
       const float sc = (mx > 0.f) ? ldexpf(1.f, min(-ilogbf(mx), 100)) : 1.f;
-      if ((l >> 4) == 0) s_scale[rl] = sc;
+      // |r * sc| (0 exactly when r is zero, else >= 1)
+      float s2 = 0.f;
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s2 = fmaf(vals[s][e] * sc, vals[s][e] * sc, s2);
+      s2 += __shfl_xor(s2, 16, 64);
+      s2 += __shfl_xor(s2, 32, 64);
+      if ((l >> 4) == 0) {
+        s_scale[rl] = sc;
+        s_snorm[rl] = sqrtf(s2);
+      }
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         u32x4 pk;
@@ -163,17 +231,18 @@ __global__ __launch_bounds__(EB) void k_encode(EncArgs a) {
     }
 
     // --- screen sweep over all atoms ------------------------------------------
-    // running best per output: |c| with its low 12 mantissa bits replaced by
-    // the complement of the 16-atom tile index, so one unsigned max keeps the
-    // larger |c| and, among equal truncated values, the lower tile
-    uint32_t bkey[4][4];
+    // the two largest keys per output row and atom column: |c| with its low
+    // 12 mantissa bits replaced by the complement of the 16-atom tile index,
+    // bit 31 set (0 = empty slot), so unsigned order is |c| order and, among
+    // equal truncated values, the lower tile first
+    uint32_t bkey[4][4], bkey2[4][4];
     // the mask lives in a register, so (x & mask) | code is one 3-input op
     uint32_t vmask = 0x7FFFF000u;
     asm volatile("" : "+v"(vmask));
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) bkey[rt][i] = 0u;
+      for (int i = 0; i < 4; ++i) bkey[rt][i] = bkey2[rt][i] = 0u;
 
     constexpr int SEGS = D / 8;                  // 16-byte segments per atom row
     constexpr int LOADS = (ECH * SEGS) / EB;     // 16-byte loads per thread per chunk
@@ -218,7 +287,7 @@ __global__ __launch_bounds__(EB) void k_encode(EncArgs a) {
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) acc[h][rt] = mfma_f16(af[rt][s], bfr[s], acc[h][rt]);
         }
-        const uint32_t tc0 = ~(uint32_t)(c * (ECH / 16) + tt) & 0xFFFu;
+        const uint32_t tc0 = (~(uint32_t)(c * (ECH / 16) + tt) & 0xFFFu) | 0x80000000u;
         const uint32_t tc1 = tc0 - 1u;  // the next tile's code
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
@@ -226,7 +295,11 @@ __global__ __launch_bounds__(EB) void k_encode(EncArgs a) {
           for (int i = 0; i < 4; ++i) {
             const uint32_t k0 = (__float_as_uint(acc[0][rt][i]) & vmask) | tc0;
             const uint32_t k1 = (__float_as_uint(acc[1][rt][i]) & vmask) | tc1;
-            bkey[rt][i] = max(bkey[rt][i], max(k0, k1));
+            const uint32_t b1 = bkey[rt][i];
+            // second largest of {b1, b2, k0, k1} (b1 >= b2): the larger of b2
+            // and the median of (b1, k0, k1)
+            bkey2[rt][i] = max(bkey2[rt][i], med3_u32(b1, k0, k1));
+            bkey[rt][i] = max(b1, max(k0, k1));
           }
       }
       if (c + 1 < nchunks) store_chunk(buf ^ 1);
@@ -239,29 +312,71 @@ __global__ __launch_bounds__(EB) void k_encode(EncArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int rl = w * 64 + rt * 16 + 4 * (l >> 4) + i;
-        s_wv[rl * 16 + (l & 15)] = __uint_as_float(bkey[rt][i] & 0x7FFFF000u);
-        s_wi[rl * 16 + (l & 15)] = (int)((~bkey[rt][i]) & 0xFFFu) * 16 + (l & 15);
+        s_k1[rl * 16 + (l & 15)] = bkey[rt][i];
+        s_k2[rl * 16 + (l & 15)] = bkey2[rt][i];
       }
     __syncthreads();
 
     // --- exact pick + residual update: one thread per vector ----------------------
+    // Error bound E (scaled units) of a kept key against the exact value:
+    // fp16 rounding of r*sc (<= 2^-11 |r sc| |d|), of fp32 atoms (<= 2^-11
+    // |r sc| |d|), truncation to 11 mantissa bits (<= 2^-11 |c|) and fp32
+    // sums (~2^-17 |r sc| |d|): E = 2^-9 |r sc| dmax (bf16 atoms, twice the
+    // bound) or 2^-8 |r sc| dmax (fp32 atoms, 2.6x), dmax >= 1 the largest
+    // atom norm.
     {
       const int rl = tid;
       const int64_t rowg = row0 + rl;
-      if (rowg < a.n) {
-        float* rr = a.r + rowg * D;
+      const bool live = rowg < a.n;
+      float* rr = a.r + min(rowg, a.n - 1) * D;
+      const float sc = s_scale[rl];
+      const float E = ldexpf(s_snorm[rl] * fmaxf(s_dmax, 1.f), a.dict_f32 ? -8 : -9);
+      float bc = 0.f, babs = -1.f;
+      int ba = 0x7FFFFFFF;
+      uint32_t fb = 0;  // columns to rescan: bit c
+      if (live && s_snorm[rl] > 0.f) {
         float vmax = 0.f;
-        for (int c = 0; c < 16; ++c) vmax = fmaxf(vmax, s_wv[rl * 16 + c]);
-        const float win = ldexpf(s_rnorm[rl] * s_scale[rl], -EWIN_SHIFT);
-        float bc = 0.f, babs = -1.f;
-        int ba = 0x7FFFFFFF;
+        for (int c = 0; c < 16; ++c) vmax = fmaxf(vmax, __uint_as_float(s_k1[rl * 16 + c] & 0x7FFFF000u));
+        const float cut = vmax - 2.f * E;
+        for (int c = 0; c < 16; ++c)
+          for (int q = 0; q < 2; ++q) {
+            const uint32_t k = q ? s_k2[rl * 16 + c] : s_k1[rl * 16 + c];
+            const int atom = (int)((~k) & 0xFFFu) * 16 + c;
+            if (k == 0u || atom >= a.N || __uint_as_float(k & 0x7FFFF000u) < cut) continue;
+            const float cx = exact_corr<D>(a, rr, atom);
+            const float ax = fabsf(cx);
+            if (ax > babs || (ax == babs && atom < ba)) { babs = ax; bc = cx; ba = atom; }
+          }
+        // a column whose second key could be within E of the winner may hide
+        // further candidates below it
+        const float lim = babs * sc;
         for (int c = 0; c < 16; ++c) {
-          const int atom = s_wi[rl * 16 + c];
-          if (atom >= a.N || s_wv[rl * 16 + c] < vmax - win) continue;
-          const float cx = exact_corr<D>(a, rr, atom);
-          const float ax = fabsf(cx);
-          if (ax > babs || (ax == babs && atom < ba)) { babs = ax; bc = cx; ba = atom; }
+          const uint32_t k = s_k2[rl * 16 + c];
+          if (k != 0u && __uint_as_float(k & 0x7FFFF000u) + E >= lim) fb |= 1u << c;
         }
+      }
+      // wave-cooperative rescans: every atom of the column, exact fp32
+      for (uint64_t pend = __ballot(fb != 0u); pend; pend = __ballot(fb != 0u)) {
+        const int ln = __builtin_ctzll(pend);
+        const uint32_t fbl = (uint32_t)__builtin_amdgcn_readlane((int)fb, ln);
+        const int c = __builtin_ctz(fbl);
+        const float* rv = a.r + (row0 + w * 64 + ln) * D;
+        uint64_t best = 0;
+        for (int atom = c + 16 * l; atom < a.N; atom += 16 * 64) {
+          const float ax = fabsf(exact_corr<D>(a, rv, atom));
+          const uint64_t key = ((uint64_t)__float_as_uint(ax) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)atom);
+          best = best > key ? best : key;
+        }
+        best = wave_max_u64(best);
+        if (l == ln) {
+          const float ax = __uint_as_float((uint32_t)(best >> 32));
+          const int atom = (int)(0xFFFFFFFFu - (uint32_t)best);
+          if (ax > babs || (ax == babs && atom < ba)) { babs = ax; ba = atom; bc = exact_corr<D>(a, rr, atom); }
+          fb &= ~(1u << c);
+        }
+      }
+      if (live) {
+        // a zero residual: every correlation is 0, atom 0 wins the tie
         if (ba == 0x7FFFFFFF) { ba = 0; bc = exact_corr<D>(a, rr, 0); }
         // update with vector loads and stores, in element order
         float nrm = 0.f;
@@ -374,25 +489,6 @@ __device__ __forceinline__ float key_coef(uint64_t k) {
 __device__ __forceinline__ int key_atom(uint64_t k) { return 0xFFFF - (int)(((uint32_t)k >> 16) & 0xFFFFu); }
 __device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
-// r (fp32) as hi + mid + lo bf16 parts, exactly: each part is the bf16
-// rounding (v_cvt_pk_bf16_f32) of what the previous ones left, and the
-// remainder after two 8-bit parts fits the third.
-typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-typedef float f32x2v __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ void split3_bf16(const float (&v)[8], u32x4& hi, u32x4& mid, u32x4& lo) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const f32x2v x = {v[2 * e], v[2 * e + 1]};
-    const bf16x2v h = __builtin_convertvector(x, bf16x2v);
-    const f32x2v r1 = x - __builtin_convertvector(h, f32x2v);
-    const bf16x2v m = __builtin_convertvector(r1, bf16x2v);
-    const f32x2v r2 = r1 - __builtin_convertvector(m, f32x2v);
-    hi[e] = __builtin_bit_cast(uint32_t, h);
-    mid[e] = __builtin_bit_cast(uint32_t, m);
-    lo[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r2, bf16x2v));
-  }
-}
-
 __device__ __forceinline__ void split3_bf16x4(float4 v, uint2& hi, uint2& mid, uint2& lo) {
   const float a[8] = {v.x, v.y, v.z, v.w, 0.f, 0.f, 0.f, 0.f};
   u32x4 h, m, o;
@@ -457,6 +553,7 @@ __global__ __launch_bounds__(ESB) void k_small(SmallLaunch L, int step) {
   __shared__ uint64_t s_key[NW * NV];
   __shared__ float s_g[NV];
   __shared__ int s_a[NV];
+  __shared__ float s_rn[NV];   // |r_step| per vector (bf16 dictionary path)
   const SmallArgs a = blockIdx.y ? L.p[1] : L.p[0];
   if constexpr (OMP) {
     if (step == L.K + 1) {
@@ -641,6 +738,11 @@ __global__ __launch_bounds__(ESB) void k_small(SmallLaunch L, int step) {
         *(uint2*)&s_p[v * RPB + kk] = hi;
         *(uint2*)&s_p[(NV + v) * RPB + kk] = mid;
         *(uint2*)&s_p[(2 * NV + v) * RPB + kk] = lo;
+        // |r|: a vector's D/4 groups sit in D/4 consecutive lanes
+        float n2 = rr[j].x * rr[j].x;
+        n2 = fmaf(rr[j].y, rr[j].y, n2); n2 = fmaf(rr[j].z, rr[j].z, n2); n2 = fmaf(rr[j].w, rr[j].w, n2);
+        n2 = vec_sum<D>(n2);
+        if (kk == 0) s_rn[v] = sqrtf(n2);
       }
       if (wg == 0 && corr) rq[gq] = rr[j];
     }
@@ -652,7 +754,35 @@ __global__ __launch_bounds__(ESB) void k_small(SmallLaunch L, int step) {
     if constexpr (!F32D) {
       // --- correlations on the matrix cores: C[atom][vector] over 16-vector
       // tiles, r split exactly into three bf16 parts (every product exact,
-      // fp32 accumulation); per wave the best of its 32 atoms per vector ------
+      // fp32 accumulation); per wave the best of its 32 atoms per vector.
+      // The matrix cores' accumulation order and rounding are not the same
+      // for an atom and its negation, so the wave's best and every atom
+      // within 2 eps of it (eps = 2^-13 |r| |d|max bounds the matrix-core
+      // sum's error: 12 accumulations of 32 exact products) are recomputed
+      // as a sequential fp32 dot product, which a duplicated or negated atom
+      // reproduces exactly; the winners compare those values. ---------------
+      // largest norm of this wave's 32 atoms
+      float dmx;
+      {
+        float n2[2] = {0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int k = 0; k < KS; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float lo = bf16_lo(bt[t][k][e]), hi = bf16_hi(bt[t][k][e]);
+              n2[t] = fmaf(lo, lo, fmaf(hi, hi, n2[t]));
+            }
+        float m = 0.f;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          float x = n2[t] + __shfl_xor(n2[t], 16, 64);
+          x += __shfl_xor(x, 32, 64);
+          m = fmaxf(m, x);
+        }
+        dmx = sqrtf(wave_max(m));
+      }
       for (int v0 = 0; v0 < n; v0 += 16) {
         f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         const int vr = min(v0 + (l & 15), n - 1);  // columns past n are never stored
@@ -685,8 +815,48 @@ __global__ __launch_bounds__(ESB) void k_small(SmallLaunch L, int step) {
           const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(k >> 32), o, 64);
           k = max_u64(k, ((uint64_t)hi << 32) | lo);
         }
+        // exact values of the candidates
+        const float thr = __uint_as_float((uint32_t)(k >> 32)) - ldexpf(s_rn[vr] * dmx, -12);
+        uint32_t cm = 0;  // candidates among this lane's 8 values: bit 4t + i
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int at = wg * ECHS + 32 * w + 16 * t + 4 * (l >> 4) + i;
+            if (at < L.N && fabsf(acc[t][i]) >= thr) cm |= 1u << (4 * t + i);
+          }
+        uint64_t ke = 0;
+        const uint16_t* rp = s_p + vr * RPB;
+        while (cm) {
+          const int b = __builtin_ctz(cm);
+          cm &= cm - 1u;
+          const int at = wg * ECHS + 32 * w + 16 * (b >> 2) + 4 * (l >> 4) + (b & 3);
+          const u32x4* dp = (const u32x4*)((const uint16_t*)a.dict + (int64_t)at * D);
+          float ce = 0.f;
+#pragma unroll 2
+          for (int k8 = 0; k8 < D / 8; ++k8) {
+            const u32x4 dv = dp[k8];
+            const u32x4 h = *(const u32x4*)&rp[8 * k8];
+            const u32x4 m = *(const u32x4*)&rp[NV * RPB + 8 * k8];
+            const u32x4 o = *(const u32x4*)&rp[2 * NV * RPB + 8 * k8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float r0 = (bf16_lo(h[e]) + bf16_lo(m[e])) + bf16_lo(o[e]);
+              const float r1 = (bf16_hi(h[e]) + bf16_hi(m[e])) + bf16_hi(o[e]);
+              ce = fmaf(bf16_lo(dv[e]), r0, ce);
+              ce = fmaf(bf16_hi(dv[e]), r1, ce);
+            }
+          }
+          ke = max_u64(ke, win_key(ce, at));
+        }
+#pragma unroll
+        for (int o = 16; o <= 32; o <<= 1) {
+          const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)ke, o, 64);
+          const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(ke >> 32), o, 64);
+          ke = max_u64(ke, ((uint64_t)hi << 32) | lo);
+        }
         const int v = v0 + l;
-        if (l < 16 && v < n) s_key[w * NV + v] = k;
+        if (l < 16 && v < n) s_key[w * NV + v] = ke;
       }
       __syncthreads();
       // the workgroup's winner per vector: the best of the waves' winners
@@ -777,6 +947,7 @@ sdkv_status plan_encode(const sdkv_encode_args* a, EncodePlan* p) {
   q.nwg = (a->n + EROWS - 1) / EROWS;
   size_t off = 0;
   q.off_dh = off;  off = align_up(off + (size_t)q.npad * a->d * 2, 256);
+  q.off_dn = off;  off = align_up(off + (size_t)kPrepBlocks * 4, 256);
   q.off_r = off;   off = align_up(off + (size_t)a->n * a->d * 4, 256);
   q.total = off;
   *p = q;
@@ -880,19 +1051,16 @@ sdkv_status launch_encode(const sdkv_encode_args* a, const EncodePlan& p, void* 
   const int dict_f32 = a->dict_dtype == SDKV_F32;
   void* const* ev = a->stage_events;
   if (!record_stage(ev, 0, stream)) return SDKV_ERR_DEVICE;
-  {
-    const int64_t total = (int64_t)p.npad * a->d;
-    const int grid = (int)std::min<int64_t>(2048, (total + 255) / 256);
-    hipLaunchKernelGGL(k_prep_dict, dim3(grid), dim3(256), 0, stream, a->dict, dict_f32,
-                       a->n_atoms, p.npad, a->d, dh);
-    if (hipGetLastError() != hipSuccess) return SDKV_ERR_DEVICE;
-  }
+  hipLaunchKernelGGL(k_prep_dict, dim3(kPrepBlocks), dim3(256), 0, stream, a->dict, dict_f32,
+                     a->n_atoms, p.npad, a->d, dh, (float*)(base + p.off_dn));
+  if (hipGetLastError() != hipSuccess) return SDKV_ERR_DEVICE;
   EncArgs e;
   e.x = a->x;
   e.x_f32 = a->x_dtype == SDKV_F32;
   e.dict = a->dict;
   e.dict_f32 = dict_f32;
   e.dh = dh;
+  e.dnorm = (const float*)(base + p.off_dn);
   e.r = (float*)(base + p.off_r);
   e.n = a->n;
   e.N = a->n_atoms;

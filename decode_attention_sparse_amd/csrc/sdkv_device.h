@@ -55,6 +55,25 @@ __device__ __forceinline__ float key_float(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
+// fp32 values as hi + mid + lo bf16 parts, exactly: each part is the bf16
+// rounding (v_cvt_pk_bf16_f32) of what the previous ones left, and the
+// remainder after two 8-bit parts fits the third.
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split3_bf16(const float (&v)[8], u32x4& hi, u32x4& mid, u32x4& lo) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const f32x2v x = {v[2 * e], v[2 * e + 1]};
+    const bf16x2v h = __builtin_convertvector(x, bf16x2v);
+    const f32x2v r1 = x - __builtin_convertvector(h, f32x2v);
+    const bf16x2v m = __builtin_convertvector(r1, bf16x2v);
+    const f32x2v r2 = r1 - __builtin_convertvector(m, f32x2v);
+    hi[e] = __builtin_bit_cast(uint32_t, h);
+    mid[e] = __builtin_bit_cast(uint32_t, m);
+    lo[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r2, bf16x2v));
+  }
+}
+
 // --- wave / block primitives ------------------------------------------------
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 // wave index as a scalar (uniform) value
@@ -199,54 +218,69 @@ __device__ __forceinline__ float block_sum(float v, float* tmp) {
 // releases (if it has not), arrives at the row's second counter, waits for
 // all P there and acquires: exact either way, fence-free when the placement
 // holds. Without `local` every workgroup releases before arriving and
-// acquires after the wait. `round` counts this row's barriers (1, 2, ...). bar[0] / bar[1] are
-// the row's counters, zeroed before launch. Every thread first completes its
-// own memory operations (s_waitcnt) and meets the others at the workgroup
-// barrier; one thread does the rest. The spins are bounded: after ~2^24
-// polls the workgroup records the failure in *err and continues, so no wave
-// can wait forever.
+// acquires after the wait. `round` counts this row's barriers (1, 2, ...).
+// bar[0] / bar[1] are the row's counters, zeroed before launch. Every thread
+// first completes its own memory operations (s_waitcnt) and meets the others
+// at the workgroup barrier; one thread does the rest. The spins are bounded:
+// after w.limit polls the workgroup records the failure in *w.err (the
+// status word the host reads after the call) and goes on, so no wave can
+// wait forever; the barrier then returns false to every thread, and callers
+// stop using exchanged data. w.extra raises every arrival target (0 in
+// normal use: the host sets it only to exercise that path).
+struct WaitCtl {
+  uint32_t* err;     // status word: 1 once any wait gave up
+  uint32_t limit;    // polls before giving up
+  uint32_t extra;    // added to every arrival target
+};
 __device__ __forceinline__ uint32_t hw_xcc_id() {
   return (uint32_t)__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 0xFu;  // HW_REG_XCC_ID
 }
 __device__ __forceinline__ bool spin_until(uint32_t* ctr, uint32_t mask, uint32_t target,
-                                           uint32_t* err, uint32_t* last) {
+                                           const WaitCtl& w, uint32_t* last) {
   uint32_t spins = 0, v;
+  bool ok = true;
   while (((v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) & mask) < target) {
     __builtin_amdgcn_s_sleep(1);
-    if (++spins > (1u << 24)) {
-      __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (++spins > w.limit) {
+      __hip_atomic_store(w.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ok = false;
       break;
     }
   }
   *last = v;
-  return true;
+  return ok;
 }
-__device__ __forceinline__ void group_barrier(uint32_t* bar, uint32_t P, uint32_t round,
-                                              bool local, uint32_t* err) {
+__device__ __forceinline__ bool group_barrier(uint32_t* bar, uint32_t P, uint32_t round,
+                                              bool local, const WaitCtl& w) {
+  __shared__ uint32_t s_ok;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  const uint32_t target = P * round + w.extra;
   if (threadIdx.x == 0 && !local) {
     // rows spread over XCDs: everyone releases, arrives, waits, acquires
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __hip_atomic_fetch_add(&bar[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     uint32_t v;
-    spin_until(&bar[0], 0xFFFFu, P * round, err, &v);
+    const bool ok = spin_until(&bar[0], 0xFFFFu, target, w, &v);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    s_ok = ok;
   } else if (threadIdx.x == 0) {
     const bool remote = hw_xcc_id() != (blockIdx.x & 7u);
     if (remote) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __hip_atomic_fetch_add(&bar[0], 1u | ((uint32_t)remote << 16), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     uint32_t v;
-    spin_until(&bar[0], 0xFFFFu, P * round, err, &v);
+    bool ok = spin_until(&bar[0], 0xFFFFu, target, w, &v);
     if ((v >> 16) != 0u) {
       if (!remote) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
       __hip_atomic_fetch_add(&bar[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      spin_until(&bar[1], 0xFFFFFFFFu, P * round, err, &v);
+      ok = spin_until(&bar[1], 0xFFFFFFFFu, target, w, &v) && ok;
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
+    s_ok = ok;
   }
   __syncthreads();
+  return s_ok != 0u;
 }
 
 __device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {

@@ -7,6 +7,7 @@
 #include <algorithm>
 
 #include "../../include/sdkv.h"
+#include "sdkv_device.h"
 
 namespace sdkv {
 
@@ -67,7 +68,7 @@ struct EncodePlan {
   int npad = 0;          // atoms padded to the sweep tile
   int rows_per_wg = 0;
   int64_t nwg = 0;
-  size_t off_dh = 0, off_r = 0, off_rh = 0, off_scale = 0;
+  size_t off_dh = 0, off_dn = 0, off_r = 0, off_rh = 0, off_scale = 0;
   int small = 0;         // n <= 64: fp32-accurate pursuit over the device
   int G = 0;             // small path: workgroups (atom slices)
   size_t off_part = 0;   // small path: per-workgroup winners [2][G][n]
@@ -81,12 +82,20 @@ sdkv_status launch_encode_pair(const sdkv_encode_args* a0, const EncodePlan& p0,
                                hipStream_t stream);
 sdkv_status launch_encode(const sdkv_encode_args* a, const EncodePlan& p, void* ws,
                           hipStream_t stream);
+// Validation and plans of a paired small encode (sdkv_encode_pair): the
+// second problem's scratch starts at byte off1, total bytes in *total.
+sdkv_status plan_pair(const sdkv_encode_args* a0, const sdkv_encode_args* a1,
+                      EncodePlan* p0, EncodePlan* p1, size_t* off1, size_t* total);
 
 // Records caller-provided timing event i on `stream` (no-op without events).
 inline bool record_stage(void* const* ev, int i, hipStream_t stream) {
   if (!ev) return true;
   return hipEventRecord((hipEvent_t)ev[i], stream) == hipSuccess;
 }
+
+// Bounds of the kernels' cross-workgroup waits, with `err` (workspace word
+// 0) as the status word: the normal bound, or what sdkv_test_set_wait set.
+WaitCtl wait_ctl(uint32_t* err);
 
 // Largest number of co-resident workgroups for a kernel on the current device.
 sdkv_status coresident_blocks(const void* kernel, int threads, size_t dyn_lds, int* out);

@@ -37,7 +37,7 @@ struct SelGroup {
   uint32_t* xchg;     // [P][2]
   uint32_t* bar;      // [2] barrier counters, zeroed before launch
   bool local;         // all workgroups of the row are in one id % 8 class
-  uint32_t* err;      // set to 1 if a barrier wait gave up
+  WaitCtl wait;       // status word and bounds of the barrier waits
   uint32_t* cand;     // [P][cap] candidate keys of each workgroup (P > 1)
   int64_t cap;        // candidate slots per workgroup (>= keys per workgroup)
 };
@@ -156,7 +156,11 @@ __device__ __forceinline__ Mask radix_select_coop(const uint32_t (&key)[SPT], ui
     const uint32_t c = sh.hist[i];
     if (c) atomicAdd(&g.ghist[i], c);
   }
-  group_barrier(g.bar, (uint32_t)g.P, bar_base + 1u, g.local, g.err);
+  if (!group_barrier(g.bar, (uint32_t)g.P, bar_base + 1u, g.local, g.wait)) {
+    // a wait gave up (reported in the status word): select nothing
+    *offset = 0; *count = 0; *tau_out = 0;
+    return 0;
+  }
   for (int i = tid; i < 2048; i += SB) sh.hist[i] = ld_agent(&g.ghist[i]);
   __syncthreads();
   uint32_t gt1;
@@ -184,7 +188,10 @@ __device__ __forceinline__ Mask radix_select_coop(const uint32_t (&key)[SPT], ui
     st_agent(&g.xchg[2 * g.p], tna);
     st_agent(&g.xchg[2 * g.p + 1], tnc);
   }
-  group_barrier(g.bar, (uint32_t)g.P, bar_base + 2u, g.local, g.err);
+  if (!group_barrier(g.bar, (uint32_t)g.P, bar_base + 2u, g.local, g.wait)) {
+    *offset = 0; *count = 0; *tau_out = 0;
+    return 0;
+  }
 
   // --- every workgroup: counts per workgroup, then all candidates ------------
   // s_qcnt layout: [0,P) above-bin counts A_q, [P,2P) candidate counts c_q,
@@ -490,7 +497,13 @@ __device__ __forceinline__ bool sample_window_select(const uint32_t (&key)[SPT],
 #pragma unroll
   for (int j = 0; j < SPT; ++j)
     if (pos[j] != 0xFFFFFFFFu) st_agent(&mywl[sh.hist[pos[j] >> 16] + (pos[j] & 0xFFFFu)], key[j]);
-  group_barrier(g.bar, (uint32_t)P, 1u, g.local, g.err);
+  if (!group_barrier(g.bar, (uint32_t)P, 1u, g.local, g.wait)) {
+    // a wait gave up (reported in the status word): select nothing, and
+    // report the select as done so that no further exchange is attempted
+    *tau_out = 0;
+    *sel_out = 0;
+    return true;
+  }
   // --- threshold bin from the counts above and the summed count tables --------
   if (tid < P) s_qcnt[tid] = ld_agent(&g.xchg[2 * tid]);
   {

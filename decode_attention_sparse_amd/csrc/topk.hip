@@ -19,7 +19,7 @@ struct TopkArgs {
   uint32_t* cand;   // [rows, P, chunk]
   uint32_t* xchg;   // [rows, P, 2]
   uint32_t* bar;    // [rows, 2] barrier counters
-  uint32_t* err;
+  WaitCtl wait;     // status word (workspace word 0) and wait bounds
   uint32_t* ticket; // [8] workgroup start-order counters (see k_rows)
   int xcd_map;
 };
@@ -57,7 +57,7 @@ __global__ __launch_bounds__(SB) void k_topk(TopkArgs a) {
   grp.xchg = a.xchg + row * a.P * 2;
   grp.bar = a.bar + 2 * (int64_t)row;
   grp.local = a.xcd_map != 0;
-  grp.err = a.err;
+  grp.wait = a.wait;
   grp.cand = a.cand + row * a.P * a.chunk;
   grp.cap = a.chunk;
   uint32_t offset, count, tau;
@@ -92,11 +92,12 @@ sdkv_status plan_topk(int64_t rows, int64_t n, int64_t k, TopkPlan* p) {
   q.spt = topk_spt(q.chunk);
   if (q.spt == 0) return SDKV_ERR_UNSUPPORTED;
   size_t off = 0;
-  q.off_ghist = off;  off += (q.P > 1) ? (size_t)rows * 2048 * 4 : 0;
-  q.off_xchg = off;   off += (size_t)rows * q.P * 2 * 4;
-  q.off_bar = off;    off += (size_t)rows * 2 * 4;
+  // cleared per call: the status word first (word 0 of the workspace)
   q.off_err = off;    off += 4;
   q.off_ticket = off; off += 8 * 4;
+  q.off_bar = off;    off += (size_t)rows * 2 * 4;
+  q.off_xchg = off;   off += (size_t)rows * q.P * 2 * 4;
+  q.off_ghist = off;  off += (q.P > 1) ? (size_t)rows * 2048 * 4 : 0;
   q.zero_bytes = align_up(off, 256);
   q.off_cand = q.zero_bytes;
   q.total = q.off_cand + align_up(q.P > 1 ? (size_t)rows * q.P * q.chunk * 4 : 0, 256);
@@ -130,7 +131,7 @@ sdkv_status launch_topk(const float* scores, int64_t ld, int32_t* idx, float* th
   a.ghist = (uint32_t*)(base + p.off_ghist);
   a.xchg = (uint32_t*)(base + p.off_xchg);
   a.bar = (uint32_t*)(base + p.off_bar);
-  a.err = (uint32_t*)(base + p.off_err);
+  a.wait = wait_ctl((uint32_t*)(base + p.off_err));
   a.cand = (uint32_t*)(base + p.off_cand);
   const void* kfn = pick_topk_kernel(p.spt);
   if (!kfn) return SDKV_ERR_UNSUPPORTED;

@@ -23,9 +23,24 @@
  *    is written. Kernel launch failures are reported as SDKV_ERR_DEVICE
  *    (faults inside an already-enqueued kernel surface at the caller's next
  *    synchronisation, as for any HIP kernel). No C++ exception crosses the
- *    ABI. Calls are reentrant and thread-safe (the only process-wide state
- *    is a mutex-guarded cache of per-device kernel occupancy); two calls
- *    that share a workspace must not overlap in time.
+ *    ABI. Calls are reentrant and thread-safe on the host (the only
+ *    process-wide state is a mutex-guarded cache of per-device kernel
+ *    occupancy and the wait bounds of sdkv_test_set_wait); two calls that
+ *    share a workspace must not overlap in time.
+ *  - Co-residency. sdkv_decode_attn and sdkv_select_topk split long rows
+ *    over several workgroups that wait for each other inside one launch
+ *    (no cooperative launch). The host checks that the device can hold a
+ *    row's workgroups at once, which assumes the call has the GPU to itself:
+ *    concurrent work on other streams that occupies compute units (another
+ *    of these calls, a persistent communication kernel) can leave a row's
+ *    workgroups unable to meet. Such calls are unsupported. The waits are
+ *    bounded (about half a second), so nothing hangs: a wait that gives up
+ *    sets the workspace's status word (below) and the results of the call
+ *    are then unreliable.
+ *  - Status word. Word 0 (uint32) of the workspace of sdkv_decode_attn and
+ *    sdkv_select_topk is cleared by the call and, once its work has
+ *    completed on the stream, holds 0, or 1 if a cross-workgroup wait gave
+ *    up (report it as SDKV_ERR_WAIT). Read it after synchronising.
  *  - Inputs must be finite. Code indices must be < n_atoms; other indices
  *    give unspecified (but in-bounds) results.
  *  - Dictionaries, encode inputs x, queries q and workspaces must start at
@@ -48,7 +63,7 @@ extern "C" {
 #define SDKV_API
 #endif
 
-#define SDKV_ABI_VERSION 7
+#define SDKV_ABI_VERSION 8
 
 typedef int32_t sdkv_status;
 #define SDKV_OK 0
@@ -58,6 +73,8 @@ typedef int32_t sdkv_status;
 #define SDKV_ERR_UNSUPPORTED 4 /* valid, but outside what the kernels take */
 #define SDKV_ERR_WORKSPACE 5   /* workspace smaller than the query result  */
 #define SDKV_ERR_DEVICE 6      /* a HIP runtime call or launch failed      */
+#define SDKV_ERR_WAIT 7        /* (status word) a cross-workgroup wait gave
+                                  up; never returned by a call itself       */
 
 /* dtype codes */
 #define SDKV_BF16 0
@@ -70,9 +87,11 @@ typedef int32_t sdkv_status;
  *     r = x;  for k < K:  a_k = argmax_a |<r, d_a>|  (lowest a on ties),
  *                          g_k = <r, d_{a_k}>,  r -= g_k d_{a_k}.
  * Atoms are expected to have unit norm (the coefficient is not divided by
- * |d|^2). g_k and the residual are fp32. For n > 64 vectors the argmax is
- * found with an fp16 matrix-core screen of all atoms followed by an exact
- * fp32 re-check of the best candidates. For n <= 64 (a decode step's new
+ * |d|^2). g_k and the residual are fp32. For n > 64 vectors an fp16
+ * matrix-core screen of all atoms is followed by an exact fp32
+ * recomputation of every atom the screen cannot rule out (the screen's
+ * error is bounded from its fp16 rounding and the largest atom norm), so
+ * the pick is the argmax of the exact fp32 correlations. For n <= 64 (a decode step's new
  * tokens, which the cache appends as codes: review page, Strengths, on
  * write endurance) every correlation is computed to fp32 accuracy with the
  * atoms spread over the whole device (bf16 dictionaries: the residual split
@@ -161,7 +180,9 @@ SDKV_API sdkv_status sdkv_encode_pair(const sdkv_encode_args* key, const sdkv_en
  * Unselected tokens do not enter the softmax.
  * ---------------------------------------------------------------------- */
 typedef struct sdkv_attn_args {
-  const void* q;        /* [B, Hq, d] queries; q_dtype must be SDKV_BF16  */
+  const void* q;        /* [B, Hq, d] queries, q_dtype SDKV_BF16 or
+                           SDKV_F32 (fp32 values are split exactly into
+                           three bf16 parts on the matrix cores)          */
   int32_t q_dtype;
   const void* dk;       /* [n_atoms, d] key dictionary, dict_dtype        */
   const void* dv;       /* [n_atoms, d] value dictionary, dict_dtype      */
@@ -278,6 +299,14 @@ SDKV_API sdkv_status sdkv_select_topk(const float* scores, int64_t rows, int64_t
 
 SDKV_API const char* sdkv_status_str(sdkv_status s);
 SDKV_API int32_t sdkv_abi_version(void);
+
+/* Test hook, for tests of the wait-failure path only: every later call's
+ * cross-workgroup waits give up after `polls` polls (0 restores the normal
+ * bound) and wait for `extra` more arrivals than exist (0 in normal use).
+ * With extra > 0 every wait gives up, the kernels select nothing from
+ * exchanged data and still exit normally, and the status word reads 1.
+ * Process-wide; not for concurrent use with other calls. */
+SDKV_API void sdkv_test_set_wait(uint32_t polls, uint32_t extra);
 
 #ifdef __cplusplus
 }

@@ -206,7 +206,7 @@ def decode_attn(q, dk, dv, key_codes, val_codes, klow: int, khigh: int,
     oracle.int_softmax (review page, Summary and Strengths: token-wise INT16
     requantization, integer polynomial exp, shift guards, fixed-point
     reciprocal) applied to s_high rounded to fp32, the precision in which
-    the scores reach the requantization; p = p_int / 2^15 and w, out follow
+    the scores reach the requantization; p = p_int / 2^30 and w, out follow
     in fp64. `s_high_in` (optional [B,Hq,m], with `sel`) supplies those fp32
     scores instead, so the integer steps can be checked bit for bit on
     another implementation's scores. The result then also holds p_int.

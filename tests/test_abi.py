@@ -20,16 +20,16 @@ def declared_symbols():
 def test_library_exports_every_declared_symbol():
     lib = sd.lib()
     names = declared_symbols()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.sdkv_abi_version() == 7
+    assert lib.sdkv_abi_version() == 8
 
 
 def test_status_strings():
     lib = sd.lib()
-    for s in range(7):
-        assert lib.sdkv_status_str(s)
+    for s in range(8):
+        assert lib.sdkv_status_str(s) != b"unknown status"
     assert lib.sdkv_status_str(99) == b"unknown status"
 
 
@@ -75,7 +75,6 @@ def test_decode_workspace_query():
     ("top_num", 0, sd.SDKV_ERR_SHAPE), ("top_num", 11, sd.SDKV_ERR_SHAPE),
     ("n_atoms", 70000, sd.SDKV_ERR_SHAPE), ("scale", float("inf"), sd.SDKV_ERR_SHAPE),
     ("q_dtype", 7, sd.SDKV_ERR_DTYPE), ("dict_dtype", -1, sd.SDKV_ERR_DTYPE),
-    ("q_dtype", sd.SDKV_F32, sd.SDKV_ERR_UNSUPPORTED),
     ("n_atoms", 40000, sd.SDKV_ERR_UNSUPPORTED),
     ("code_stride", 15, sd.SDKV_ERR_SHAPE), ("code_stride", -32, sd.SDKV_ERR_SHAPE),
     ("code_stride", 65537, sd.SDKV_ERR_SHAPE),
@@ -251,3 +250,75 @@ def test_omp_encoder_limits():
         assert lib.sdkv_encode_workspace(ctypes.byref(c), ctypes.byref(nb)) == status
     k, v = good_enc(n=8), good_enc(n=8, algorithm=sd.SDKV_ENCODE_OMP)
     assert lib.sdkv_encode_pair_workspace(ctypes.byref(k), ctypes.byref(v), ctypes.byref(nb)) == sd.SDKV_ERR_SHAPE
+
+
+def test_fp32_queries_accepted():
+    st, nb = ws_status(good_attn(q_dtype=sd.SDKV_F32))
+    assert st == 0 and nb > 0
+
+
+def test_status_word_is_workspace_word_zero():
+    """The status word the header documents is word 0 of the workspace, and
+    the binding turns a nonzero word into SdkvError(SDKV_ERR_WAIT). Checked
+    on a host-memory stand-in for a workspace (no kernel runs here)."""
+    import torch
+    txt = open(sd.HEADER).read()
+    assert "Word 0 (uint32) of the workspace" in txt
+    assert re.search(r"#define SDKV_ERR_WAIT 7\b", txt)
+    ws = sd.Workspace(device="cpu")
+    assert ws.status() == 0
+    ws.buf = torch.zeros(256, dtype=torch.uint8)
+    ws.check()
+    ws.buf[0] = 1
+    assert ws.status() == 1
+    with pytest.raises(sd.SdkvError) as e:
+        ws.check("probe")
+    assert e.value.status == sd.SDKV_ERR_WAIT
+    assert b"gave up" in sd.lib().sdkv_status_str(sd.SDKV_ERR_WAIT)
+    ws.buf[0] = 0
+    ws.buf[3] = 1
+    assert ws.status() == 1 << 24
+
+
+def test_temporary_workspace_kept_for_the_launch_stream(monkeypatch):
+    """A workspace the binding makes for one call is returned to the caller
+    (kept alive across the C call) and tied to a non-current launch stream
+    with record_stream, so the caching allocator cannot hand its memory to
+    other work before that stream has finished with it."""
+    recorded = []
+
+    class FakeBuf:
+        def __init__(self, n):
+            self.n = n
+
+        def numel(self):
+            return self.n
+
+        def data_ptr(self):
+            return 4096
+
+        def record_stream(self, st):
+            recorded.append(st)
+
+    class FakeStream:
+        pass
+
+    class FakeCuda:
+        @staticmethod
+        def current_stream():
+            return "current"
+
+    class FakeTorch:
+        cuda = FakeCuda
+
+    monkeypatch.setattr(sd.Workspace, "get", lambda self, n: FakeBuf(n))
+    monkeypatch.setattr(sd, "_torch", lambda: FakeTorch)
+    other = FakeStream()
+    ws, ptr, n = sd._ws(None, 1000, other)
+    assert isinstance(ws, sd.Workspace) and ptr == 4096 and n == 1000
+    assert recorded == [other]
+    ws2, _, _ = sd._ws(None, 1000, "current")
+    assert recorded == [other]
+    mine = sd.Workspace()
+    ws3, _, _ = sd._ws(mine, 1000, other)
+    assert ws3 is mine and recorded == [other]

@@ -179,10 +179,12 @@ def test_llama_batch8_32k_full_size():
     compare(case, run_gpu(case))
 
 
-@pytest.mark.parametrize("layer", [0, 27])
+@pytest.mark.slow
+@pytest.mark.parametrize("layer", list(range(28)))
 def test_qwen_full_model_layers(layer):
-    """Layers of the Qwen-2.5-7B-shaped step (28/4 heads, 262,144 tokens),
-    each with its own dictionaries."""
+    """Every layer of the Qwen-2.5-7B-shaped full-model step (28 layers,
+    28/4 heads, 262,144 tokens), each with its own key and value
+    dictionaries, stage by stage against the oracle."""
     H.log(f"decode qwen layer {layer} (T=262144)")
     case = synth.qwen_layer_case(layer)
     compare(case, run_gpu(case))

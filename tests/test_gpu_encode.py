@@ -109,14 +109,115 @@ def test_deterministic():
         assert np.array_equal(a[k], b[k]), k
 
 
-def test_prefill_encode_full_size_sampled():
-    """The prefill encode workload at full size for the key stream (262,144
-    bf16 vectors, 32,768 atoms, K=16) as the benchmark runs it; the oracle
-    checks a seeded sample of 2,048 vectors."""
-    H.log("encode prefill key stream (262144 vectors), oracle on 2048 sampled")
-    e = synth.encode_case(stream=0)
+def near_tie_case(rng, n, N=4096, d=128, winner_high=True):
+    """Vectors whose two largest correlations belong to atoms a < b of the
+    same 16-atom column (a = b mod 16, b in a higher tile), apart by a
+    relative 2^-12 .. 2^-15: below what an fp16 screen resolves. x = d_a +
+    d_b + e (d_w - d_l) in fp32, w the intended winner (b when
+    winner_high). Returns (x, D, a, b) after checking in fp64 that the two
+    lead and how far apart they are."""
+    D = synth.make_dictionary(rng, N, d, "bf16")
+    ntile = N // 16
+    c = rng.integers(0, 16, n)
+    t1 = rng.integers(0, ntile - 1, n)
+    t2 = t1 + 1 + (rng.integers(0, ntile, n) % (ntile - 1 - t1))
+    a, b = 16 * t1 + c, 16 * t2 + c
+    eps = 2.0 ** -rng.uniform(12, 15, n)
+    w, lo = (b, a) if winner_high else (a, b)
+    # x = alpha d_lo + beta d_w with <x, d_lo> = 1 and <x, d_w> = 1 + eps
+    # (fp64 solve of the 2x2 Gram system), stored in fp32
+    Dl, Dw = D[lo].astype(np.float64), D[w].astype(np.float64)
+    gll, gww, glw = (Dl * Dl).sum(1), (Dw * Dw).sum(1), (Dl * Dw).sum(1)
+    det = gll * gww - glw * glw
+    tl, tw = np.ones(n), 1.0 + eps
+    alpha = (gww * tl - glw * tw) / det
+    beta = (gll * tw - glw * tl) / det
+    x = (alpha[:, None] * Dl + beta[:, None] * Dw).astype(np.float32)
+    C = x.astype(np.float64) @ D.T.astype(np.float64)
+    top2 = np.argsort(-np.abs(C), axis=1)[:, :2]
+    assert np.array_equal(top2[:, 0], w), "construction: intended winner is not first"
+    assert np.array_equal(top2[:, 1], lo), "construction: partner is not second"
+    gap = (np.abs(C[np.arange(n), w]) - np.abs(C[np.arange(n), lo])) / np.abs(C[np.arange(n), w])
+    assert np.all(gap > 2.0 ** -17) and np.all(gap < 2.0 ** -11), gap
+    return x, D, a, b
+
+
+@pytest.mark.parametrize("n", [1030, 48])
+@pytest.mark.parametrize("winner_high", [True, False])
+def test_near_ties_within_one_screen_column(n, winner_high):
+    """The two best atoms share a screen column and differ by less than the
+    fp16 screen resolves: the exact pick must still find the larger one
+    (batch path n > 64 and the small path), at every step."""
+    H.log(f"encode near ties in one column n={n} winner_high={winner_high}")
+    rng = np.random.default_rng(500 + n + winner_high)
+    x, D, a, b = near_tie_case(rng, n, winner_high=winner_high)
+    g = run(x, D, 2, x_dtype="f32")
+    gi, _ = H.unpack_words(g["codes"])
+    ri, rg, _ = oracle.mp_encode(x, D, 2)
+    assert np.array_equal(ri[:, 0], b if winner_high else a)
+    bad = np.nonzero((gi != ri).any(axis=1))[0]
+    assert bad.size == 0, f"{bad.size} vectors differ, first {bad[:5]}: gpu {gi[bad[:3]]} oracle {ri[bad[:3]]}"
+    np.testing.assert_allclose(g["coef_f32"], rg, atol=H.COEF_TOL, rtol=0)
+
+
+def exact_tie_dictionary(rng, N=8192, d=128):
+    """A bf16 dictionary with exact ties: rows copied or negated onto other
+    rows of the same screen column and of other columns, and three equal
+    rows in one column (which the exact pick must rescan). Returns
+    (D, groups): each group lists rows whose |<x, d>| are all equal."""
+    D = synth.make_dictionary(rng, N, d, "bf16")
+    groups = []
+    for j in range(40):
+        base = 16 * (2 * j + 1) + (j % 16)
+        if j % 4 == 0:      # copy in the same column, higher tile
+            others = [base + 16 * (50 + j)]
+        elif j % 4 == 1:    # negated copy in the same column
+            others = [base + 16 * (60 + j)]
+        elif j % 4 == 2:    # copy in another column
+            others = [base + 16 * (70 + j) + 3]
+        else:               # three equal rows in one column
+            others = [base + 16 * (80 + j), base + 16 * (150 + j)]
+        sign = -1.0 if j % 4 == 1 else 1.0
+        assert all(o < N for o in others)
+        for o in others:
+            D[o] = sign * D[base]
+        groups.append([base] + others)
+    rows = [r for gr in groups for r in gr]
+    assert len(set(rows)) == len(rows)
+    return D, groups
+
+
+@pytest.mark.parametrize("n", [1000, 40])
+def test_exact_ties_take_the_lowest_atom(n):
+    """Vectors aligned with rows that have exact duplicates (copied or
+    negated, in the same screen column or not, up to three in a column):
+    equal |correlations|, and the lowest atom index must win, as in the
+    oracle (numpy's argmax takes the first maximum)."""
+    H.log(f"encode exact ties n={n}")
+    rng = np.random.default_rng(600 + n)
+    D, groups = exact_tie_dictionary(rng)
+    gsel = rng.integers(0, len(groups), n)
+    heads = np.array([groups[k][0] for k in gsel])
+    x = (2.0 * D[heads] + 0.01 * rng.standard_normal((n, 128))).astype(np.float32)
+    g = run(x, D, 3, x_dtype="f32")
+    gi, _ = H.unpack_words(g["codes"])
+    ri, rg, _ = oracle.mp_encode(x, D, 3)
+    assert np.array_equal(ri[:, 0], heads)
+    bad = np.nonzero((gi != ri).any(axis=1))[0]
+    assert bad.size == 0, f"{bad.size} vectors differ, first {bad[:5]}: gpu {gi[bad[:3]]} oracle {ri[bad[:3]]}"
+    np.testing.assert_allclose(g["coef_f32"], rg, atol=H.COEF_TOL, rtol=0)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("stream", [0, 1])
+def test_prefill_encode_full_size_sampled(stream):
+    """The prefill encode workload at full size for the key (0) and value (1)
+    stream (262,144 bf16 vectors each, 32,768 atoms, K=16) as the benchmark
+    runs it; the oracle checks a seeded sample of 16,384 vectors of each."""
+    H.log(f"encode prefill stream {stream} (262144 vectors), oracle on 16384 sampled")
+    e = synth.encode_case(stream=stream)
     g = run(e.x, e.dictionary, 16)
-    rng = np.random.default_rng(99)
-    pick = np.sort(rng.choice(e.x.shape[0], 2048, replace=False))
+    rng = np.random.default_rng(99 + stream)
+    pick = np.sort(rng.choice(e.x.shape[0], 16384, replace=False))
     sub = {k: v[pick] for k, v in g.items()}
-    compare(e.x[pick], e.dictionary, 16, sub, "prefill sample")
+    compare(e.x[pick], e.dictionary, 16, sub, f"prefill stream {stream} sample")
