@@ -109,6 +109,8 @@ def _lib():
         lib.sdkv_encode_pair_workspace.argtypes = [P(EncodeArgs), P(EncodeArgs), P(c_size_t)]
         lib.sdkv_encode_pair.restype = c_int32
         lib.sdkv_encode_pair.argtypes = [P(EncodeArgs), P(EncodeArgs), c_void_p, c_size_t, c_void_p]
+        lib.sdkv_encode_pair_noalloc.restype = c_int32
+        lib.sdkv_encode_pair_noalloc.argtypes = [P(EncodeArgs), P(EncodeArgs), c_void_p]
         lib.sdkv_decode_attn_workspace.restype = c_int32
         lib.sdkv_decode_attn_workspace.argtypes = [P(AttnArgs), P(c_size_t)]
         lib.sdkv_decode_attn.restype = c_int32
@@ -396,6 +398,13 @@ def sdkv_encode_pair(ak: "EncodeArgs", av: "EncodeArgs", workspace: Optional[Wor
     del ws
 
 
+def sdkv_encode_pair_noalloc(ak: "EncodeArgs", av: "EncodeArgs", stream=None):
+    """sdkv_encode_pair with the library's static per-GPU scratch instead of
+    a workspace: nothing is allocated (see include/sdkv.h)."""
+    _check(_lib().sdkv_encode_pair_noalloc(ctypes.byref(ak), ctypes.byref(av), _stream(stream)),
+           "sdkv_encode_pair_noalloc")
+
+
 def sdkv_append_tokens(xk, xv, dk, dv, key_codes, val_codes, t: int, *, key_low=None,
                        workspace: Optional[Workspace] = None, stream=None):
     """Encode one decode step's new key and value vectors xk, xv [B, Hkv, d]
@@ -558,5 +567,5 @@ __all__ = ["sdkv_encode", "sdkv_decode_attn", "sdkv_select_topk", "selected_coun
            "SDKV_READING_A", "SDKV_READING_B", "SDKV_ENCODE_PURSUIT", "SDKV_ENCODE_OMP",
            "Workspace", "SdkvError", "lib", "LIB_PATH", "HEADER", "EncodeArgs", "AttnArgs",
            "SDKV_ERR_WAIT", "set_test_wait",
-           "sdkv_append_tokens", "sdkv_encode_pair",
+           "sdkv_append_tokens", "sdkv_encode_pair", "sdkv_encode_pair_noalloc",
            "attn_args", "decode_attn_workspace_bytes", "DecodeCall", "EncodeCall"]

@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsdkv.so")
-SOURCES = ["api.hip", "decode.hip", "topk.hip", "encode.hip"]
+SOURCES = ["api.hip", "decode.hip", "topk.hip", "encode.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

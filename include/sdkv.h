@@ -163,6 +163,21 @@ SDKV_API sdkv_status sdkv_encode_pair_workspace(const sdkv_encode_args* key,
 SDKV_API sdkv_status sdkv_encode_pair(const sdkv_encode_args* key, const sdkv_encode_args* val,
                                       void* ws, size_t ws_bytes, void* stream);
 
+/* sdkv_encode_pair without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation): the scratch lives in a static device array of
+ * SDKV_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends, whose
+ * address is looked up on the first call on each device. Same arguments,
+ * kernels and results as sdkv_encode_pair (bit for bit); no allocation or
+ * free. A problem whose scratch would exceed the array returns
+ * SDKV_ERR_WORKSPACE (every n <= 64, n_atoms <= 65536, K <= 32 problem
+ * fits). All calls on one GPU share its array, and the kernels write every
+ * scratch word before reading it: calls that overlap in time on one GPU
+ * (other streams, other host threads) race and are unsupported. */
+#define SDKV_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+SDKV_API sdkv_status sdkv_encode_pair_noalloc(const sdkv_encode_args* key,
+                                              const sdkv_encode_args* val, void* stream);
+
 /* ------------------------------------------------------------------------
  * Decode attention for one layer and one decode step (review page, Summary:
  * every token gets a cheap score from its first Klow = 3 atoms and only the

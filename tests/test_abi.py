@@ -20,7 +20,7 @@ def declared_symbols():
 def test_library_exports_every_declared_symbol():
     lib = sd.lib()
     names = declared_symbols()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), n
     assert lib.sdkv_abi_version() == 8
