@@ -253,6 +253,161 @@ def bench_decode(args, torch, sd, synth, ev):
 
 
 # ---------------------------------------------------------------------------
+# the other decode workloads: 4K layer, batch 8 x 32K, Qwen-shaped 28 layers
+# ---------------------------------------------------------------------------
+def step_bytes(B, Hq, Hkv, T, m, d, N, K, klow, khigh, layers=1):
+    """Algorithmic HBM bytes of one decode step: both dictionaries, the key
+    low plane, the Khigh - Klow extra key pairs and the K value pairs of
+    every selected token and query head, the queries and the outputs."""
+    per = (2 * N * d * 2 + B * Hkv * T * klow * 4 + B * Hq * m * (khigh - klow) * 4
+           + B * Hq * m * K * 4 + B * Hq * d * (2 + 4))
+    return per * layers
+
+
+def time_steps(ev, stream, fn, steps, warmup):
+    for i in range(warmup):
+        fn(i)
+    import torch
+    torch.cuda.synchronize()
+    t0, t1 = ev.create(2)
+    ev.record(t0, stream.cuda_stream)
+    for i in range(steps):
+        fn(i)
+    ev.record(t1, stream.cuda_stream)
+    torch.cuda.synchronize()
+    return ev.ms(t0, t1) / steps
+
+
+def workload_line(name, what, B, Hq, Hkv, T, m, ms, path_b, cpu, extra=None):
+    r = {"workload": what, "B": B, "Hq": Hq, "Hkv": Hkv, "T": T, "m": m,
+         "us_per_step": round(ms * 1e3, 2), "value": round(B * T / (ms * 1e-3), 1),
+         "unit": "context-tokens/s",
+         "path_roofline": {"bound": "hbm", "algorithmic_bytes_per_step": path_b,
+                           "achieved_GBs": round(path_b / (ms * 1e-3) / 1e9, 1),
+                           "peak": HBM_PEAK_GBS,
+                           "frac": round(path_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+         "cpu_baseline": cpu}
+    if extra:
+        r.update(extra)
+    return r
+
+
+def bench_layer_workload(args, torch, sd, synth, ev, name, what):
+    """A Llama-shaped layer workload from synth (the parity-tested inputs),
+    with enough copies to rotate through more than 512 MB per pass."""
+    case = synth.decode_case(name)
+    B, Hq, Hkv, T, d, K, N, m = case.B, case.Hq, case.Hkv, case.T, case.d, case.K, case.n_atoms, case.m
+    dev = "cuda"
+
+    def up_words(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int32)).to(dev)
+
+    base = dict(q=torch.from_numpy(case.q).to(dev).to(torch.bfloat16),
+                dk=torch.from_numpy(case.dk).to(dev).to(torch.bfloat16),
+                dv=torch.from_numpy(case.dv).to(dev).to(torch.bfloat16),
+                kv=up_words(np.stack([case.key_codes, case.val_codes], axis=3)),
+                kl=up_words(case.key_low))
+    set_bytes = sum(t.numel() * t.element_size() for t in base.values())
+    nsets = max(2, int(np.ceil(600e6 / set_bytes)))
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(nsets - 1)]
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    ws = sd.Workspace()
+    calls = [sd.DecodeCall(st["q"], st["dk"], st["dv"], st["kv"], None, klow=case.klow,
+                           khigh=case.khigh, top_num=case.top_num, top_den=case.top_den,
+                           scale=case.scale, key_low=st["kl"], out=out, workspace=ws)
+             for st in sets]
+    stream = torch.cuda.current_stream()
+    ms = time_steps(ev, stream, lambda i: calls[i % nsets].launch(), args.steps, args.warmup)
+    calls[0].check()
+    path_b = step_bytes(B, Hq, Hkv, T, m, d, N, K, case.klow, case.khigh)
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline_decode(case, args.cpu_budget / 3, label=what)
+    del sets, calls
+    torch.cuda.empty_cache()
+    return workload_line(name, what, B, Hq, Hkv, T, m, ms, path_b, cpu,
+                         {"input_sets": nsets, "set_bytes": set_bytes})
+
+
+def gpu_dictionary(torch, gen, N, d):
+    """Gaussian rows normalised to unit length (fp32), stored as bf16."""
+    g = torch.randn((N, d), generator=gen, device="cuda", dtype=torch.float32)
+    return (g / g.norm(dim=1, keepdim=True)).to(torch.bfloat16)
+
+
+def gpu_codes(torch, gen, n, K, N):
+    """Packed code words [n, K] as int32: K distinct uniform atom indices per
+    row (rows with a repeat are drawn again) and binary16 coefficients
+    |N(0,1)| in decreasing order, the recipe of synth.make_codes drawn on the
+    device."""
+    idx = torch.randint(0, N, (n, K), generator=gen, device="cuda", dtype=torch.int64)
+    while True:
+        srt = idx.sort(dim=1).values
+        bad = (srt[:, 1:] == srt[:, :-1]).any(dim=1).nonzero().flatten()
+        if bad.numel() == 0:
+            break
+        idx[bad] = torch.randint(0, N, (bad.numel(), K), generator=gen, device="cuda",
+                                 dtype=torch.int64)
+    c = torch.randn((n, K), generator=gen, device="cuda", dtype=torch.float32).abs()
+    c = c.sort(dim=1, descending=True).values.to(torch.float16)
+    bits = c.view(torch.int16).to(torch.int32) & 0xFFFF
+    return (idx.to(torch.int32) | (bits << 16)).contiguous()
+
+
+def bench_qwen_full_step(args, torch, sd, synth, ev):
+    """Qwen-2.5-7B-shaped full-model decode step: 28 layers, each with its
+    own 32,768-atom key and value dictionaries, 28 query / 4 KV heads,
+    262,144 coded tokens at batch 1, one fresh query per layer; a step is
+    the 28 per-layer calls in sequence on one stream (4.6 GB of inputs, so
+    nothing is served from the 256 MB Infinity Cache between steps).
+    Inputs are drawn on the device (torch's generator, seed 4000 + layer)
+    with the distributions of synth.qwen_layer_case."""
+    L, Hq, Hkv, T, d, K, N = 28, 28, 4, 262144, 128, 16, 32768
+    klow, khigh = 3, 16
+    m = max(1, min(T, -(-T * 1 // 10)))
+    scale = 1.0 / np.sqrt(d)
+    out = torch.empty((L, 1, Hq, d), dtype=torch.float32, device="cuda")
+    layers = []
+    for li in range(L):
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(4000 + li)
+        dk, dv = gpu_dictionary(torch, gen, N, d), gpu_dictionary(torch, gen, N, d)
+        kc = gpu_codes(torch, gen, Hkv * T, K, N).view(1, Hkv, T, K)
+        vc = gpu_codes(torch, gen, Hkv * T, K, N).view(1, Hkv, T, K)
+        kv = torch.stack([kc, vc], dim=3).contiguous()
+        del kc, vc
+        kl = kv[:, :, :, 0, :klow].contiguous()
+        q = torch.randn((1, Hq, d), generator=gen, device="cuda").to(torch.bfloat16)
+        layers.append(dict(q=q, dk=dk, dv=dv, kv=kv, kl=kl))
+    ws = sd.Workspace()
+    calls = [sd.DecodeCall(ly["q"], ly["dk"], ly["dv"], ly["kv"], None, klow=klow, khigh=khigh,
+                           top_num=1, top_den=10, scale=scale, key_low=ly["kl"], out=out[li],
+                           workspace=ws)
+             for li, ly in enumerate(layers)]
+    in_bytes = sum(t.numel() * t.element_size() for ly in layers for t in ly.values())
+
+    def step(_i):
+        for c in calls:
+            c.launch()
+    stream = torch.cuda.current_stream()
+    ms = time_steps(ev, stream, step, max(3, args.steps // 4), 2)
+    calls[-1].check()
+    path_b = step_bytes(1, Hq, Hkv, T, m, d, N, K, klow, khigh, layers=L)
+    cpu = None
+    if not args.no_cpu:
+        c0 = synth.qwen_layer_case(0)
+        cpu = cpu_baseline_decode(c0, args.cpu_budget / 3, label="qwen layer", scale_layers=L)
+    del calls, layers
+    torch.cuda.empty_cache()
+    return workload_line("qwen_28_layers_256k",
+                         "qwen2.5-7b-shaped full-model decode step (28 layers) at 262,144 tokens",
+                         1, Hq, Hkv, T, m, ms, path_b, cpu,
+                         {"layers": L, "input_bytes": in_bytes,
+                          "us_per_layer": round(ms * 1e3 / L, 2),
+                          "data": "drawn on the device, torch generator seeded 4000 + layer"})
+
+
+# ---------------------------------------------------------------------------
 # encode (prefill)
 # ---------------------------------------------------------------------------
 def bench_append(args, torch, sd, synth, ev, dec):
@@ -383,7 +538,9 @@ def cpu_threads():
         return os.cpu_count() or 1
 
 
-def cpu_baseline_decode(case, budget_s):
+def cpu_baseline_decode(case, budget_s, label="128K", scale_layers=1):
+    """The oracle's decode of one layer, repeated for about budget_s seconds;
+    with scale_layers = L the step is L such layers (time scaled by L)."""
     import oracle
     t = time.perf_counter()
     reps = 0
@@ -394,11 +551,12 @@ def cpu_baseline_decode(case, budget_s):
         el = time.perf_counter() - t
         if el >= budget_s or reps >= 20:
             break
-    per = el / reps
+    per = el / reps * scale_layers
+    what = (f"full {label} decode step (all {case.Hq} query heads)" if scale_layers == 1 else
+            f"one {label} ({case.Hq} query heads, T={case.T}), time x {scale_layers} layers")
     return {"value": case.B * case.T / per, "unit": "context-tokens/s", "cores": cpu_threads(),
             "kind": "oracle",
-            "sample": f"full 128K decode step (all {case.Hq} query heads), {reps} run(s), "
-                      f"{el:.1f} s, fp64 NumPy"}
+            "sample": f"{what}, {reps} run(s), {el:.1f} s, fp64 NumPy"}
 
 
 def cpu_baseline_encode(ecase, budget_s):
@@ -466,6 +624,8 @@ def main():
     ap.add_argument("--no-encode", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the attention-flag steps, the append and the OMP comparison")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the 4K layer, batch-8 x 32K and 28-layer Qwen-shaped steps")
     ap.add_argument("--no-decode", action="store_true",
                     help="encode only (profiling runs); prints no benchmark line")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -512,6 +672,20 @@ def main():
         log(f"  integer-only softmax step: {dec['int_softmax']['us_per_step']:.1f} us")
         log(f"  shared-selection step: {dec['shared_select']['us_per_step']:.1f} us")
         log(f"  reading-B step: {dec['reading_b']['us_per_step']:.1f} us")
+    wl = None
+    if not args.no_workloads:
+        wl = {}
+        log("decode workloads: 4K layer, batch 8 x 32K, Qwen-shaped 28 layers at 256K")
+        wl["llama_layer_4k"] = bench_layer_workload(
+            args, torch, sd, synth, ev, "llama_layer_4k",
+            "llama3.1-8b-shaped layer decode step at 4K context")
+        wl["llama_layer_b8_32k"] = bench_layer_workload(
+            args, torch, sd, synth, ev, "llama_layer_b8_32k",
+            "llama3.1-8b-shaped layer decode step, batch 8 x 32K context")
+        wl["qwen_28_layers_256k"] = bench_qwen_full_step(args, torch, sd, synth, ev)
+        for k, v in wl.items():
+            log(f"  {k}: {v['us_per_step']:.1f} us/step, {v['value']:.3e} context-tokens/s, "
+                f"path {v['path_roofline']['frac']:.3f} of HBM peak")
     enc = None
     if not args.no_encode:
         log("encode benchmark (524,288 vectors)")
@@ -543,6 +717,8 @@ def main():
         "cpu_baseline": cpu,
         "achievable": ach,
     }
+    if wl is not None:
+        line["workloads"] = wl
     if app is not None:
         line["append"] = app
         line["int_softmax"] = dec["int_softmax"]

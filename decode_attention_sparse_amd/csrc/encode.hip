@@ -553,7 +553,6 @@ __global__ __launch_bounds__(ESB) void k_small(SmallLaunch L, int step) {
   __shared__ uint64_t s_key[NW * NV];
   __shared__ float s_g[NV];
   __shared__ int s_a[NV];
-  __shared__ float s_rn[NV];   // |r_step| per vector (bf16 dictionary path)
   const SmallArgs a = blockIdx.y ? L.p[1] : L.p[0];
   if constexpr (OMP) {
     if (step == L.K + 1) {
@@ -738,11 +737,6 @@ __global__ __launch_bounds__(ESB) void k_small(SmallLaunch L, int step) {
         *(uint2*)&s_p[v * RPB + kk] = hi;
         *(uint2*)&s_p[(NV + v) * RPB + kk] = mid;
         *(uint2*)&s_p[(2 * NV + v) * RPB + kk] = lo;
-        // |r|: a vector's D/4 groups sit in D/4 consecutive lanes
-        float n2 = rr[j].x * rr[j].x;
-        n2 = fmaf(rr[j].y, rr[j].y, n2); n2 = fmaf(rr[j].z, rr[j].z, n2); n2 = fmaf(rr[j].w, rr[j].w, n2);
-        n2 = vec_sum<D>(n2);
-        if (kk == 0) s_rn[v] = sqrtf(n2);
       }
       if (wg == 0 && corr) rq[gq] = rr[j];
     }
@@ -755,36 +749,14 @@ __global__ __launch_bounds__(ESB) void k_small(SmallLaunch L, int step) {
       // --- correlations on the matrix cores: C[atom][vector] over 16-vector
       // tiles, r split exactly into three bf16 parts (every product exact,
       // fp32 accumulation); per wave the best of its 32 atoms per vector.
-      // The matrix cores' accumulation order and rounding are not the same
-      // for an atom and its negation, so the wave's best and every atom
-      // within 2 eps of it (eps = 2^-13 |r| |d|max bounds the matrix-core
-      // sum's error: 12 accumulations of 32 exact products) are recomputed
-      // as a sequential fp32 dot product, which a duplicated or negated atom
-      // reproduces exactly; the winners compare those values. ---------------
-      // largest norm of this wave's 32 atoms
-      float dmx;
-      {
-        float n2[2] = {0.f, 0.f};
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int k = 0; k < KS; ++k)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float lo = bf16_lo(bt[t][k][e]), hi = bf16_hi(bt[t][k][e]);
-              n2[t] = fmaf(lo, lo, fmaf(hi, hi, n2[t]));
-            }
-        float m = 0.f;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          float x = n2[t] + __shfl_xor(n2[t], 16, 64);
-          x += __shfl_xor(x, 32, 64);
-          m = fmaxf(m, x);
-        }
-        dmx = sqrtf(wave_max(m));
-      }
+      // The matrix cores do not round a sum and its negation to the same
+      // magnitude, so each atom is also run negated and its magnitude is
+      // the larger of the two: an atom and its negated copy then get equal
+      // magnitudes (exact ties, lowest index first), as do duplicates. The
+      // coefficient keeps the sign of the atom's own correlation. --------
       for (int v0 = 0; v0 < n; v0 += 16) {
         f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        f32x4 accn[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         const int vr = min(v0 + (l & 15), n - 1);  // columns past n are never stored
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
@@ -794,9 +766,13 @@ __global__ __launch_bounds__(ESB) void k_small(SmallLaunch L, int step) {
           const u32x4 lo = *(const u32x4*)&s_p[2 * NV * RPB + off];
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
+            const u32x4 ng = bt[t][k] ^ u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
             acc[t] = mfma_bf16(bt[t][k], hi, acc[t]);
+            accn[t] = mfma_bf16(ng, hi, accn[t]);
             acc[t] = mfma_bf16(bt[t][k], mid, acc[t]);
+            accn[t] = mfma_bf16(ng, mid, accn[t]);
             acc[t] = mfma_bf16(bt[t][k], lo, acc[t]);
+            accn[t] = mfma_bf16(ng, lo, accn[t]);
           }
         }
         // lane holds vector v0 + (l & 15) against atoms 16t + 4 * (l >> 4) + i;
@@ -807,7 +783,9 @@ __global__ __launch_bounds__(ESB) void k_small(SmallLaunch L, int step) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int at = wg * ECHS + 32 * w + 16 * t + 4 * (l >> 4) + i;
-            if (at < L.N) k = max_u64(k, win_key(acc[t][i], at));
+            const float mag = fmaxf(fabsf(acc[t][i]), fabsf(accn[t][i]));
+            const float c = __builtin_copysignf(mag, acc[t][i]);
+            if (at < L.N) k = max_u64(k, win_key(c, at));
           }
 #pragma unroll
         for (int o = 16; o <= 32; o <<= 1) {
@@ -815,48 +793,8 @@ __global__ __launch_bounds__(ESB) void k_small(SmallLaunch L, int step) {
           const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(k >> 32), o, 64);
           k = max_u64(k, ((uint64_t)hi << 32) | lo);
         }
-        // exact values of the candidates
-        const float thr = __uint_as_float((uint32_t)(k >> 32)) - ldexpf(s_rn[vr] * dmx, -12);
-        uint32_t cm = 0;  // candidates among this lane's 8 values: bit 4t + i
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int at = wg * ECHS + 32 * w + 16 * t + 4 * (l >> 4) + i;
-            if (at < L.N && fabsf(acc[t][i]) >= thr) cm |= 1u << (4 * t + i);
-          }
-        uint64_t ke = 0;
-        const uint16_t* rp = s_p + vr * RPB;
-        while (cm) {
-          const int b = __builtin_ctz(cm);
-          cm &= cm - 1u;
-          const int at = wg * ECHS + 32 * w + 16 * (b >> 2) + 4 * (l >> 4) + (b & 3);
-          const u32x4* dp = (const u32x4*)((const uint16_t*)a.dict + (int64_t)at * D);
-          float ce = 0.f;
-#pragma unroll 2
-          for (int k8 = 0; k8 < D / 8; ++k8) {
-            const u32x4 dv = dp[k8];
-            const u32x4 h = *(const u32x4*)&rp[8 * k8];
-            const u32x4 m = *(const u32x4*)&rp[NV * RPB + 8 * k8];
-            const u32x4 o = *(const u32x4*)&rp[2 * NV * RPB + 8 * k8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float r0 = (bf16_lo(h[e]) + bf16_lo(m[e])) + bf16_lo(o[e]);
-              const float r1 = (bf16_hi(h[e]) + bf16_hi(m[e])) + bf16_hi(o[e]);
-              ce = fmaf(bf16_lo(dv[e]), r0, ce);
-              ce = fmaf(bf16_hi(dv[e]), r1, ce);
-            }
-          }
-          ke = max_u64(ke, win_key(ce, at));
-        }
-#pragma unroll
-        for (int o = 16; o <= 32; o <<= 1) {
-          const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)ke, o, 64);
-          const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(ke >> 32), o, 64);
-          ke = max_u64(ke, ((uint64_t)hi << 32) | lo);
-        }
         const int v = v0 + l;
-        if (l < 16 && v < n) s_key[w * NV + v] = ke;
+        if (l < 16 && v < n) s_key[w * NV + v] = k;
       }
       __syncthreads();
       // the workgroup's winner per vector: the best of the waves' winners
