@@ -269,13 +269,16 @@ __global__ __launch_bounds__(EB) void k_encode(EncArgs a) {
     for (int c = 0; c < nchunks; ++c) {
       const int buf = c & 1;
       if (c + 1 < nchunks) load_chunk(c + 1);
-      // tiles in pairs: 8 independent accumulation chains, then one 3-way
-      // max per output for the two tiles
+      // four tiles at a time: 16 independent accumulation chains, then per
+      // output two 3-way maxima for the best and, for the second best, the
+      // medians of (best, k0, k1) and (best', k2, k3) folded by one 3-way max
+      // (9 VALU ops per four products)
+      static_assert(ECH % 64 == 0, "chunks hold whole groups of four tiles");
 #pragma unroll
-      for (int tt = 0; tt < ECH / 16; tt += 2) {
-        f32x4 acc[2][4];
+      for (int tt = 0; tt < ECH / 16; tt += 4) {
+        f32x4 acc[4][4];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < 4; ++h) {
           u32x4 bfr[KS];
 #pragma unroll
           for (int s = 0; s < KS; ++s)
@@ -288,18 +291,20 @@ __global__ __launch_bounds__(EB) void k_encode(EncArgs a) {
             for (int rt = 0; rt < 4; ++rt) acc[h][rt] = mfma_f16(af[rt][s], bfr[s], acc[h][rt]);
         }
         const uint32_t tc0 = (~(uint32_t)(c * (ECH / 16) + tt) & 0xFFFu) | 0x80000000u;
-        const uint32_t tc1 = tc0 - 1u;  // the next tile's code
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const uint32_t k0 = (__float_as_uint(acc[0][rt][i]) & vmask) | tc0;
-            const uint32_t k1 = (__float_as_uint(acc[1][rt][i]) & vmask) | tc1;
-            const uint32_t b1 = bkey[rt][i];
-            // second largest of {b1, b2, k0, k1} (b1 >= b2): the larger of b2
-            // and the median of (b1, k0, k1)
-            bkey2[rt][i] = max(bkey2[rt][i], med3_u32(b1, k0, k1));
-            bkey[rt][i] = max(b1, max(k0, k1));
+            const uint32_t k1 = (__float_as_uint(acc[1][rt][i]) & vmask) | (tc0 - 1u);
+            const uint32_t k2 = (__float_as_uint(acc[2][rt][i]) & vmask) | (tc0 - 2u);
+            const uint32_t k3 = (__float_as_uint(acc[3][rt][i]) & vmask) | (tc0 - 3u);
+            const uint32_t b0 = bkey[rt][i];
+            const uint32_t b1 = max(b0, max(k0, k1));
+            // second largest of {b0, b2, k0..k3} (b0 >= b2): the largest of
+            // b2, the median of (b0, k0, k1) and the median of (b1, k2, k3)
+            bkey2[rt][i] = max(bkey2[rt][i], max(med3_u32(b0, k0, k1), med3_u32(b1, k2, k3)));
+            bkey[rt][i] = max(b1, max(k2, k3));
           }
       }
       if (c + 1 < nchunks) store_chunk(buf ^ 1);
