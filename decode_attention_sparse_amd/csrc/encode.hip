@@ -110,6 +110,14 @@ __global__ __launch_bounds__(256) void k_prep_dict(const void* dict, int dict_f3
 __device__ __forceinline__ uint32_t med3_u32(uint32_t a, uint32_t b, uint32_t c) {
   return max(min(a, b), min(max(a, b), c));
 }
+// the same as one v_med3_u32 the optimiser cannot see into: next to
+// max(a, max(b, c)), the min/max form shares max(a, b) with it and the
+// maximum then takes two ops instead of one v_max3_u32
+__device__ __forceinline__ uint32_t med3_u32_op(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t r;
+  asm("v_med3_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 
 template <int D>
 __device__ __forceinline__ float exact_corr(const EncArgs& a, const float* rrow, int atom) {
@@ -303,7 +311,7 @@ __global__ __launch_bounds__(EB) void k_encode(EncArgs a) {
             const uint32_t b1 = max(b0, max(k0, k1));
             // second largest of {b0, b2, k0..k3} (b0 >= b2): the largest of
             // b2, the median of (b0, k0, k1) and the median of (b1, k2, k3)
-            bkey2[rt][i] = max(bkey2[rt][i], max(med3_u32(b0, k0, k1), med3_u32(b1, k2, k3)));
+            bkey2[rt][i] = max(bkey2[rt][i], max(med3_u32_op(b0, k0, k1), med3_u32_op(b1, k2, k3)));
             bkey[rt][i] = max(b1, max(k2, k3));
           }
       }
