@@ -242,18 +242,14 @@ struct Words3 {
 constexpr int kTokBatch = 2;   // selected tokens per thread per load batch
 constexpr int kListCap = 3072; // selected tokens per workgroup kept in LDS
 
-// Loads the first `nw` words of a code record (record length K words).
-// FAST: K == 16, the record is 64-byte aligned and read as 4 x 16 bytes.
-template <bool FAST>
-__device__ __forceinline__ void load_record(const uint32_t* rec, int K, int nw, uint32_t (&w)[32]) {
-  if (FAST) {
+// Loads a 16-word code record, 64-byte aligned, as 4 x 16 bytes, into the
+// first 16 words of w (32-word arrays: a register-allocation choice; with
+// 16-word arrays the 32-key extension build spills far more).
+__device__ __forceinline__ void load_record(const uint32_t* rec, uint32_t (&w)[32]) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const u32x4 v = ((const u32x4*)rec)[q];
-      w[4 * q] = v[0]; w[4 * q + 1] = v[1]; w[4 * q + 2] = v[2]; w[4 * q + 3] = v[3];
-    }
-  } else {
-    for (int i = 0; i < nw && i < K; ++i) w[i] = rec[i];
+  for (int q = 0; q < 4; ++q) {
+    const u32x4 v = ((const u32x4*)rec)[q];
+    w[4 * q] = v[0]; w[4 * q + 1] = v[1]; w[4 * q + 2] = v[2]; w[4 * q + 3] = v[3];
   }
 }
 
@@ -507,6 +503,9 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   // (lmax, vb): running max of s_high and sum_t exp(s_t - lmax) sum_j |kappa^v_tj|
   float lmax = -INFINITY, vb = 0.f;
   float lmin = INFINITY, vmax = 0.f;  // integer mode: score range, largest sum_j |kappa^v|
+  // (the 16-pair records are held in registers; other code lengths read
+  // their words in the loops, so no register array is indexed at run time
+  // and the kernel keeps no per-lane scratch)
   uint32_t vw[kTokBatch][32];
   for (int64_t base = 0; base < cnt; base += (int64_t)SB * kTokBatch) {
     int64_t tt[kTokBatch];
@@ -518,10 +517,12 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
       tt[r] = min(max(t, (int64_t)0), a.T - 1);
     }
     uint32_t kw[kTokBatch][32];
+    if (FAST) {
 #pragma unroll
-    for (int r = 0; r < kTokBatch; ++r) {
-      load_record<FAST>(kbase + tt[r] * a.rs, a.K, a.khigh, kw[r]);
-      load_record<FAST>(vbase + tt[r] * a.rs, a.K, a.K, vw[r]);
+      for (int r = 0; r < kTokBatch; ++r) {
+        load_record(kbase + tt[r] * a.rs, kw[r]);
+        load_record(vbase + tt[r] * a.rs, vw[r]);
+      }
     }
 #pragma unroll
     for (int r = 0; r < kTokBatch; ++r) {
@@ -534,9 +535,11 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
           va += fabsf(code_coef(vw[r][q]));
         }
       } else {
+        const uint32_t* kr = kbase + tt[r] * a.rs;
+        const uint32_t* vr = vbase + tt[r] * a.rs;
         for (int q = 0; q < a.khigh; ++q)
-          s = fmaf(code_coef(kw[r][q]), s_u[code_idx(kw[r][q]) & AMASK], s);
-        for (int q = 0; q < a.K; ++q) va += fabsf(code_coef(vw[r][q]));
+          s = fmaf(code_coef(kr[q]), s_u[code_idx(kr[q]) & AMASK], s);
+        for (int q = 0; q < a.K; ++q) va += fabsf(code_coef(vr[q]));
       }
       if (i < cnt) {
         if (in_lds) s_ls[i] = s;
@@ -684,7 +687,7 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   float lsum = 0.f;
   for (int64_t base = 0; base < cnt; base += (int64_t)SB * kTokBatch) {
     float pt[kTokBatch];
-    if (!one_batch) {
+    if (FAST && !one_batch) {
       int64_t tt[kTokBatch];
 #pragma unroll
       for (int r = 0; r < kTokBatch; ++r) {
@@ -694,7 +697,7 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
         tt[r] = min(max(t, (int64_t)0), a.T - 1);
       }
 #pragma unroll
-      for (int r = 0; r < kTokBatch; ++r) load_record<FAST>(vbase + tt[r] * a.rs, a.K, a.K, vw[r]);
+      for (int r = 0; r < kTokBatch; ++r) load_record(vbase + tt[r] * a.rs, vw[r]);
     }
 #pragma unroll
     for (int r = 0; r < kTokBatch; ++r) {
@@ -715,9 +718,12 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
             atomicAdd((uint32_t*)&s_w[code_idx(vw[r][q]) & AMASK],
                       (uint32_t)(int32_t)rintf(ps * code_coef(vw[r][q])));
         } else {
-          for (int q = 0; q < a.K; ++q)
-            atomicAdd((uint32_t*)&s_w[code_idx(vw[r][q]) & AMASK],
-                      (uint32_t)(int32_t)rintf(ps * code_coef(vw[r][q])));
+          const int64_t t = in_lds ? t0 + s_lt[i] : (int64_t)sel_g[i];
+          const uint32_t* vr = vbase + min(max(t, (int64_t)0), a.T - 1) * a.rs;
+          for (int q = 0; q < a.K; ++q) {
+            const uint32_t wv = vr[q];
+            atomicAdd((uint32_t*)&s_w[code_idx(wv) & AMASK], (uint32_t)(int32_t)rintf(ps * code_coef(wv)));
+          }
         }
       }
     }

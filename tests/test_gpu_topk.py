@@ -22,6 +22,8 @@ def run(scores, k):
     (1, 1, 1, "normal"), (1, 100, 10, "normal"), (3, 5000, 500, "ties"),
     (2, 100000, 10000, "normal"), (4, 70000, 1, "ties"), (2, 65537, 65537, "normal"),
     (5, 2047, 1024, "signed_zero"), (1, 1 << 22, 419431, "normal"), (300, 3000, 300, "ties"),
+    # rows split over several workgroups at 32 keys per thread (P = 4 and 31)
+    (64, 100000, 10000, "normal"), (16, 1000000, 100000, "ties"),
 ])
 def test_topk_matches_oracle(rows, n, k, kind):
     H.log(f"topk rows={rows} n={n} k={k} {kind}")
