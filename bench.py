@@ -133,6 +133,30 @@ def calibrate_copy(torch, mib: int, reps: int = 5):
                       "copy_GBs": round(2 * n * 4 / el / 1e9, 1)}), flush=True)
 
 
+def calibrate_gather(torch, rows_log2: int = 20, reps: int = 5):
+    """A gather of 2**rows_log2 random 128-byte rows (32 fp32) out of a
+    2**22-row table, by torch.index_select: a second reference for the
+    rocprofv3 FETCH_SIZE counter, whose requests are scattered 128-byte
+    lines like the row kernel's record reads (the copy reference streams).
+    Bytes read: 128 per gathered row plus 8 per int64 index; bytes written:
+    128 per row."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    table = torch.ones((1 << 22, 32), dtype=torch.float32, device="cuda")
+    n = 1 << rows_log2
+    idx = torch.randint(0, 1 << 22, (n,), generator=g, device="cuda")
+    out = torch.index_select(table, 0, idx)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(reps):
+        torch.index_select(table, 0, idx, out=out)
+    torch.cuda.synchronize()
+    el = (time.perf_counter() - t) / reps
+    print(json.dumps({"gather_rows": n, "gather_bytes_read": n * (128 + 8),
+                      "gather_bytes_written": n * 128, "reps": reps + 1,
+                      "gather_GBs": round(n * (2 * 128 + 8) / el / 1e9, 1)}), flush=True)
+
+
 # ---------------------------------------------------------------------------
 # decode at 128K
 # ---------------------------------------------------------------------------
@@ -628,6 +652,8 @@ def main():
                     help="skip the 4K layer, batch-8 x 32K and 28-layer Qwen-shaped steps")
     ap.add_argument("--no-decode", action="store_true",
                     help="encode only (profiling runs); prints no benchmark line")
+    ap.add_argument("--calibrate-gather", action="store_true",
+                    help="only run a random 128-byte row gather (counter calibration)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
@@ -647,6 +673,9 @@ def main():
         raise SystemExit("no GPU visible")
     if args.calibrate_copy:
         calibrate_copy(torch, args.calibrate_copy)
+        return
+    if args.calibrate_gather:
+        calibrate_gather(torch)
         return
     sd.lib()
     ev = HipEvents()
