@@ -6,7 +6,9 @@
 // Per vector x:  r = x;  for k < K: a_k = argmax_a |<r, d_a>| (lowest index on
 // ties), g_k = <r, d_{a_k}>, r -= g_k d_{a_k}.
 //
-// Structure (one workgroup = 8 waves = 512 vectors, all K steps inside):
+// Structure (one workgroup = 4 waves = 256 vectors, all K steps inside; two
+// workgroups share a compute unit, so one's chunk barriers do not stall the
+// other's matrix work):
 //   * screen: every step correlates the workgroup's residuals with all atoms
 //     on the matrix cores (v_mfma_f32_16x16x32_f16). The residual rows are
 //     scaled by a power of two and rounded to fp16; the dictionary is an fp16
@@ -32,7 +34,7 @@
 
 namespace sdkv {
 
-constexpr int EB = 512;            // threads per workgroup
+constexpr int EB = 256;            // threads per workgroup (two per CU: <= 256 VGPRs)
 constexpr int ENW = EB / 64;       // waves
 constexpr int EROWS = ENW * 64;    // vectors per workgroup (64 per wave)
 constexpr int ECH = 64;            // atoms per LDS chunk
@@ -148,7 +150,7 @@ __device__ __forceinline__ float exact_corr(const EncArgs& a, const float* rrow,
 }
 
 template <int D>
-__global__ __launch_bounds__(EB) void k_encode(EncArgs a) {
+__global__ __launch_bounds__(EB, 2) void k_encode(EncArgs a) {
   constexpr int KS = D / 32;           // MFMA k-steps per 16x16 tile
   constexpr int BP = D + 8;            // LDS row pitch (fp16 elements)
   __shared__ __attribute__((aligned(16))) uint16_t s_b[2][ECH * BP];
