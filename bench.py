@@ -92,11 +92,9 @@ def sources_digest(paths):
     return h.hexdigest()
 
 
-def read_traffic(kernel: str, workload: str):
-    """HBM bytes per launch measured with rocprofv3 counters, from the
-    committed summary profiles/traffic_<kernel>_<workload>.md, if the digest it
-    records of the kernel's sources still matches them; else None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.md")
+def read_digest(path: str):
+    """The '- key: value' lines of a committed profile summary, if the
+    digest it records of the kernel's sources still matches them; else None."""
     if not os.path.exists(path):
         return None
     vals = {}
@@ -110,8 +108,31 @@ def read_traffic(kernel: str, workload: str):
     try:
         if sources_digest(srcs) != vals["sources_sha256"]:
             return None
-        return float(vals["hbm_bytes_per_launch"])
-    except (OSError, KeyError, ValueError):
+    except OSError:
+        return None
+    return vals
+
+
+def read_mfma_busy(kernel: str, workload: str):
+    """Share of SIMD-cycles the matrix cores were busy in the kernel
+    (rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE), from the
+    committed summary profiles/mfma_<workload>.md while its source digest
+    matches; else None. Clock-free, unlike a rate against the peak."""
+    vals = read_digest(os.path.join(ROOT, "profiles", f"mfma_{workload}.md"))
+    try:
+        return float(vals[f"mfma_busy_{kernel}"]) if vals else None
+    except (KeyError, ValueError):
+        return None
+
+
+def read_traffic(kernel: str, workload: str):
+    """HBM bytes per launch measured with rocprofv3 counters, from the
+    committed summary profiles/traffic_<kernel>_<workload>.md, if the digest it
+    records of the kernel's sources still matches them; else None."""
+    vals = read_digest(os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.md"))
+    try:
+        return float(vals["hbm_bytes_per_launch"]) if vals else None
+    except (KeyError, ValueError):
         return None
 
 
@@ -546,6 +567,7 @@ def bench_encode(args, torch, sd, synth, ev):
                 roofline={"bound": "mfma", "achieved": round(tflops, 1), "peak": F16_PEAK_TFLOPS,
                           "unit": "TFLOP/s", "frac": round(tflops / F16_PEAK_TFLOPS, 4),
                           "traffic": read_traffic("k_encode", "prefill_524k"),
+                          "mfma_busy": read_mfma_busy("k_encode", "prefill_524k"),
                           "kernel": "k_encode<128>", "algorithmic_flops_per_step": flops},
                 streams=streams)
 
