@@ -158,8 +158,9 @@ struct RowsArgs {
   float* s_high_out;        // optional [rows, m]
   int32_t* sel;             // [rows, P, chunk] per-workgroup lists (when LDS is short)
   float* s_high;            // [rows, P, chunk]
-  float* wpart;             // [rows, P, N] per-workgroup unnormalised weights
-  float2* stats;            // [rows, P] (local max, local sum of exp)
+  uint16_t* wpart;          // [rows, P, N] per-workgroup unnormalised weights, fp16
+                            // bits scaled by 1 / stats.z
+  float4* stats;            // [rows, P] (local max, local sum of exp, weight scale, 0)
   uint32_t* ghist;          // [rows, 2048]
   uint32_t* wtab;           // [rows, P, 2048] window tables: count | start << 16
   uint32_t* cand;           // [rows, P, chunk] threshold-bin candidates
@@ -748,31 +749,36 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   __syncthreads();
 
   // 7. this workgroup's unnormalised weights and its (max, sum of exp) pair;
-  // the W.Dv kernel merges the P partials of each row.
-  float* dst = a.wpart + ((int64_t)row * a.P + p) * a.N;
-  const float invS = 1.f / S;
-  const int n4 = a.N >> 2;
+  // the W.Dv kernel merges the P partials of each row. The bins (|bin| <
+  // 2^30) are stored as fp16 of bin * 2^-16 (below 2^14, so always finite):
+  // a relative rounding of at most 2^-11 per weight. stats.z = 2^16 / S
+  // turns a stored value back into a weight.
+  uint16_t* dst = a.wpart + ((int64_t)row * a.P + p) * a.N;
+  const int n8 = a.N >> 3;
   // (streaming stores: the partials are read once, by the next kernel)
-  for (int i = tid; i < n4; i += SB) {
-    const int4 v = ((const int4*)s_w)[i];
-    __builtin_nontemporal_store((float)v.x * invS, &dst[4 * i]);
-    __builtin_nontemporal_store((float)v.y * invS, &dst[4 * i + 1]);
-    __builtin_nontemporal_store((float)v.z * invS, &dst[4 * i + 2]);
-    __builtin_nontemporal_store((float)v.w * invS, &dst[4 * i + 3]);
+  for (int i = tid; i < n8; i += SB) {
+    const int4 v0 = ((const int4*)s_w)[2 * i], v1 = ((const int4*)s_w)[2 * i + 1];
+    u32x4 h;
+    h[0] = f32_to_f16_bits((float)v0.x * 0x1p-16f) | (f32_to_f16_bits((float)v0.y * 0x1p-16f) << 16);
+    h[1] = f32_to_f16_bits((float)v0.z * 0x1p-16f) | (f32_to_f16_bits((float)v0.w * 0x1p-16f) << 16);
+    h[2] = f32_to_f16_bits((float)v1.x * 0x1p-16f) | (f32_to_f16_bits((float)v1.y * 0x1p-16f) << 16);
+    h[3] = f32_to_f16_bits((float)v1.z * 0x1p-16f) | (f32_to_f16_bits((float)v1.w * 0x1p-16f) << 16);
+    __builtin_nontemporal_store(h, (u32x4*)(dst + 8 * i));
   }
-  for (int i = (n4 << 2) + tid; i < a.N; i += SB) dst[i] = (float)s_w[i] * invS;
+  for (int i = (n8 << 3) + tid; i < a.N; i += SB)
+    dst[i] = (uint16_t)f32_to_f16_bits((float)s_w[i] * 0x1p-16f);
   // (integer mode: the weights are already normalised; the merge adds them)
   if (tid == 0)
     a.stats[(int64_t)row * a.P + p] =
-        im ? make_float2(0.f, 1.f) : make_float2(M, lsum_all);
+        make_float4(im ? 0.f : M, im ? 1.f : lsum_all, ldexpf(1.f, 16 - min(sexp, 100)), 0.f);
 }
 
 // ---------------------------------------------------------------------------
 // out = W . Dv  (split-K over atom chunks, then a fixed-order sum)
 // ---------------------------------------------------------------------------
 struct WdvArgs {
-  const float* wpart;     // [rows, P, N] unnormalised per-workgroup weights
-  const float2* stats;    // [rows, P] (max, sum of exp) per partial
+  const uint16_t* wpart;  // [rows, P, N] unnormalised per-workgroup weights (fp16, scaled)
+  const float4* stats;    // [rows, P] (max, sum of exp, weight scale, 0) per partial
   const void* dv;         // [N, d]
   int N, d, P, rows, nrt, nsub, nchunks;
   float* opart;           // [nchunks, rows, d]
@@ -785,22 +791,24 @@ constexpr int WRT = 32;                   // rows per workgroup tile
 constexpr int WPITCH = WSUB + 8;          // u16 per A row in LDS
 constexpr int BPITCH = WSUB / 2 + 4;      // u32 (atom pairs) per B row in LDS
 
-// s_coef[r][q] = exp(M_q - max_q M_q) / sum_q exp(M_q - max M) l_q for the
-// tile's rows: the softmax merge of the row's P partial results.
+// s_coef[r][q] = g_q exp(M_q - max_q M_q) / sum_q exp(M_q - max M) l_q for
+// the tile's rows: the softmax merge of the row's P partial results, with
+// g_q the scale that turns partial q's stored fp16 values into weights.
 __device__ __forceinline__ void wdv_coefs(const WdvArgs& a, int r0, float* s_coef) {
   const int w = wave_id(), l = lane_id();
   for (int r = w; r < WRT; r += 4) {
     const int row = r0 + r;
-    float Mq = -INFINITY, lq = 0.f;
+    float Mq = -INFINITY, lq = 0.f, gq = 0.f;
     if (row < a.rows && l < a.P) {
-      const float2 st = a.stats[(int64_t)row * a.P + l];
+      const float4 st = a.stats[(int64_t)row * a.P + l];
       Mq = st.x;
       lq = st.y;
+      gq = st.z;
     }
     const float Mx = wave_max(Mq);
     const float c = (lq > 0.f) ? __expf(Mq - Mx) : 0.f;
     const float Lr = wave_sum(c * lq);
-    if (l < a.P) s_coef[r * kMaxRowP + l] = a.presum ? 1.f : (Lr > 0.f) ? c / Lr : 0.f;
+    if (l < a.P) s_coef[r * kMaxRowP + l] = gq * (a.presum ? 1.f : (Lr > 0.f) ? c / Lr : 0.f);
   }
 }
 
@@ -810,26 +818,27 @@ __device__ __forceinline__ void wdv_merge16(const WdvArgs& a, const float* s_coe
 #pragma unroll
   for (int e = 0; e < 16; ++e) v[e] = 0.f;
   if (row >= a.rows) return;
-  const float* src = a.wpart + (int64_t)row * a.P * a.N + a0;
-  if (a0 + 16 <= a.N && (a.N & 3) == 0) {
+  const uint16_t* src = a.wpart + (int64_t)row * a.P * a.N + a0;
+  if (a0 + 16 <= a.N && (a.N & 7) == 0) {
 #pragma unroll 4
     for (int q = 0; q < a.P; ++q) {
       const float c = s_coef[r * kMaxRowP + q];
-      const float4* sp = (const float4*)(src + (int64_t)q * a.N);
+      const u32x4* sp = (const u32x4*)(src + (int64_t)q * a.N);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float4 x = sp[k];
-        v[4 * k] = fmaf(c, x.x, v[4 * k]);
-        v[4 * k + 1] = fmaf(c, x.y, v[4 * k + 1]);
-        v[4 * k + 2] = fmaf(c, x.z, v[4 * k + 2]);
-        v[4 * k + 3] = fmaf(c, x.w, v[4 * k + 3]);
+      for (int k = 0; k < 2; ++k) {
+        const u32x4 x = sp[k];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[8 * k + 2 * j] = fmaf(c, f16_bits_to_f32(x[j] & 0xFFFFu), v[8 * k + 2 * j]);
+          v[8 * k + 2 * j + 1] = fmaf(c, f16_bits_to_f32(x[j] >> 16), v[8 * k + 2 * j + 1]);
+        }
       }
     }
   } else {
     for (int q = 0; q < a.P; ++q) {
       const float c = s_coef[r * kMaxRowP + q];
       for (int e = 0; e < 16 && a0 + e < a.N; ++e)
-        v[e] = fmaf(c, src[(int64_t)q * a.N + e], v[e]);
+        v[e] = fmaf(c, f16_bits_to_f32(src[(int64_t)q * a.N + e]), v[e]);
     }
   }
   if (a.w_out) {
@@ -859,20 +868,16 @@ __global__ __launch_bounds__(512) void k_wdv_bf16(WdvArgs a) {
   // this thread's A slot (row r, atoms c0 .. c0+8) and B items
   const int ar = tid >> 4, ac0 = (tid & 15) * 8;
   const int arow = r0 + ar;
-  const bool a_fast = (a.N & 3) == 0;
+  const bool a_fast = (a.N & 7) == 0;
   constexpr int BIT = (WSUB / 2) * (128 / 8) / 512;  // B items per thread (d = 128)
-  float4 px[WDV_PQ][2];
+  u32x4 px[WDV_PQ];
   u32x4 bx[BIT][2];
   auto load_sub = [&](int a0) {
 #pragma unroll
     for (int q = 0; q < WDV_PQ; ++q) {
-      px[q][0] = make_float4(0.f, 0.f, 0.f, 0.f);
-      px[q][1] = px[q][0];
-      if (q < a.P && arow < a.rows && a_fast && a0 + ac0 + 8 <= a.N) {
-        const float4* sp = (const float4*)(a.wpart + ((int64_t)arow * a.P + q) * a.N + a0 + ac0);
-        px[q][0] = sp[0];
-        px[q][1] = sp[1];
-      }
+      px[q] = u32x4{0u, 0u, 0u, 0u};
+      if (q < a.P && arow < a.rows && a_fast && a0 + ac0 + 8 <= a.N)
+        px[q] = *(const u32x4*)(a.wpart + ((int64_t)arow * a.P + q) * a.N + a0 + ac0);
     }
 #pragma unroll
     for (int k = 0; k < BIT; ++k) {
@@ -892,11 +897,11 @@ __global__ __launch_bounds__(512) void k_wdv_bf16(WdvArgs a) {
 
   // softmax-merge coefficients of the tile's rows (all stats loads first)
   {
-    float2 st[WRT / 8];
+    float4 st[WRT / 8];
 #pragma unroll
     for (int k = 0; k < WRT / 8; ++k) {
       const int row = r0 + w + 8 * k;
-      st[k] = make_float2(-INFINITY, 0.f);
+      st[k] = make_float4(-INFINITY, 0.f, 0.f, 0.f);
       if (row < a.rows && l < a.P) st[k] = a.stats[(int64_t)row * a.P + l];
     }
 #pragma unroll
@@ -905,7 +910,9 @@ __global__ __launch_bounds__(512) void k_wdv_bf16(WdvArgs a) {
       const float Mx = wave_max(Mq);
       const float c = (lq > 0.f) ? __expf(Mq - Mx) : 0.f;
       const float Lr = wave_sum(c * lq);
-      if (l < a.P) s_coef[(w + 8 * k) * kMaxRowP + l] = a.presum ? 1.f : (Lr > 0.f) ? c / Lr : 0.f;
+      if (l < a.P)
+        s_coef[(w + 8 * k) * kMaxRowP + l] =
+            st[k].z * (a.presum ? 1.f : (Lr > 0.f) ? c / Lr : 0.f);
     }
   }
   __syncthreads();
@@ -926,28 +933,29 @@ __global__ __launch_bounds__(512) void k_wdv_bf16(WdvArgs a) {
           for (int q = 0; q < WDV_PQ; ++q) {
             if (q < a.P) {
               const float c = s_coef[ar * kMaxRowP + q];
-              v[0] = fmaf(c, px[q][0].x, v[0]); v[1] = fmaf(c, px[q][0].y, v[1]);
-              v[2] = fmaf(c, px[q][0].z, v[2]); v[3] = fmaf(c, px[q][0].w, v[3]);
-              v[4] = fmaf(c, px[q][1].x, v[4]); v[5] = fmaf(c, px[q][1].y, v[5]);
-              v[6] = fmaf(c, px[q][1].z, v[6]); v[7] = fmaf(c, px[q][1].w, v[7]);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                v[2 * j] = fmaf(c, f16_bits_to_f32(px[q][j] & 0xFFFFu), v[2 * j]);
+                v[2 * j + 1] = fmaf(c, f16_bits_to_f32(px[q][j] >> 16), v[2 * j + 1]);
+              }
             }
           }
           // partials beyond the prefetched batch
           for (int q = WDV_PQ; q < a.P; ++q) {
             const float c = s_coef[ar * kMaxRowP + q];
-            const float4* sp = (const float4*)(a.wpart + ((int64_t)arow * a.P + q) * a.N + a0 + ac0);
-            const float4 x0 = sp[0], x1 = sp[1];
-            v[0] = fmaf(c, x0.x, v[0]); v[1] = fmaf(c, x0.y, v[1]);
-            v[2] = fmaf(c, x0.z, v[2]); v[3] = fmaf(c, x0.w, v[3]);
-            v[4] = fmaf(c, x1.x, v[4]); v[5] = fmaf(c, x1.y, v[5]);
-            v[6] = fmaf(c, x1.z, v[6]); v[7] = fmaf(c, x1.w, v[7]);
+            const u32x4 x = *(const u32x4*)(a.wpart + ((int64_t)arow * a.P + q) * a.N + a0 + ac0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              v[2 * j] = fmaf(c, f16_bits_to_f32(x[j] & 0xFFFFu), v[2 * j]);
+              v[2 * j + 1] = fmaf(c, f16_bits_to_f32(x[j] >> 16), v[2 * j + 1]);
+            }
           }
         } else {
-          const float* src = a.wpart + (int64_t)arow * a.P * a.N + a0 + ac0;
+          const uint16_t* src = a.wpart + (int64_t)arow * a.P * a.N + a0 + ac0;
           for (int q = 0; q < a.P; ++q) {
             const float c = s_coef[ar * kMaxRowP + q];
             for (int e = 0; e < 8 && a0 + ac0 + e < a.N; ++e)
-              v[e] = fmaf(c, src[(int64_t)q * a.N + e], v[e]);
+              v[e] = fmaf(c, f16_bits_to_f32(src[(int64_t)q * a.N + e]), v[e]);
           }
         }
         if (a.w_out) {
@@ -1136,8 +1144,8 @@ sdkv_status plan_decode(const sdkv_attn_args* a, DecodePlan* p) {
   const size_t list = (size_t)rows * q.P * q.chunk * 4;  // per-workgroup regions
   q.off_sel = off;    off = align_up(off + list, A);
   q.off_shigh = off;  off = align_up(off + list, A);
-  q.off_wpart = off;  off = align_up(off + (size_t)rows * q.P * N * 4, A);
-  q.off_stats = off;  off = align_up(off + (size_t)rows * q.P * 8, A);
+  q.off_wpart = off;  off = align_up(off + (size_t)rows * q.P * N * 2, A);
+  q.off_stats = off;  off = align_up(off + (size_t)rows * q.P * 16, A);
   q.off_opart = off;  off = align_up(off + (size_t)q.nchunks * rows * a->d * 4, A);
   q.off_cand = off;   off = align_up(off + (q.P > 1 ? (size_t)rows * q.P * q.chunk * 4 : 0), A);
   q.off_wtab = off;   off = align_up(off + (q.P > 1 ? (size_t)rows * q.P * 2048 * 4 : 0), A);
@@ -1172,8 +1180,8 @@ sdkv_status launch_decode(const sdkv_attn_args* a, const DecodePlan& p, void* ws
   float* U = (float*)(base + p.off_u);
   int32_t* sel = (int32_t*)(base + p.off_sel);
   float* shigh = (float*)(base + p.off_shigh);
-  float* wpart = (float*)(base + p.off_wpart);
-  float2* stats = (float2*)(base + p.off_stats);
+  uint16_t* wpart = (uint16_t*)(base + p.off_wpart);
+  float4* stats = (float4*)(base + p.off_stats);
   uint32_t* ghist = (uint32_t*)(base + p.off_ghist);
   uint32_t* xchg = (uint32_t*)(base + p.off_xchg);
   uint32_t* bar = (uint32_t*)(base + p.off_bar);

@@ -19,6 +19,14 @@ SEL_TOL = 1e-5
 OUT_RTOL = 2e-3
 IDX_AGREE = 0.999
 COEF_TOL = 1e-4
+# Value weights W (an intermediate of the decode step): each workgroup adds
+# its weights in int32 fixed point (step 2^-29..2^-30 of its total weight
+# mass, ~2e-5 relative L2 over ~5e4 contributions) and hands them to the
+# W.Dv pass as binary16, whose round-to-nearest error is uniform within half
+# an ulp: 2^-10/sqrt(12) to 2^-11/sqrt(12) (2.8e-4 to 1.4e-4) relative rms per
+# weight, so W's relative L2 error is expected near 2e-4. The bound is 1e-3;
+# W.Dv carries the same relative error into the output, inside OUT_RTOL.
+W_RTOL = 1e-3
 
 
 def log(msg):

@@ -35,11 +35,7 @@ def run_gpu(case, debug=True, key_low=True, ws=None, interleaved=False):
     return {k: H.host(v) for k, v in r.items()}
 
 
-# The value weights accumulate in int32 fixed point whose step is 2^-29..2^-30
-# of the workgroup's total weight mass; with n ~ 5e4 contributions spread over
-# ~3e4 atoms the expected relative L2 error of W is ~ sqrt(n) * 2^-29 ~ 2e-5,
-# so the intermediate bound is 1e-4 (the output bound stays 2e-3).
-W_RTOL = 1e-4
+W_RTOL = H.W_RTOL
 
 
 def compare(case, g, heads=None, w_tol=W_RTOL):

@@ -13,7 +13,7 @@ from tests import gpu_helpers as H
 pytestmark = pytest.mark.gpu
 
 P1 = 2.0 ** oracle.INT_SOFTMAX_P_BITS
-W_RTOL = 1e-4       # as for the fp32 softmax (fixed-point value weights)
+W_RTOL = H.W_RTOL    # fixed-point sums handed over as binary16
 QUANT_RTOL = 2e-2   # integer vs fp32 softmax, output rel-L2
 
 

@@ -13,7 +13,7 @@ from tests import gpu_helpers as H
 
 pytestmark = pytest.mark.gpu
 
-W_RTOL = 1e-4
+W_RTOL = H.W_RTOL    # fixed-point sums handed over as binary16
 
 
 def run(case, *, val_low=True, interleaved=False, select="head", debug=True, reading="B",
