@@ -44,3 +44,6 @@ def test_select_core_emulated(emulator, spt, P, T, m, kind, window):
     r = subprocess.run([emulator, str(spt), str(P), str(T), str(m), str(spt * 100 + P), kind,
                         str(window)], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stdout + r.stderr
+    if window and kind != "ties":
+        # the window holds the threshold: no workgroup falls back to the radix select
+        assert "window fallbacks 0," in r.stdout, r.stdout
