@@ -1,7 +1,8 @@
-// Host emulation of the device primitives the select core uses, so that the
-// select core's own source (select_core.h) can run on the CPU: every GPU
-// thread is a fiber (ucontext), workgroup barriers, wave exchanges and the
-// cross-workgroup barrier are cooperative waits. Test infrastructure only.
+// Host emulation of the device primitives the select core and the decode
+// row kernel use, so that their own source (select_core.h, the row kernel of
+// decode.hip) can run on the CPU: every GPU thread is a fiber (ucontext),
+// workgroup barriers, wave exchanges and the cross-workgroup barrier are
+// cooperative waits. Test infrastructure only.
 //
 // The harness copies select_core.h next to this file under the name the
 // header includes (sdkv_device.h resolves to this file), then compiles it
@@ -14,8 +15,28 @@
 #include <algorithm>
 
 #define __device__
+#define __global__
+#define __launch_bounds__(...)
 #define __forceinline__ inline
 #define __HIP_MEMORY_SCOPE_AGENT 0
+#define __builtin_nontemporal_store(v, p) (*(p) = (v))
+
+typedef uint32_t u32x4 __attribute__((vector_size(16)));
+struct float2 {
+  float x, y;
+};
+struct float4 {
+  float x, y, z, w;
+};
+struct int4 {
+  int x, y, z, w;
+};
+inline float2 make_float2(float x, float y) { return float2{x, y}; }
+inline float4 make_float4(float x, float y, float z, float w) { return float4{x, y, z, w}; }
+inline float __expf(float x) { return expf(x); }
+inline int __clz(uint32_t x) { return x ? __builtin_clz(x) : 32; }
+inline int __clzll(unsigned long long x) { return x ? __builtin_clzll(x) : 64; }
+inline void __threadfence_block() {}
 
 namespace emu {
 struct D3 {
@@ -70,6 +91,9 @@ inline T __hip_atomic_fetch_add(T* p, T v, int, int) {
 }
 using std::max;
 using std::min;
+inline int64_t min(int64_t a, int b) { return a < b ? a : (int64_t)b; }
+inline int64_t min(int a, int64_t b) { return a < b ? (int64_t)a : b; }
+inline int64_t max(int64_t a, int b) { return a > b ? a : (int64_t)b; }
 
 // wave exchange: every lane deposits a value, then reads any lane's
 inline uint64_t wave_xchg_read(uint64_t mine, int lane, int src) {
@@ -112,6 +136,35 @@ inline float key_float(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
+// IEEE binary16 <-> binary32 from the formats' definitions (the device uses
+// the hardware conversions, round to nearest even)
+inline float f16_bits_to_f32(uint32_t b) {
+  const uint32_t s = (b >> 15) & 1u, e = (b >> 10) & 31u, f = b & 1023u;
+  float v;
+  if (e == 0) v = ldexpf((float)f, -24);
+  else if (e == 31) v = f ? NAN : INFINITY;
+  else v = ldexpf((float)(f | 1024u), (int)e - 25);
+  return s ? -v : v;
+}
+inline uint32_t f32_to_f16_bits(float x) {
+  const uint32_t s = (__float_as_uint(x) >> 31) << 15;
+  const float a = fabsf(x);
+  if (a != a) return s | 0x7E00u;
+  if (a >= 65520.f) return s | 0x7C00u;  // rounds to infinity
+  if (a < 0x1p-14f) {                     // subnormal: multiples of 2^-24
+    return s | (uint32_t)nearbyintf(a * 0x1p24f);  // round half even (default mode)
+  }
+  int e;
+  frexpf(a, &e);                          // a = m 2^e, m in [0.5, 1)
+  const float q = nearbyintf(ldexpf(a, 11 - e));  // 11 significant bits
+  uint32_t m = (uint32_t)q, E = (uint32_t)(e - 1 + 15);
+  if (m == 2048u) { m = 1024u; ++E; }
+  if (E >= 31u) return s | 0x7C00u;
+  return s | (E << 10) | (m - 1024u);
+}
+inline uint32_t code_idx(uint32_t w) { return w & 0xFFFFu; }
+inline float code_coef(uint32_t w) { return f16_bits_to_f32(w >> 16); }
+
 // wave reductions and scans by exchange (lane order, as the DPP versions)
 template <class Op>
 inline uint32_t wave_fold(uint32_t v, Op op, bool inclusive_scan) {
@@ -138,6 +191,45 @@ inline uint32_t wave_max_u32(uint32_t v) {
   return wave_fold(v, [](uint32_t a, uint32_t b) { return max(a, b); }, false);
 }
 
+inline float wave_max(float v) {
+  uint64_t* s = emu::wave_slots();
+  s[lane_id()] = __float_as_uint(v);
+  emu::wave_barrier();
+  float r = __uint_as_float((uint32_t)s[0]);
+  for (int i = 1; i < 64; ++i) r = fmaxf(r, __uint_as_float((uint32_t)s[i]));
+  emu::wave_barrier();
+  return r;
+}
+inline float wave_sum(float v) {
+  uint64_t* s = emu::wave_slots();
+  s[lane_id()] = __float_as_uint(v);
+  emu::wave_barrier();
+  float r = __uint_as_float((uint32_t)s[0]);
+  for (int i = 1; i < 64; ++i) r += __uint_as_float((uint32_t)s[i]);
+  emu::wave_barrier();
+  return r;
+}
+template <int NW>
+inline float block_max(float v, float* tmp) {
+  v = wave_max(v);
+  if (lane_id() == 0) tmp[wave_id()] = v;
+  __syncthreads();
+  float r = tmp[0];
+  for (int i = 1; i < NW; ++i) r = fmaxf(r, tmp[i]);
+  __syncthreads();
+  return r;
+}
+template <int NW>
+inline float block_sum(float v, float* tmp) {
+  v = wave_sum(v);
+  if (lane_id() == 0) tmp[wave_id()] = v;
+  __syncthreads();
+  float r = 0.f;
+  for (int i = 0; i < NW; ++i) r += tmp[i];
+  __syncthreads();
+  return r;
+}
+
 template <int NW>
 inline uint32_t block_excl_scan(uint32_t v, uint32_t* tmp, uint32_t* total) {
   const uint32_t inc = wave_incl_scan(v);
@@ -161,6 +253,14 @@ struct WaitCtl {
 };
 inline uint32_t ld_agent(const uint32_t* p) { return *p; }
 inline void st_agent(uint32_t* p, uint32_t v) { *p = v; }
+// workgroup start order, as the device's tickets
+inline int ticket_tile(uint32_t* tickets, int nb, bool xcd) {
+  if (xcd) {
+    const int c = (int)(blockIdx.x & 7u);
+    return c * (nb >> 3) + (int)atomicAdd(&tickets[c], 1u);
+  }
+  return (int)atomicAdd(&tickets[0], 1u);
+}
 
 // arrival counter and bounded wait, as the device barrier (one thread
 // arrives and waits; the workgroup meets before and after)

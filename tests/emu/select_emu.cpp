@@ -4,69 +4,20 @@
 // element. Test infrastructure only (see emu_device.h).
 //
 // usage: select_emu SPT P T m seed kind(normal|ties|plateau) [window(1)|radix(0)]
-#include <ucontext.h>
-
+//                   [order: 0 ascending | 1 descending | 2 shuffled]
+//
+// The order is the one in which runnable fibers are resumed between their
+// synchronisations. A result that depends on it means two threads touch the
+// same location with no synchronisation between them (a race).
 #include <cstdio>
+#include <algorithm>
 #include <cstdlib>
 #include <random>
 #include <vector>
 
 #include "sdkv_device.h"  // the emulation header, copied under this name
+#include "emu_fibers.h"
 #include "select_core.h"
-
-namespace emu {
-struct Fiber {
-  ucontext_t ctx;
-  int tid = 0, wg = 0;
-  bool done = false;
-};
-static ucontext_t g_main;
-static Fiber* g_cur = nullptr;
-static std::vector<Fiber*> g_fibers;
-struct Wave {
-  uint64_t slots[64];
-  int count = 0;
-  unsigned gen = 0;
-};
-struct Group {
-  int count = 0;
-  unsigned gen = 0;
-  uint32_t flag = 0;
-  std::vector<Wave> waves;
-};
-static std::vector<Group> g_groups;
-static int g_sb = 0;
-
-D3 tid3() { return D3{(unsigned)g_cur->tid, 0, 0}; }
-D3 bid3() { return D3{(unsigned)g_cur->wg, 0, 0}; }
-static void yield_now() {
-  Fiber* f = g_cur;
-  swapcontext(&f->ctx, &g_main);
-}
-void spin_yield() { yield_now(); }
-void block_barrier() {
-  Group& g = g_groups[g_cur->wg];
-  const unsigned my = g.gen;
-  if (++g.count == g_sb) {
-    g.count = 0;
-    ++g.gen;
-  } else {
-    while (g.gen == my) yield_now();
-  }
-}
-void wave_barrier() {
-  Wave& w = g_groups[g_cur->wg].waves[g_cur->tid >> 6];
-  const unsigned my = w.gen;
-  if (++w.count == 64) {
-    w.count = 0;
-    ++w.gen;
-  } else {
-    while (w.gen == my) yield_now();
-  }
-}
-uint64_t* wave_slots() { return g_groups[g_cur->wg].waves[g_cur->tid >> 6].slots; }
-uint32_t* wg_flag() { return &g_groups[g_cur->wg].flag; }
-}  // namespace emu
 
 using namespace sdkv;
 
@@ -134,12 +85,12 @@ static void thread_body() {
 template <int SPT>
 static void fiber_entry() {
   thread_body<SPT>();
-  emu::g_cur->done = true;
-  swapcontext(&emu::g_cur->ctx, &emu::g_main);
+  emu::fiber_exit();
 }
 
 template <int SPT>
-static int run(int P, int64_t T, int64_t m, uint32_t seed, const char* kind, bool window) {
+static int run(int P, int64_t T, int64_t m, uint32_t seed, const char* kind, bool window,
+               int order) {
   Row& R = g_row;
   R.P = P;
   R.T = T;
@@ -169,35 +120,7 @@ static int run(int P, int64_t T, int64_t m, uint32_t seed, const char* kind, boo
   R.ghist.assign(2048, 0u);
   R.sh.assign(P, SelShared{});
   R.qcnt.assign(P, std::vector<uint32_t>(5 * 64 + 1, 0u));
-  emu::g_sb = SB;
-  emu::g_groups.assign(P, emu::Group{});
-  for (auto& g : emu::g_groups) g.waves.assign(SB / 64, emu::Wave{});
-  const size_t stack = 64 * 1024;
-  std::vector<char> stacks((size_t)P * SB * stack);
-  for (int p = 0; p < P; ++p)
-    for (int t = 0; t < SB; ++t) {
-      auto* f = new emu::Fiber;
-      f->tid = t;
-      f->wg = p;
-      getcontext(&f->ctx);
-      f->ctx.uc_stack.ss_sp = &stacks[((size_t)p * SB + t) * stack];
-      f->ctx.uc_stack.ss_size = stack;
-      f->ctx.uc_link = nullptr;
-      makecontext(&f->ctx, (void (*)())fiber_entry<SPT>, 0);
-      emu::g_fibers.push_back(f);
-    }
-  size_t live = emu::g_fibers.size();
-  while (live) {
-    live = 0;
-    for (auto* f : emu::g_fibers) {
-      if (f->done) continue;
-      emu::g_cur = f;
-      swapcontext(&emu::g_main, &f->ctx);
-      if (!f->done) ++live;
-    }
-  }
-  for (auto* f : emu::g_fibers) delete f;
-  emu::g_fibers.clear();
+  emu::run_fibers(P, SB, fiber_entry<SPT>, order, seed);
 
   // check: m selected; none unselected above a selected one; among keys
   // equal to the threshold, the lowest elements selected
@@ -215,9 +138,9 @@ static int run(int P, int64_t T, int64_t m, uint32_t seed, const char* kind, boo
     }
   }
   const int64_t want = std::min<int64_t>(m, T);
-  printf("SPT %d P %d T %lld m %lld %s %s: selected %lld (want %lld), misplaced %d, window "
+  printf("SPT %d P %d T %lld m %lld %s %s order %d: selected %lld (want %lld), misplaced %d, window "
          "fallbacks %d, status %u\n",
-         SPT, P, (long long)T, (long long)m, kind, window ? "window" : "radix", (long long)n,
+         SPT, P, (long long)T, (long long)m, kind, window ? "window" : "radix", order, (long long)n,
          (long long)want, bad, R.fallbacks, R.err);
   return (n == want && bad == 0 && R.err == 0) ? 0 : 1;
 }
@@ -231,9 +154,10 @@ int main(int argc, char** argv) {
   const int64_t T = atoll(argv[3]), m = atoll(argv[4]);
   const uint32_t seed = (uint32_t)atoi(argv[5]);
   const bool window = argc > 7 ? atoi(argv[7]) != 0 : true;
-  if (spt == 16) return run<16>(P, T, m, seed, argv[6], window);
-  if (spt == 32) return run<32>(P, T, m, seed, argv[6], window);
-  if (spt == 8) return run<8>(P, T, m, seed, argv[6], window);
+  const int order = argc > 8 ? atoi(argv[8]) : 0;
+  if (spt == 16) return run<16>(P, T, m, seed, argv[6], window, order);
+  if (spt == 32) return run<32>(P, T, m, seed, argv[6], window, order);
+  if (spt == 8) return run<8>(P, T, m, seed, argv[6], window, order);
   fprintf(stderr, "SPT must be 8, 16 or 32\n");
   return 2;
 }

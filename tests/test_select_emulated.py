@@ -22,6 +22,7 @@ def emulator(tmp_path_factory):
     # select_core.h includes "sdkv_device.h": the emulation header takes its place
     shutil.copy(os.path.join(HERE, "emu", "emu_device.h"), d / "sdkv_device.h")
     shutil.copy(os.path.join(CSRC, "select_core.h"), d / "select_core.h")
+    shutil.copy(os.path.join(HERE, "emu", "emu_fibers.h"), d / "emu_fibers.h")
     shutil.copy(os.path.join(HERE, "emu", "select_emu.cpp"), d / "select_emu.cpp")
     exe = d / "select_emu"
     subprocess.run(["g++", "-O2", "-std=c++17", "-o", str(exe), str(d / "select_emu.cpp")],
@@ -40,9 +41,27 @@ def emulator(tmp_path_factory):
     (32, 8, 262144, 26215, "normal", 0),     # two-barrier radix select directly
     (8, 3, 20000, 2000, "normal", 1),        # ragged last chunk
 ])
-def test_select_core_emulated(emulator, spt, P, T, m, kind, window):
+@pytest.mark.parametrize("order", [0])
+def test_select_core_emulated(emulator, spt, P, T, m, kind, window, order):
+    _run_case(emulator, spt, P, T, m, kind, window, order)
+
+
+# Fibers resumed in reversed and shuffled order between synchronisations: a
+# selection that changed with the order would show two threads touching one
+# location with no synchronisation between them.
+@pytest.mark.parametrize("spt,P,T,m,kind,window,order", [
+    (32, 8, 262144, 26215, "normal", 1, 1),
+    (32, 8, 262144, 26215, "plateau", 1, 2),
+    (32, 4, 131072, 13108, "ties", 1, 2),
+    (16, 8, 131072, 13108, "normal", 0, 1),
+])
+def test_select_core_emulated_thread_order(emulator, spt, P, T, m, kind, window, order):
+    _run_case(emulator, spt, P, T, m, kind, window, order)
+
+
+def _run_case(emulator, spt, P, T, m, kind, window, order):
     r = subprocess.run([emulator, str(spt), str(P), str(T), str(m), str(spt * 100 + P), kind,
-                        str(window)], capture_output=True, text=True, timeout=300)
+                        str(window), str(order)], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stdout + r.stderr
     if window and kind != "ties":
         # the window holds the threshold: no workgroup falls back to the radix select
