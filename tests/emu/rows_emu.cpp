@@ -4,11 +4,14 @@
 // rows_kernel.inc, cut from decode.hip by the test with its __shared__
 // declarations turned into per-workgroup storage. Test infrastructure only.
 //
-// usage: rows_emu SPT in.bin out.bin [order]
+// usage: rows_emu SPT in.bin out.bin [order] [mode]
+//   mode   : 0 the default build; the build that takes the attention flags
+//            with 1 none set, 2 the integer-only softmax, 3 reading B
 //   in.bin : int64 N T m P klow khigh, then f32 U[N], u32 low[T][3],
 //            u32 kc[T][16], u32 vc[T][16]
 //   out.bin: f32 s_low[T], i32 sel[m], f32 s_high[m], u16 wpart[P][N],
-//            f32 stats[P][4], u32 status, u32 cross-workgroup barrier rounds
+//            f32 stats[P][4], i32 p_int[m], u32 status, u32 cross-workgroup
+//            barrier arrivals
 #include <cstdio>
 #include <cstdlib>
 #include <map>
@@ -54,9 +57,9 @@ using namespace sdkv;
 static RowsArgs g_args;
 static int g_spt = 16;
 
-template <int SPT>
+template <int SPT, bool EXT>
 static void fiber_entry() {
-  k_rows<SPT, true, false>(g_args);
+  k_rows<SPT, true, EXT>(g_args);
   emu::fiber_exit();
 }
 
@@ -76,6 +79,7 @@ int main(int argc, char** argv) {
   }
   g_spt = atoi(argv[1]);
   const int order = argc > 4 ? atoi(argv[4]) : 0;
+  const int mode = argc > 5 ? atoi(argv[5]) : 0;
   FILE* fi = fopen(argv[2], "rb");
   if (!fi) return 2;
   int64_t h[6];
@@ -97,7 +101,7 @@ int main(int argc, char** argv) {
 
   // workspace: words the launcher clears are zero, the rest hold a pattern
   std::vector<float> s_low(T), s_high_out(m);
-  std::vector<int32_t> sel_out(m, -1), sel((size_t)P * chunk);
+  std::vector<int32_t> sel_out(m, -1), sel((size_t)P * chunk), p_int(m, 0);
   std::vector<float> s_high((size_t)P * chunk);
   std::vector<uint16_t> wpart((size_t)P * N, 0xA5A5u);
   std::vector<float4> stats(P);
@@ -141,8 +145,13 @@ int main(int argc, char** argv) {
   a.ticket = ticket.data();
   a.xcd_map = 0;
   a.ixchg = ixchg.data();
+  a.imode = mode == 2 ? 1 : 0;
+  a.p_int_out = mode == 2 ? p_int.data() : nullptr;
+  a.readb = mode == 3 ? 1 : 0;  // value low words from the value records
 
-  void (*entry)() = g_spt == 32 ? fiber_entry<32> : g_spt == 16 ? fiber_entry<16> : nullptr;
+  void (*entry)() = nullptr;
+  if (g_spt == 32) entry = mode ? fiber_entry<32, true> : fiber_entry<32, false>;
+  if (g_spt == 16) entry = mode ? fiber_entry<16, true> : fiber_entry<16, false>;
   if (!entry) {
     fprintf(stderr, "SPT must be 16 or 32\n");
     return 2;
@@ -156,11 +165,12 @@ int main(int argc, char** argv) {
   fwrite(s_high_out.data(), 4, m, fo);
   fwrite(wpart.data(), 2, (size_t)P * N, fo);
   fwrite(stats.data(), 16, P, fo);
+  fwrite(p_int.data(), 4, m, fo);
   const uint32_t rounds = bar[0] & 0xFFFFu;
   fwrite(&err, 4, 1, fo);
   fwrite(&rounds, 4, 1, fo);
   fclose(fo);
-  printf("SPT %d P %d T %lld m %lld: status %u, barrier arrivals %u\n", g_spt, P, (long long)T,
-         (long long)m, err, rounds);
+  printf("SPT %d P %d T %lld m %lld mode %d: status %u, barrier arrivals %u\n", g_spt, P,
+         (long long)T, (long long)m, mode, err, rounds);
   return 0;
 }

@@ -7,10 +7,13 @@ and the results are compared with the oracle: s_low, the selection (ties to
 the lower token), s_high on that selection, and the value weights merged
 from the workgroups' binary16 partials and softmax statistics.
 
-The 32-keys-per-thread instance is built here with the cross-workgroup
+The 32-keys-per-thread instances are built here with the cross-workgroup
 window select, which the library does not plan (it returned wrong
 selections on the GPU); these cases check that the kernel's source, as
-written, selects and weights correctly at that size. Needs g++ only."""
+written, selects and weights correctly at that size, in the default build
+and in the build that takes the attention flags (none set, the integer-only
+softmax with p_int bit for bit against the oracle's integer steps on the
+kernel's own scores, reading B). Needs g++ only."""
 import os
 import re
 import shutil
@@ -63,36 +66,46 @@ def test_shared_declarations_all_rewritten():
     assert s.count("wg_shared") >= 7
 
 
-def _tied_case(T, seed):
-    """A one-row layer in which every fifth token carries the key record of
-    the token at the 97th percentile of s_low: about 3% of the row scores
-    above that value and a fifth of it ties there, so the threshold falls on
-    the tie and the row's workgroups split the tied tokens, lowest first."""
+def _tied_case(T, seed, every=5, above=None):
+    """A one-row layer in which every `every`-th token carries the key record
+    of the token ranked `above` from the top by s_low (default: at the 97th
+    percentile), so that about that many tokens score above the tied value
+    and the threshold falls on the tie: the row's workgroups split the tied
+    tokens, lowest first. With every fifth token tied the threshold bin is
+    too full for the window select (radix select); with every 200th it is
+    not (window select and its tie quota)."""
     c = synth.decode_case(B=1, Hq=1, Hkv=1, T=T, seed=seed, n_atoms=32768)
     ref = oracle.decode_attn(c.q, c.dk, c.dv, c.key_codes, c.val_codes, c.klow, c.khigh,
                              c.top_num, c.top_den, c.scale)
     s = ref["s_low"][0, 0]
-    src = int(np.argsort(s, kind="stable")[int(0.97 * T)])
+    order = np.argsort(-s, kind="stable")
+    src = int(order[above if above is not None else int(0.03 * T)])
     kc = c.key_codes.copy()
-    kc[0, 0, ::5] = kc[0, 0, src]
+    kc[0, 0, ::every] = kc[0, 0, src]
     c.key_codes = kc
     c.key_low = np.ascontiguousarray(kc[..., :c.klow])
     return c
 
 
-def _run(emu_dir, case, spt, P, order):
+MODE_DEFAULT, MODE_EXT, MODE_INT, MODE_READB = 0, 1, 2, 3
+
+
+def _run(emu_dir, case, spt, P, order, mode=MODE_DEFAULT):
+    reading = "B" if mode == MODE_READB else "A"
     ref = oracle.decode_attn(case.q, case.dk, case.dv, case.key_codes, case.val_codes,
-                             case.klow, case.khigh, case.top_num, case.top_den, case.scale)
+                             case.klow, case.khigh, case.top_num, case.top_den, case.scale,
+                             reading=reading)
     T, m, N = case.T, case.m, case.n_atoms
-    fin, fout = emu_dir / f"in_{spt}_{P}_{T}.bin", emu_dir / f"out_{spt}_{P}_{T}.bin"
+    fin = emu_dir / f"in_{spt}_{P}_{T}_{mode}.bin"
+    fout = emu_dir / f"out_{spt}_{P}_{T}_{mode}.bin"
     with open(fin, "wb") as f:
         np.array([N, T, m, P, case.klow, case.khigh], np.int64).tofile(f)
         ref["u"][0, 0].astype(np.float32).tofile(f)
         np.ascontiguousarray(case.key_low[0, 0], np.uint32).tofile(f)
         np.ascontiguousarray(case.key_codes[0, 0], np.uint32).tofile(f)
         np.ascontiguousarray(case.val_codes[0, 0], np.uint32).tofile(f)
-    r = subprocess.run([str(emu_dir / "rows_emu"), str(spt), str(fin), str(fout), str(order)],
-                       capture_output=True, text=True, timeout=600)
+    r = subprocess.run([str(emu_dir / "rows_emu"), str(spt), str(fin), str(fout), str(order),
+                        str(mode)], capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stdout + r.stderr
     raw = fout.read_bytes()
     off = 0
@@ -106,20 +119,32 @@ def _run(emu_dir, case, spt, P, order):
     s_low, sel, s_high = take(np.float32, T), take(np.int32, m), take(np.float32, m)
     wpart = take(np.uint16, P * N).reshape(P, N)
     stats = take(np.float32, P * 4).reshape(P, 4).astype(np.float64)
+    p_int = take(np.int32, m)
     status, arrivals = take(np.uint32, 2)
     assert status == 0
     assert np.abs(s_low - ref["s_low"][0, 0]).max() < 2e-6
     H.check_selection(sel[None].astype(np.int64), ref["s_low"][0, 0][None], m)
     ref_g = oracle.decode_attn(case.q, case.dk, case.dv, case.key_codes, case.val_codes,
                                case.klow, case.khigh, case.top_num, case.top_den, case.scale,
-                               sel=sel.reshape(1, 1, m))
+                               sel=sel.reshape(1, 1, m), reading=reading)
     assert np.abs(s_high - ref_g["s_high"][0, 0]).max() < 5e-6
-    # softmax merge of the partials: weight q holds binary16 values scaled by
-    # stats.z, with its (max, sum of exp) in stats.x, stats.y
+    h = wpart.view(np.float16).astype(np.float64)
     M, lsum, g = stats[:, 0], stats[:, 1], stats[:, 2]
-    Mx = M[lsum > 0].max()
-    c = np.where(lsum > 0, np.exp(M - Mx), 0.0)
-    w = (((c * g) / (c * lsum).sum())[:, None] * wpart.view(np.float16).astype(np.float64)).sum(0)
+    if mode == MODE_INT:
+        # integer steps bit for bit on the kernel's own selection and scores;
+        # the partials are already normalised and add (each scaled by stats.z)
+        ref_g = oracle.decode_attn(case.q, case.dk, case.dv, case.key_codes, case.val_codes,
+                                   case.klow, case.khigh, case.top_num, case.top_den,
+                                   case.scale, sel=sel.reshape(1, 1, m), softmax="int",
+                                   s_high_in=s_high.reshape(1, 1, m))
+        np.testing.assert_array_equal(p_int, ref_g["p_int"][0, 0])
+        w = (g[:, None] * h).sum(0)
+    else:
+        # softmax merge of the partials: weight q holds binary16 values scaled
+        # by stats.z, with its (max, sum of exp) in stats.x, stats.y
+        Mx = M[lsum > 0].max()
+        c = np.where(lsum > 0, np.exp(M - Mx), 0.0)
+        w = (((c * g) / (c * lsum).sum())[:, None] * h).sum(0)
     assert H.rel_l2(w, ref_g["w"][0, 0]) < H.W_RTOL
     return sel, ref, int(arrivals)
 
@@ -138,10 +163,33 @@ def test_row_kernel_emulated(emulator, spt, P, T, order):
     assert arrivals == 2 * P
 
 
-@pytest.mark.parametrize("spt,P", [(16, 4), (32, 2)])
-def test_row_kernel_emulated_ties(emulator, spt, P):
-    case = _tied_case(65536, seed=77)
-    sel, ref, _ = _run(emulator, case, spt, P, 0)
+@pytest.mark.parametrize("spt,P,every", [(16, 4, 5), (32, 2, 5), (16, 4, 200), (32, 4, 200)])
+def test_row_kernel_emulated_ties(emulator, spt, P, every):
+    T = 65536
+    m = -(-T // 10)
+    # every 200th token tied (328 tokens): about 197 of them are needed, so
+    # the tie is split across the first workgroups
+    case = _tied_case(T, seed=77, every=every, above=None if every == 5 else m - 164)
+    sel, ref, arrivals = _run(emulator, case, spt, P, 0)
     # identical records give identical scores on both sides: the selection is
     # the oracle's exactly, lowest tokens first among the tied ones
     np.testing.assert_array_equal(np.sort(sel), ref["sel"][0, 0])
+    tied = np.arange(0, T, every)
+    n_tied_sel = int(np.isin(tied, sel).sum())
+    assert 0 < n_tied_sel < tied.size
+    if every == 200:
+        assert arrivals == 2 * P   # decided by the window select
+
+
+@pytest.mark.parametrize("spt,P,T,mode", [
+    (32, 8, 262144, MODE_EXT),     # the attention-flag build, no flag set
+    (32, 4, 131072, MODE_INT),     # integer-only softmax: two more exchanges
+    (32, 4, 131072, MODE_READB),   # reading B: unselected tokens enter the softmax
+    (16, 8, 131072, MODE_INT),
+])
+def test_row_kernel_emulated_flag_build(emulator, spt, P, T, mode):
+    case = synth.decode_case(B=1, Hq=1, Hkv=1, T=T, seed=60 + spt + P + mode, n_atoms=32768)
+    _, _, arrivals = _run(emulator, case, spt, P, 0, mode)
+    # window select + list placement, and for the integer softmax its two
+    # exchanges (score range, sum of e')
+    assert arrivals == (4 if mode == MODE_INT else 2) * P
