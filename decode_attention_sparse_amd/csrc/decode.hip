@@ -1123,7 +1123,9 @@ sdkv_status plan_decode(const sdkv_attn_args* a, DecodePlan* p) {
   q.fast = (a->K == 16 && a->klow <= 4 && a->khigh <= 16) ? 1 : 0;
   q.nrt = (int)((q.rows + WRT - 1) / WRT);
   const int nsub_total = (a->n_atoms + WSUB - 1) / WSUB;
-  const int target = std::max(1, 512 / q.nrt);
+  // about one W.Dv workgroup per compute unit: more atom chunks would each
+  // add an output partial for k_reduce_out to read
+  const int target = std::max(1, kPlanCUs / q.nrt);
   q.nsub = std::max(1, (nsub_total + target - 1) / target);
   q.nchunks = (nsub_total + q.nsub - 1) / q.nsub;
 
