@@ -1110,7 +1110,9 @@ sdkv_status plan_decode(const sdkv_attn_args* a, DecodePlan* p) {
   const int64_t T = a->T;
   const int64_t p_min = (T + kMaxChunk - 1) / kMaxChunk;
   const int64_t p_par = std::max<int64_t>(1, kPlanCUs / std::max<int64_t>(1, q.rows));
-  const int64_t p_cap = std::max<int64_t>(1, (T + 2047) / 2048);
+  // a row is split only into chunks of at least 4096 tokens: below that the
+  // cross-workgroup exchange costs more than the split saves
+  const int64_t p_cap = std::max<int64_t>(1, (T + 4095) / 4096);
   int64_t P = std::max(p_min, std::min(p_par, p_cap));
   // rows split over several workgroups hold at most kMaxCoopSPT keys per
   // thread (the 32-key row kernel is built for single-workgroup rows only)
