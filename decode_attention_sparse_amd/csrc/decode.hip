@@ -34,6 +34,10 @@ struct UArgs {
   float scale;
   float* U;            // [rows, N] (workspace)
   float* u_dbg;        // optional copy
+  // shared selection: Ug[(b, g)] = scale * (sum_j q[b, g G + j]) Dk^T, the
+  // group sums of U by linearity (bf16 dictionaries); ngroups = 0 otherwise
+  float* Ug;           // [ngroups, N]
+  int ngroups, Hq, Hkv, G;
   uint32_t* zero;      // region cleared by this kernel
   int64_t zero_words;
 };
@@ -44,14 +48,25 @@ __device__ __forceinline__ void clear_region(const UArgs& a) {
     a.zero[i] = 0u;
 }
 
-// bf16 dictionary: each wave owns 16 atoms; loops over 16-row query tiles.
+// bf16 dictionary: each wave owns 16 atoms (its Dk fragments stay in
+// registers); the workgroup stages the query rows in LDS, 64 at a time, so a
+// query row is read from memory once per workgroup, not once per wave. bf16
+// query rows go to the matrix cores as they are; fp32 query rows and the
+// group rows of the shared selection (the group's query rows summed in fp32,
+// head order) are split into three bf16 parts that hold them exactly, and
+// run as three accumulating MFMAs.
+constexpr int UQR = 64;          // query rows staged per pass
+constexpr int UQP = 128 + 8;     // LDS pitch of a staged row (bf16 elements)
 __global__ __launch_bounds__(256) void k_utable_bf16(UArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t s_qh[UQR * UQP];
+  __shared__ __attribute__((aligned(16))) uint16_t s_qm[UQR * UQP];
+  __shared__ __attribute__((aligned(16))) uint16_t s_ql[UQR * UQP];
   clear_region(a);
-  const int w = wave_id(), l = lane_id();
+  const int tid = threadIdx.x, w = wave_id(), l = lane_id();
   const int a0 = (blockIdx.x * 4 + w) * 16;
-  if (a0 >= a.N) return;
   const int atom = a0 + (l & 15);
   const int ks = a.d >> 5;
+  const int segs = a.d >> 3;  // 8-element segments per row
   const uint16_t* dk = (const uint16_t*)a.dk;
   u32x4 bf[4];
 #pragma unroll
@@ -60,49 +75,87 @@ __global__ __launch_bounds__(256) void k_utable_bf16(UArgs a) {
     if (s < ks && atom < a.N)
       bf[s] = *(const u32x4*)(dk + (int64_t)atom * a.d + 32 * s + 8 * (l >> 4));
   }
-  for (int r0 = 0; r0 < a.rows; r0 += 16) {
-    const int row = r0 + (l & 15);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (a.q_f32) {
-      // fp32 queries: three exact bf16 parts, each product exact on the
-      // matrix cores, fp32 accumulation
+  // pass kind 0: query rows [p0, p0 + 64) of [0, rows); kind 1: group rows
+  for (int kind = 0; kind < 2; ++kind) {
+    const int nrows = kind == 0 ? a.rows : a.ngroups;
+    const bool split = kind == 1 || a.q_f32;
+    for (int p0 = 0; p0 < nrows; p0 += UQR) {
+      __syncthreads();  // the previous pass's fragments have been read
+      // stage: item = (row, 8-element segment), UQR * segs <= 1024 items
+      for (int it = tid; it < UQR * segs; it += 256) {
+        const int r = it / segs, sg = it % segs, row = p0 + r;
+        float v[8];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        if (s < ks) {
-          float v[8];
+        for (int e = 0; e < 8; ++e) v[e] = 0.f;
+        u32x4 raw = u32x4{0u, 0u, 0u, 0u};
+        if (row < nrows) {
+          if (kind == 0) {
+            const int64_t off = (int64_t)row * a.d + 8 * sg;
+            if (a.q_f32) {
+              const float4* qp = (const float4*)((const float*)a.q + off);
+              const float4 x0 = qp[0], x1 = qp[1];
+              v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
+              v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+            } else {
+              raw = *(const u32x4*)((const uint16_t*)a.q + off);
+            }
+          } else {
+            const int64_t q0 = (int64_t)(row / a.Hkv) * a.Hq + (int64_t)(row % a.Hkv) * a.G;
+            for (int j = 0; j < a.G; ++j) {
+              const int64_t off = (q0 + j) * a.d + 8 * sg;
+              if (a.q_f32) {
+                const float4* qp = (const float4*)((const float*)a.q + off);
+                const float4 x0 = qp[0], x1 = qp[1];
+                v[0] += x0.x; v[1] += x0.y; v[2] += x0.z; v[3] += x0.w;
+                v[4] += x1.x; v[5] += x1.y; v[6] += x1.z; v[7] += x1.w;
+              } else {
+                const u32x4 q = *(const u32x4*)((const uint16_t*)a.q + off);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = 0.f;
-          if (row < a.rows) {
-            const float4* qp = (const float4*)((const float*)a.q + (int64_t)row * a.d + 32 * s + 8 * (l >> 4));
-            const float4 x0 = qp[0], x1 = qp[1];
-            v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
-            v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+                for (int e = 0; e < 4; ++e) {
+                  v[2 * e] += bf16_lo(q[e]);
+                  v[2 * e + 1] += bf16_hi(q[e]);
+                }
+              }
+            }
           }
+        }
+        const int o = r * UQP + 8 * sg;
+        if (split) {
           u32x4 hi, mid, lo;
           split3_bf16(v, hi, mid, lo);
-          acc = mfma_bf16(hi, bf[s], acc);
-          acc = mfma_bf16(mid, bf[s], acc);
-          acc = mfma_bf16(lo, bf[s], acc);
+          *(u32x4*)(s_qh + o) = hi;
+          *(u32x4*)(s_qm + o) = mid;
+          *(u32x4*)(s_ql + o) = lo;
+        } else {
+          *(u32x4*)(s_qh + o) = raw;
         }
       }
-    } else {
+      __syncthreads();
+      float* dst = kind == 0 ? a.U : a.Ug;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        if (s < ks) {
-          u32x4 af = u32x4{0u, 0u, 0u, 0u};
-          if (row < a.rows)
-            af = *(const u32x4*)((const uint16_t*)a.q + (int64_t)row * a.d + 32 * s + 8 * (l >> 4));
-          acc = mfma_bf16(af, bf[s], acc);
+      for (int rt = 0; rt < UQR / 16; ++rt) {
+        if (p0 + 16 * rt >= nrows) break;
+        const int o = (16 * rt + (l & 15)) * UQP + 8 * (l >> 4);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          if (s < ks) {
+            acc = mfma_bf16(*(const u32x4*)(s_qh + o + 32 * s), bf[s], acc);
+            if (split) {
+              acc = mfma_bf16(*(const u32x4*)(s_qm + o + 32 * s), bf[s], acc);
+              acc = mfma_bf16(*(const u32x4*)(s_ql + o + 32 * s), bf[s], acc);
+            }
+          }
         }
-      }
-    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = r0 + 4 * (l >> 4) + i;
-      if (rr < a.rows && atom < a.N) {
-        const float v = acc[i] * a.scale;
-        a.U[(int64_t)rr * a.N + atom] = v;
-        if (a.u_dbg) a.u_dbg[(int64_t)rr * a.N + atom] = v;
+        for (int i = 0; i < 4; ++i) {
+          const int rr = p0 + 16 * rt + 4 * (l >> 4) + i;
+          if (rr < nrows && atom < a.N) {
+            const float v = acc[i] * a.scale;
+            dst[(int64_t)rr * a.N + atom] = v;
+            if (kind == 0 && a.u_dbg) a.u_dbg[(int64_t)rr * a.N + atom] = v;
+          }
+        }
       }
     }
   }
@@ -1206,6 +1259,13 @@ sdkv_status launch_decode(const sdkv_attn_args* a, const DecodePlan& p, void* ws
   ua.u_dbg = a->u;
   ua.zero = (uint32_t*)(base + p.off_zero);
   ua.zero_words = (int64_t)(p.zero_bytes / 4);
+  const bool shared = a->select_mode == SDKV_SELECT_KV;
+  const bool ug_in_utable = shared && a->dict_dtype == SDKV_BF16;
+  ua.Ug = (float*)(base + p.off_ug);
+  ua.ngroups = ug_in_utable ? a->B * a->Hkv : 0;
+  ua.Hq = a->Hq;
+  ua.Hkv = a->Hkv;
+  ua.G = a->Hq / a->Hkv;
   if (!record_stage(ev, 0, stream)) return SDKV_ERR_DEVICE;
   if (a->dict_dtype == SDKV_BF16) {
     const int grid = (a->n_atoms + 63) / 64;
@@ -1217,8 +1277,8 @@ sdkv_status launch_decode(const sdkv_attn_args* a, const DecodePlan& p, void* ws
   }
   if (hipGetLastError() != hipSuccess) return SDKV_ERR_DEVICE;
 
-  // shared selection: the group sums of U
-  if (a->select_mode == SDKV_SELECT_KV) {
+  // shared selection with an fp32 dictionary: the group sums of U
+  if (shared && !ug_in_utable) {
     const int64_t n = (int64_t)a->B * a->Hkv * a->n_atoms;
     hipLaunchKernelGGL(k_usum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, U,
                        (float*)(base + p.off_ug), n, a->n_atoms, a->Hq / a->Hkv);
