@@ -900,37 +900,47 @@ __device__ __forceinline__ void wdv_merge16(const WdvArgs& a, const float* s_coe
   }
 }
 
-// 512 threads: the A tile (32 rows x 128 atoms) is merged 8 atoms per thread;
-// wave w computes output columns [16w, 16w+16) for both 16-row tiles. The
-// loads of a sub-chunk (up to 8 weight partials per thread and the Dv rows)
+// 512 threads: the A tile (RT = 32 or 64 rows x 128 atoms) is merged 8
+// atoms per thread and row (RT / 32 rows per thread); wave w computes output
+// columns [16w, 16w+16) for all RT / 16 row tiles. Taller tiles read each Dv
+// sub-chunk for more rows (layers with many query rows). The loads of a
+// sub-chunk (up to 8 weight partials per thread, and the Dv rows)
 // are issued before anything waits on them; the first sub-chunk's loads go
 // out before the softmax-merge coefficients are computed.
 constexpr int WDV_PQ = 8;                 // partials per prefetched batch
+template <int RT>
 __global__ __launch_bounds__(512) void k_wdv_bf16(WdvArgs a) {
-  __shared__ float s_coef[WRT * kMaxRowP];
-  __shared__ __attribute__((aligned(16))) uint16_t s_ahi[WRT * WPITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t s_alo[WRT * WPITCH];
+  static_assert(RT == 32 || RT == 64, "row tile height");
+  constexpr int RPT = RT / 32;            // A rows per thread
+  constexpr int NRT = RT / 16;            // 16-row MFMA tiles
+  constexpr int PQ = WDV_PQ / RPT;        // partials per row prefetched
+  __shared__ float s_coef[RT * kMaxRowP];
+  __shared__ __attribute__((aligned(16))) uint16_t s_ahi[RT * WPITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t s_alo[RT * WPITCH];
   __shared__ __attribute__((aligned(16))) uint32_t s_bt[128 * BPITCH];
 
   const int tid = threadIdx.x, w = wave_id(), l = lane_id();
   const int L = xcd_tile(blockIdx.x, a.nchunks * a.nrt);
   const int chunk = L / a.nrt, rt = L % a.nrt;
-  const int r0 = rt * WRT;
+  const int r0 = rt * RT;
   const uint16_t* dv = (const uint16_t*)a.dv;
   const int ncol = a.d >> 4;
-  // this thread's A slot (row r, atoms c0 .. c0+8) and B items
+  // this thread's A slots (rows ar + 32 u, atoms c0 .. c0+8) and B items
   const int ar = tid >> 4, ac0 = (tid & 15) * 8;
-  const int arow = r0 + ar;
   const bool a_fast = (a.N & 7) == 0;
   constexpr int BIT = (WSUB / 2) * (128 / 8) / 512;  // B items per thread (d = 128)
-  u32x4 px[WDV_PQ];
+  u32x4 px[RPT][PQ];
   u32x4 bx[BIT][2];
   auto load_sub = [&](int a0) {
 #pragma unroll
-    for (int q = 0; q < WDV_PQ; ++q) {
-      px[q] = u32x4{0u, 0u, 0u, 0u};
-      if (q < a.P && arow < a.rows && a_fast && a0 + ac0 + 8 <= a.N)
-        px[q] = *(const u32x4*)(a.wpart + ((int64_t)arow * a.P + q) * a.N + a0 + ac0);
+    for (int u = 0; u < RPT; ++u) {
+      const int arow = r0 + ar + 32 * u;
+#pragma unroll
+      for (int q = 0; q < PQ; ++q) {
+        px[u][q] = u32x4{0u, 0u, 0u, 0u};
+        if (q < a.P && arow < a.rows && a_fast && a0 + ac0 + 8 <= a.N)
+          px[u][q] = *(const u32x4*)(a.wpart + ((int64_t)arow * a.P + q) * a.N + a0 + ac0);
+      }
     }
 #pragma unroll
     for (int k = 0; k < BIT; ++k) {
@@ -950,15 +960,15 @@ __global__ __launch_bounds__(512) void k_wdv_bf16(WdvArgs a) {
 
   // softmax-merge coefficients of the tile's rows (all stats loads first)
   {
-    float4 st[WRT / 8];
+    float4 st[RT / 8];
 #pragma unroll
-    for (int k = 0; k < WRT / 8; ++k) {
+    for (int k = 0; k < RT / 8; ++k) {
       const int row = r0 + w + 8 * k;
       st[k] = make_float4(-INFINITY, 0.f, 0.f, 0.f);
       if (row < a.rows && l < a.P) st[k] = a.stats[(int64_t)row * a.P + l];
     }
 #pragma unroll
-    for (int k = 0; k < WRT / 8; ++k) {
+    for (int k = 0; k < RT / 8; ++k) {
       const float Mq = st[k].x, lq = st[k].y;
       const float Mx = wave_max(Mq);
       const float c = (lq > 0.f) ? __expf(Mq - Mx) : 0.f;
@@ -969,33 +979,37 @@ __global__ __launch_bounds__(512) void k_wdv_bf16(WdvArgs a) {
     }
   }
   __syncthreads();
-  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  f32x4 acc[NRT];
+#pragma unroll
+  for (int rr = 0; rr < NRT; ++rr) acc[rr] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int sub = 0; sub < a.nsub; ++sub) {
     a0 = (chunk * a.nsub + sub) * WSUB;
     if (a0 >= a.N) break;
     if (sub > 0) load_sub(a0);
-    // A: merged weights of (row ar, atoms ac0 .. ac0+8), split into bf16 hi + lo
-    {
+    // A: merged weights of (row, atoms ac0 .. ac0+8), split into bf16 hi + lo
+#pragma unroll
+    for (int u = 0; u < RPT; ++u) {
+      const int lr = ar + 32 * u, arow = r0 + lr;
       float v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = 0.f;
       if (arow < a.rows) {
         if (a_fast && a0 + ac0 + 8 <= a.N) {
 #pragma unroll
-          for (int q = 0; q < WDV_PQ; ++q) {
+          for (int q = 0; q < PQ; ++q) {
             if (q < a.P) {
-              const float c = s_coef[ar * kMaxRowP + q];
+              const float c = s_coef[lr * kMaxRowP + q];
 #pragma unroll
               for (int j = 0; j < 4; ++j) {
-                v[2 * j] = fmaf(c, f16_bits_to_f32(px[q][j] & 0xFFFFu), v[2 * j]);
-                v[2 * j + 1] = fmaf(c, f16_bits_to_f32(px[q][j] >> 16), v[2 * j + 1]);
+                v[2 * j] = fmaf(c, f16_bits_to_f32(px[u][q][j] & 0xFFFFu), v[2 * j]);
+                v[2 * j + 1] = fmaf(c, f16_bits_to_f32(px[u][q][j] >> 16), v[2 * j + 1]);
               }
             }
           }
           // partials beyond the prefetched batch
-          for (int q = WDV_PQ; q < a.P; ++q) {
-            const float c = s_coef[ar * kMaxRowP + q];
+          for (int q = PQ; q < a.P; ++q) {
+            const float c = s_coef[lr * kMaxRowP + q];
             const u32x4 x = *(const u32x4*)(a.wpart + ((int64_t)arow * a.P + q) * a.N + a0 + ac0);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -1006,7 +1020,7 @@ __global__ __launch_bounds__(512) void k_wdv_bf16(WdvArgs a) {
         } else {
           const uint16_t* src = a.wpart + (int64_t)arow * a.P * a.N + a0 + ac0;
           for (int q = 0; q < a.P; ++q) {
-            const float c = s_coef[ar * kMaxRowP + q];
+            const float c = s_coef[lr * kMaxRowP + q];
             for (int e = 0; e < 8 && a0 + ac0 + e < a.N; ++e)
               v[e] = fmaf(c, f16_bits_to_f32(src[(int64_t)q * a.N + e]), v[e]);
           }
@@ -1021,8 +1035,8 @@ __global__ __launch_bounds__(512) void k_wdv_bf16(WdvArgs a) {
         const uint32_t h0 = f32_to_bf16_rne(v[e]), h1 = f32_to_bf16_rne(v[e + 1]);
         const uint32_t l0 = f32_to_bf16_rne(v[e] - __uint_as_float(h0 << 16));
         const uint32_t l1 = f32_to_bf16_rne(v[e + 1] - __uint_as_float(h1 << 16));
-        *(uint32_t*)&s_ahi[ar * WPITCH + ac0 + e] = h0 | (h1 << 16);
-        *(uint32_t*)&s_alo[ar * WPITCH + ac0 + e] = l0 | (l1 << 16);
+        *(uint32_t*)&s_ahi[lr * WPITCH + ac0 + e] = h0 | (h1 << 16);
+        *(uint32_t*)&s_alo[lr * WPITCH + ac0 + e] = l0 | (l1 << 16);
       }
     }
     // B: Dv rows a0..a0+127 transposed to [dim][atom pair]
@@ -1045,7 +1059,7 @@ __global__ __launch_bounds__(512) void k_wdv_bf16(WdvArgs a) {
         const int kk = ks * 32 + 8 * (l >> 4);
         const u32x4 b0 = *(const u32x4*)(s_bt + (16 * w + (l & 15)) * BPITCH + (kk >> 1));
 #pragma unroll
-        for (int rr = 0; rr < 2; ++rr) {
+        for (int rr = 0; rr < NRT; ++rr) {
           const u32x4 ah = *(const u32x4*)(s_ahi + (rr * 16 + (l & 15)) * WPITCH + kk);
           const u32x4 al = *(const u32x4*)(s_alo + (rr * 16 + (l & 15)) * WPITCH + kk);
           acc[rr] = mfma_bf16(ah, b0, acc[rr]);
@@ -1058,7 +1072,7 @@ __global__ __launch_bounds__(512) void k_wdv_bf16(WdvArgs a) {
   if (w < ncol) {
     float* dst = a.opart + (int64_t)chunk * a.rows * a.d;
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr)
+    for (int rr = 0; rr < NRT; ++rr)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = r0 + rr * 16 + 4 * (l >> 4) + i;
@@ -1176,7 +1190,10 @@ sdkv_status plan_decode(const sdkv_attn_args* a, DecodePlan* p) {
   q.spt = spt_for(q.chunk);
   if (q.spt == 0) return SDKV_ERR_UNSUPPORTED;
   q.fast = (a->K == 16 && a->klow <= 4 && a->khigh <= 16) ? 1 : 0;
-  q.nrt = (int)((q.rows + WRT - 1) / WRT);
+  // W.Dv row tiles: 64 rows with a bf16 dictionary when there are more than
+  // 32 query rows (each Dv sub-chunk is then read for twice the rows)
+  q.wrt = (a->dict_dtype == SDKV_BF16 && q.rows > 32) ? 64 : WRT;
+  q.nrt = (int)((q.rows + q.wrt - 1) / q.wrt);
   const int nsub_total = (a->n_atoms + WSUB - 1) / WSUB;
   // about one W.Dv workgroup per compute unit: more atom chunks would each
   // add an output partial for k_reduce_out to read
@@ -1369,7 +1386,10 @@ sdkv_status launch_decode(const sdkv_attn_args* a, const DecodePlan& p, void* ws
   const dim3 wgrid((unsigned)(p.nchunks * p.nrt));
   if (!record_stage(ev, 2, stream)) return SDKV_ERR_DEVICE;
   if (a->dict_dtype == SDKV_BF16)
-    hipLaunchKernelGGL(k_wdv_bf16, wgrid, dim3(512), 0, stream, wa);
+  {
+    if (p.wrt == 64) hipLaunchKernelGGL(k_wdv_bf16<64>, wgrid, dim3(512), 0, stream, wa);
+    else hipLaunchKernelGGL(k_wdv_bf16<32>, wgrid, dim3(512), 0, stream, wa);
+  }
   else
     hipLaunchKernelGGL(k_wdv_f32, wgrid, dim3(256), 0, stream, wa);
   if (hipGetLastError() != hipSuccess) return SDKV_ERR_DEVICE;

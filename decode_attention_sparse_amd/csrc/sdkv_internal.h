@@ -35,7 +35,8 @@ struct DecodePlan {
   int64_t chunk = 0;     // tokens per workgroup
   int spt = 0;           // keys per thread (template instance)
   int fast = 0;          // K == 16, klow <= 4, khigh <= 16: vector code loads
-  int nrt = 0;           // 32-row tiles in the W.Dv kernel
+  int wrt = 32;          // rows per W.Dv tile (32, or 64 for bf16 with > 32 rows)
+  int nrt = 0;           // row tiles in the W.Dv kernel
   int nsub = 1;          // 128-atom sub-chunks per W.Dv workgroup
   int nchunks = 0;       // atom chunks in the W.Dv kernel
   // workspace byte offsets
