@@ -117,6 +117,14 @@ def test_cooperative_rows_with_the_selection_list_in_the_workspace():
     compare(case, run_gpu(case))
 
 
+def test_tall_value_weight_tiles_partly_filled():
+    """40 query rows: the W.Dv kernel takes one 64-row tile, 24 rows of it
+    empty, and merges the partials of 3 workgroups per row."""
+    H.log("decode B=5 Hq=8 Hkv=2 T=9000 (40 rows)")
+    case = synth.decode_case(B=5, Hq=8, Hkv=2, T=9000, seed=16, n_atoms=4096)
+    compare(case, run_gpu(case))
+
+
 def test_low_plane_from_key_codes():
     H.log("decode without a separate low plane")
     case = synth.decode_case(B=1, Hq=4, Hkv=1, T=3000, seed=8, n_atoms=1024)

@@ -16,10 +16,10 @@ pytestmark = pytest.mark.gpu
 W_RTOL = H.W_RTOL    # fixed-point sums handed over as binary16
 
 
-def run(case, *, select="kv", softmax="float", interleaved=False, debug=True):
+def run(case, *, select="kv", softmax="float", interleaved=False, debug=True, q_f32=False):
     import decode_attention_sparse_amd as sd
     torch = H.torch_mod()
-    q = H.to_bf16(case.q)
+    q = H.to_f32(case.q) if q_f32 else H.to_bf16(case.q)
     dk, dv = H.to_bf16(case.dk), H.to_bf16(case.dv)
     if interleaved:
         kc = H.to_words(np.stack([case.key_codes, case.val_codes], axis=3))
@@ -132,3 +132,15 @@ def test_shared_select_128k_layer():
     o = run(case, interleaved=True, debug=False)["out"]
     assert H.rel_l2(o, g["out"]) < 1e-5
     H.log(f"  128k shared: group {gk} sel-diff-rows {ndiff} out {o_err:.2e}")
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (28, 4)])
+def test_shared_select_fp32_queries(Hq, Hkv):
+    """fp32 queries (not bf16-representable): the group rows of the ranking
+    table come from the fp32 sum of each group's query rows (G = 4 and 7)."""
+    H.log(f"shared selection: fp32 queries, Hq={Hq} Hkv={Hkv}")
+    case = synth.decode_case(B=1, Hq=Hq, Hkv=Hkv, T=9000, seed=450 + Hq, n_atoms=4096)
+    rng = np.random.default_rng(451 + Hq)
+    case.q = rng.standard_normal(case.q.shape).astype(np.float32)
+    assert not np.array_equal(case.q, synth.bf16_round(case.q))
+    check(case, run(case, q_f32=True), f"fp32 q, G={Hq // Hkv}")
