@@ -176,6 +176,24 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* tmp, u
   *total = tot;
   return base + inc - v;
 }
+// The same scan without its closing barrier: the caller passes a workgroup
+// barrier before `tmp` is written again.
+template <int NW>
+__device__ __forceinline__ uint32_t block_excl_scan_open(uint32_t v, uint32_t* tmp,
+                                                         uint32_t* total) {
+  const uint32_t inc = wave_incl_scan(v);
+  if (lane_id() == 63) tmp[wave_id()] = inc;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const uint32_t s = tmp[i];
+    base += (i < wave_id()) ? s : 0u;
+    tot += s;
+  }
+  *total = tot;
+  return base + inc - v;
+}
 template <int NW>
 __device__ __forceinline__ float block_max(float v, float* tmp) {
   v = wave_max(v);

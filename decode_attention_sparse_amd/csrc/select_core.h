@@ -84,10 +84,12 @@ __device__ __forceinline__ uint32_t ordered_ranks(Mask bits, SelShared& sh, F&& 
 // uniform across the block. (If fewer than need[q] keys exist, v[q] = 0 and
 // above[q] = 0.) One prefix scan over the per-thread bin sums serves every
 // rank: the count above thread t's bins is total - (inclusive prefix at t).
+// zero_bins: every thread clears its own bins once it has read them, so the
+// histogram is zero when the function returns.
 template <int NQ>
 __device__ __forceinline__ void find_digits(SelShared& sh, int nbins, const uint32_t (&need)[NQ],
                                             uint32_t (&v)[NQ], uint32_t (&above_out)[NQ],
-                                            uint32_t* total = nullptr) {
+                                            uint32_t* total = nullptr, bool zero_bins = false) {
   static_assert(NQ >= 1 && NQ <= 2, "bcast holds two (digit, above) pairs");
   const int tid = threadIdx.x;
   const int bpt = nbins / SB;
@@ -96,7 +98,8 @@ __device__ __forceinline__ void find_digits(SelShared& sh, int nbins, const uint
   if (tid == 0)
     for (int q = 0; q < 2 * NQ; ++q) sh.bcast[q] = 0u;
   uint32_t tot;
-  const uint32_t ex = block_excl_scan<SNW>(loc, sh.tmp, &tot);
+  // (sh.tmp is next written after the barriers below)
+  const uint32_t ex = block_excl_scan_open<SNW>(loc, sh.tmp, &tot);
   const uint32_t above = tot - ex - loc;
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
@@ -113,6 +116,8 @@ __device__ __forceinline__ void find_digits(SelShared& sh, int nbins, const uint
       }
     }
   }
+  if (zero_bins)
+    for (int i = 0; i < bpt; ++i) sh.hist[tid * bpt + i] = 0u;
   __syncthreads();
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
@@ -452,7 +457,7 @@ __device__ __forceinline__ bool sample_window_select(const uint32_t (&key)[SPT],
   __syncthreads();  // also: every thread has read sh.tmp
   const uint32_t rr[2] = {r_hi, r_lo};
   uint32_t bb[2], gtx[2];
-  find_digits<2>(sh, 2048, rr, bb, gtx);
+  find_digits<2>(sh, 2048, rr, bb, gtx, nullptr, true);  // leaves sh.hist zero
   const int b_hi = (int)bb[0], b_lo = (int)bb[1];
   // key thresholds at the edges of the coarse bins b_lo and b_hi
   uint32_t lo_key = 1u, hi_key = 0xFFFFFFFFu;
@@ -464,8 +469,6 @@ __device__ __forceinline__ bool sample_window_select(const uint32_t (&key)[SPT],
   const uint32_t mulc =
       (uint32_t)fmin(4294967295.0, 2048.0 * 4294967296.0 / (double)(hi_key - lo_key));
   // --- publish: count above the window; window keys sorted by fine bin --------
-  for (int i = tid; i < 2048; i += SB) sh.hist[i] = 0u;
-  __syncthreads();
   uint32_t na = 0;
   uint32_t pos[SPT];  // (fine bin << 16 | rank in bin) of window keys, else ~0
 #pragma unroll
@@ -484,7 +487,8 @@ __device__ __forceinline__ bool sample_window_select(const uint32_t (&key)[SPT],
   // exclusive prefix over the 2048 bins, two per thread
   const uint32_t c0 = sh.hist[2 * tid], c1 = sh.hist[2 * tid + 1];
   uint32_t tot;
-  const uint32_t ex = block_excl_scan<SNW>(c0 + c1, sh.tmp, &tot);
+  // (sh.tmp is next written after the barrier below)
+  const uint32_t ex = block_excl_scan_open<SNW>(c0 + c1, sh.tmp, &tot);
   uint32_t* mywt = wt + (int64_t)g.p * 2048;
   __hip_atomic_store((uint64_t*)(mywt + 2 * tid),
                      ((uint64_t)(c1 | ((ex + c0) << 16)) << 32) | (c0 | (ex << 16)),

@@ -246,6 +246,21 @@ inline uint32_t block_excl_scan(uint32_t v, uint32_t* tmp, uint32_t* total) {
   return base + inc - v;
 }
 
+template <int NW>
+inline uint32_t block_excl_scan_open(uint32_t v, uint32_t* tmp, uint32_t* total) {
+  const uint32_t inc = wave_incl_scan(v);
+  if (lane_id() == 63) tmp[wave_id()] = inc;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+  for (int i = 0; i < NW; ++i) {
+    const uint32_t s = tmp[i];
+    base += (i < wave_id()) ? s : 0u;
+    tot += s;
+  }
+  *total = tot;
+  return base + inc - v;
+}
+
 struct WaitCtl {
   uint32_t* err;
   uint32_t limit;
