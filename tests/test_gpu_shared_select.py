@@ -20,7 +20,10 @@ def run(case, *, select="kv", softmax="float", interleaved=False, debug=True, q_
     import decode_attention_sparse_amd as sd
     torch = H.torch_mod()
     q = H.to_f32(case.q) if q_f32 else H.to_bf16(case.q)
-    dk, dv = H.to_bf16(case.dk), H.to_bf16(case.dv)
+    if case.dict_dtype == "f32":
+        dk, dv = H.to_f32(case.dk), H.to_f32(case.dv)
+    else:
+        dk, dv = H.to_bf16(case.dk), H.to_bf16(case.dv)
     if interleaved:
         kc = H.to_words(np.stack([case.key_codes, case.val_codes], axis=3))
         vc = None
@@ -144,3 +147,23 @@ def test_shared_select_fp32_queries(Hq, Hkv):
     case.q = rng.standard_normal(case.q.shape).astype(np.float32)
     assert not np.array_equal(case.q, synth.bf16_round(case.q))
     check(case, run(case, q_f32=True), f"fp32 q, G={Hq // Hkv}")
+
+
+def test_shared_select_many_groups():
+    """80 KV-head groups (B=10, Hkv=8): the U-table kernel stages their summed
+    queries in two passes of 64."""
+    H.log("shared selection: B=10 Hq=16 Hkv=8 T=3000 (80 groups)")
+    case = synth.decode_case(B=10, Hq=16, Hkv=8, T=3000, seed=460, n_atoms=2048)
+    check(case, run(case), "80 groups")
+
+
+def test_shared_select_fp32_dictionary():
+    """fp32 dictionaries: the group rows of U are summed from the heads' U rows
+    by their own kernel."""
+    H.log("shared selection: fp32 dictionaries, B=2 Hq=8 Hkv=2 T=5000")
+    case = synth.decode_case(B=2, Hq=8, Hkv=2, T=5000, seed=470, n_atoms=2048)
+    rng = np.random.default_rng(471)
+    case.dk = synth.make_dictionary(rng, 2048, 128, "f32")
+    case.dv = synth.make_dictionary(rng, 2048, 128, "f32")
+    case.dict_dtype = "f32"
+    check(case, run(case), "fp32 dictionaries")
