@@ -92,6 +92,21 @@ def test_ragged_sizes(n, N, K):
     assert np.array_equal(g["low_plane"], g["codes"][:, :min(3, K)])
 
 
+@pytest.mark.parametrize("n", [40, 200])
+def test_max_atoms(n):
+    """65,536 atoms, the largest dictionary the boundary takes (uint16
+    indices; 4,096 16-atom tiles fill the batch screen's 12-bit tile field),
+    on the small path (n <= 64) and the batch path."""
+    H.log(f"encode n={n} N=65536")
+    rng = np.random.default_rng(65536 + n)
+    D = synth.make_dictionary(rng, 65536, 128, "bf16")
+    x, _, _ = synth.make_sparse_vectors(rng, D, n, 16, 0.05, "absdesc")
+    x = synth.bf16_round(x)
+    g = run(x, D, 16)
+    ri, _, _ = compare(x, D, 16, g, f"n={n} N=65536")
+    assert ri.max() >= 32768   # atoms in the upper half are picked
+
+
 def test_head_dim_64_bf16():
     rng = np.random.default_rng(21)
     D = synth.make_dictionary(rng, 3000, 64, "bf16")
