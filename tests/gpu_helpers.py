@@ -106,3 +106,24 @@ def f16_half_ulp(x):
     x = np.abs(np.asarray(x, dtype=np.float64))
     e = np.floor(np.log2(np.maximum(x, 2.0 ** -14)))
     return 2.0 ** (e - 11)
+
+
+def random_decode_shape(seed, base=9000):
+    """A seeded random decode shape over the planner's paths: from one query row to a
+    few hundred (32- and 64-row W.Dv tiles), contexts that split a row over 1 to
+    8+ workgroups, 4 to 16 keys per thread, head dims 64/128, code lengths
+    16/32 and selected fractions from 1/20 to 1/2. `base` picks the
+    family of shapes (one per test file)."""
+    rng = np.random.default_rng(base + seed)
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([1, 2, 4, 7]))
+    B = int(rng.integers(1, 8))
+    T = int(rng.choice([1, 7, 500, 4096, 4097, 9000, 20000, 60000]))
+    d = int(rng.choice([64, 128]))
+    K = int(rng.choice([16, 32]))
+    klow = int(rng.integers(1, 5))
+    khigh = int(rng.integers(klow, K + 1))
+    num, den = [(1, 20), (1, 10), (1, 4), (1, 2)][int(rng.integers(0, 4))]
+    n_atoms = int(rng.choice([777, 2048, 8192]))
+    return dict(B=B, Hq=Hkv * G, Hkv=Hkv, T=T, d=d, K=K, klow=klow, khigh=khigh,
+                top_num=num, top_den=den, n_atoms=n_atoms, seed=base - 8300 + seed)

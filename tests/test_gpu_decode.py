@@ -125,29 +125,9 @@ def test_tall_value_weight_tiles_partly_filled():
     compare(case, run_gpu(case))
 
 
-def _random_shape(seed):
-    """A seeded random decode shape over the planner's paths: rows from 1 to
-    ~200 (32- and 64-row W.Dv tiles), contexts that split a row over 1 to
-    8+ workgroups, 4 to 16 keys per thread, head dims 64/128, code lengths
-    16/32 and selected fractions from 1/20 to 1/2."""
-    rng = np.random.default_rng(9000 + seed)
-    Hkv = int(rng.choice([1, 2, 4, 8]))
-    G = int(rng.choice([1, 2, 4, 7]))
-    B = int(rng.integers(1, 8))
-    T = int(rng.choice([1, 7, 500, 4096, 4097, 9000, 20000, 60000]))
-    d = int(rng.choice([64, 128]))
-    K = int(rng.choice([16, 32]))
-    klow = int(rng.integers(1, 5))
-    khigh = int(rng.integers(klow, K + 1))
-    num, den = [(1, 20), (1, 10), (1, 4), (1, 2)][int(rng.integers(0, 4))]
-    n_atoms = int(rng.choice([777, 2048, 8192]))
-    return dict(B=B, Hq=Hkv * G, Hkv=Hkv, T=T, d=d, K=K, klow=klow, khigh=khigh,
-                top_num=num, top_den=den, n_atoms=n_atoms, seed=700 + seed)
-
-
 @pytest.mark.parametrize("seed", range(20))
 def test_random_shapes(seed):
-    kw = _random_shape(seed)
+    kw = H.random_decode_shape(seed)
     # record layouts in turn: a separate low plane, none (the first klow
     # words read from the key records), interleaved key/value records
     layout = seed % 3

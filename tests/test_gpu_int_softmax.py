@@ -130,3 +130,11 @@ def test_int_softmax_128k_layer_sampled():
     o = run_int(case, interleaved=True, debug=False)["out"]
     assert H.rel_l2(o, g["out"]) < 1e-5
     H.log(f"  128k: p_int exact on {Hq} heads; group {gk} out {o_err:.2e}")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_int_softmax_random_shapes(seed):
+    kw = H.random_decode_shape(seed, base=9100)
+    H.log(f"integer softmax: random shape {seed}: {kw}")
+    case = synth.decode_case(**kw)
+    check(case, run_int(case, interleaved=seed % 2 == 1), f"random {seed}")

@@ -128,3 +128,14 @@ def test_reading_b_128k_layer():
     o = run(case, interleaved=True, debug=False)["out"]
     assert H.rel_l2(o, g["out"]) < 1e-5
     H.log(f"  128k reading B: group {gk} sel-diff-rows {ndiff} out {o_err:.2e}")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_reading_b_random_shapes(seed):
+    kw = H.random_decode_shape(seed, base=9200)
+    # value low words in turn from their own plane, the value records, the
+    # interleaved records
+    layout = seed % 3
+    H.log(f"reading B: random shape {seed}, layout {layout}: {kw}")
+    case = synth.decode_case(**kw)
+    check(case, run(case, val_low=layout == 0, interleaved=layout == 2), f"random {seed}")

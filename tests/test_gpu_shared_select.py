@@ -167,3 +167,11 @@ def test_shared_select_fp32_dictionary():
     case.dv = synth.make_dictionary(rng, 2048, 128, "f32")
     case.dict_dtype = "f32"
     check(case, run(case), "fp32 dictionaries")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_shared_select_random_shapes(seed):
+    kw = H.random_decode_shape(seed, base=9300)
+    H.log(f"shared selection: random shape {seed}: {kw}")
+    case = synth.decode_case(**kw)
+    check(case, run(case, interleaved=seed % 2 == 1, q_f32=seed % 4 == 2), f"random {seed}")
