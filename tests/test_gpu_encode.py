@@ -236,3 +236,35 @@ def test_prefill_encode_full_size_sampled(stream):
     pick = np.sort(rng.choice(e.x.shape[0], 16384, replace=False))
     sub = {k: v[pick] for k, v in g.items()}
     compare(e.x[pick], e.dictionary, 16, sub, f"prefill stream {stream} sample")
+
+
+def random_encode_shape(seed):
+    """A seeded random encode problem: vector counts on the small path
+    (n <= 64) and the batch path, dictionaries from 17 to 12,000 atoms,
+    head dims 64/128, code lengths 1 to 32, bf16 or fp32 inputs and
+    dictionaries, with and without the low plane."""
+    rng = np.random.default_rng(9400 + seed)
+    return dict(n=int(rng.choice([33, 64, 65, 300, 1500])),
+                N=int(rng.choice([17, 1000, 4096, 12000])),
+                d=int(rng.choice([64, 128])), K=int(rng.integers(1, 33)),
+                x_dtype=str(rng.choice(["bf16", "f32"])),
+                dict_dtype=str(rng.choice(["bf16", "f32"])),
+                klow=int(rng.integers(0, 5)), seed=1100 + seed)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shapes(seed):
+    s = random_encode_shape(seed)
+    H.log(f"encode random shape {seed}: {s}")
+    rng = np.random.default_rng(s["seed"])
+    D = synth.make_dictionary(rng, s["N"], s["d"], s["dict_dtype"])
+    # at most a quarter of the atoms in each vector (the distinct-index draw
+    # rejects duplicates, which a near-full draw would take forever to avoid)
+    x, _, _ = synth.make_sparse_vectors(rng, D, s["n"], min(16, s["N"] // 4), 0.05, "absdesc")
+    if s["x_dtype"] == "bf16":
+        x = synth.bf16_round(x)
+    klow = min(s["klow"], s["K"])
+    g = run(x, D, s["K"], x_dtype=s["x_dtype"], dict_dtype=s["dict_dtype"], klow=klow)
+    compare(x, D, s["K"], g, f"random {seed}")
+    if klow:
+        assert np.array_equal(g["low_plane"], g["codes"][:, :klow])
