@@ -474,9 +474,26 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
         const int64_t i = min((int64_t)(tid + j * SB), ns - 1);
         const int64_t t = all ? i : ((i >> 4) * a.T) / kSampleRuns + (i & 15);
         wps[j] = lo + t * lw;
+        // (klow = 3 gets its own straight path: every instruction this kernel
+        // runs is fetched from L2 once per compute unit, at a measured
+        // ~0.3 us per KB, so shorter executed code is faster code)
+        if (low3) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) wd[j][c] = wps[j][min(c, a.klow - 1)];
+          for (int c = 0; c < 3; ++c) wd[j][c] = wps[j][c];
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) wd[j][c] = wps[j][min(c, a.klow - 1)];
+        }
       }
+      if (low3) {
+#pragma unroll
+        for (int j = 0; j < kSamplePT; ++j) {
+          float s = 0.f;
+#pragma unroll
+          for (int c = 0; c < 3; ++c) s = fmaf(code_coef(wd[j][c]), s_u[code_idx(wd[j][c]) & AMASK], s);
+          skey[j] = (tid + j * SB < ns) ? float_key(s) : 0u;
+        }
+      } else
 #pragma unroll
       for (int j = 0; j < kSamplePT; ++j) {
         const uint32_t* wp = wps[j];
@@ -582,7 +599,15 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
     for (int r = 0; r < kTokBatch; ++r) {
       const int64_t i = base + (int64_t)r * SB + tid;
       float s = 0.f, va = 0.f;
-      if (FAST) {
+      if (FAST && a.khigh == 16) {
+        // (the usual khigh: no per-pair test, and the 16 table reads issue
+        // together)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          s = fmaf(code_coef(kw[r][q]), s_u[code_idx(kw[r][q]) & AMASK], s);
+          va += fabsf(code_coef(vw[r][q]));
+        }
+      } else if (FAST) {
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
           if (q < a.khigh) s = fmaf(code_coef(kw[r][q]), s_u[code_idx(kw[r][q]) & AMASK], s);
