@@ -158,41 +158,39 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-// Exclusive scan over the block (NW waves). `tmp` holds >= NW words of LDS.
-// Returns the exclusive prefix; *total receives the block total.
-template <int NW>
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* tmp, uint32_t* total) {
-  const uint32_t inc = wave_incl_scan(v);
-  if (lane_id() == 63) tmp[wave_id()] = inc;
-  __syncthreads();
-  uint32_t base = 0, tot = 0;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    const uint32_t s = tmp[i];
-    base += (i < wave_id()) ? s : 0u;
-    tot += s;
-  }
-  __syncthreads();
-  *total = tot;
-  return base + inc - v;
+// Inclusive scan over each row of 16 lanes (row_shr 1, 2, 4, 8).
+__device__ __forceinline__ uint32_t row16_incl_scan(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  return v;
 }
-// The same scan without its closing barrier: the caller passes a workgroup
-// barrier before `tmp` is written again.
+// Exclusive scan over the block (NW <= 16 waves) without its closing
+// barrier: the caller passes a workgroup barrier before `tmp` (>= NW words of
+// LDS) is written again. Returns the exclusive prefix; *total receives the
+// block total. The wave totals are scanned across the 16 lanes of each row
+// and read back with scalar lane reads (short code: this library's kernels
+// are bound in part by fetching the instructions they execute).
 template <int NW>
 __device__ __forceinline__ uint32_t block_excl_scan_open(uint32_t v, uint32_t* tmp,
                                                          uint32_t* total) {
+  static_assert(NW >= 1 && NW <= 16, "one row of lanes scans the wave totals");
   const uint32_t inc = wave_incl_scan(v);
-  if (lane_id() == 63) tmp[wave_id()] = inc;
+  const int w = wave_id();
+  if (lane_id() == 63) tmp[w] = inc;
   __syncthreads();
-  uint32_t base = 0, tot = 0;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    const uint32_t s = tmp[i];
-    base += (i < wave_id()) ? s : 0u;
-    tot += s;
-  }
-  *total = tot;
-  return base + inc - v;
+  const int r = lane_id() & 15;
+  const uint32_t ws = row16_incl_scan(r < NW ? tmp[r] : 0u);
+  *total = (uint32_t)__builtin_amdgcn_readlane((int)ws, NW - 1);
+  const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)ws, (w + 63) & 63);
+  return (w > 0 ? base : 0u) + inc - v;
+}
+template <int NW>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* tmp, uint32_t* total) {
+  const uint32_t ex = block_excl_scan_open<NW>(v, tmp, total);
+  __syncthreads();
+  return ex;
 }
 template <int NW>
 __device__ __forceinline__ float block_max(float v, float* tmp) {
