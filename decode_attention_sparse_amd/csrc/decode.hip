@@ -795,7 +795,7 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
 #pragma unroll
           for (int q = 0; q < 16; ++q)
             atomicAdd((uint32_t*)&s_w[code_idx(vw[r][q]) & AMASK],
-                      (uint32_t)(int32_t)rintf(ps * code_coef(vw[r][q])));
+                      (uint32_t)(int32_t)rintf(fmaf(code_coef(vw[r][q]), ps, 0.f)));
         } else {
           const int64_t t = in_lds ? t0 + s_lt[i] : (int64_t)sel_g[i];
           const uint32_t* vr = vbase + min(max(t, (int64_t)0), a.T - 1) * a.rs;

@@ -46,10 +46,12 @@ __device__ __forceinline__ float code_coef(uint32_t w) { return f16_bits_to_f32(
 
 // Order-preserving map float -> uint32 (larger float -> larger key). Finite
 // scores never map to 0, which marks "no token" in the select kernels.
+// Adding +0 turns -0 into +0 (so both compare equal) and leaves every other
+// non-NaN value as it is; negative values are then complemented and others
+// get the top bit set, in three integer ops.
 __device__ __forceinline__ uint32_t float_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  u = (u == 0x80000000u) ? 0u : u;  // -0 and +0 compare equal
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __float_as_uint(f + 0.f);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 __device__ __forceinline__ float key_float(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
