@@ -700,13 +700,20 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
         st_agent(&ix[4 * p + 1], __float_as_uint(mn));
       }
       const bool ok = group_barrier(grp.bar, (uint32_t)a.P, ++nbar, grp.local, grp.wait);
-      if (tid == 0) {
-        for (int q = 0; q < a.P && ok; ++q) {
-          smax = fmaxf(smax, __uint_as_float(ld_agent(&ix[4 * q])));
-          smin = fminf(smin, __uint_as_float(ld_agent(&ix[4 * q + 1])));
+      if (wave_id() == 0) {
+        // lane q reads workgroup q's pair: all P loads in one round trip
+        const int l = lane_id();
+        float qmax = smax, qmin = smin;
+        if (ok && l < a.P) {
+          qmax = __uint_as_float(ld_agent(&ix[4 * l]));
+          qmin = __uint_as_float(ld_agent(&ix[4 * l + 1]));
         }
-        sh.bcast[0] = __float_as_uint(smax);
-        sh.bcast[1] = __float_as_uint(smin);
+        qmax = fmaxf(wave_max(qmax), smax);
+        qmin = fminf(-wave_max(-qmin), smin);
+        if (l == 0) {
+          sh.bcast[0] = __float_as_uint(qmax);
+          sh.bcast[1] = __float_as_uint(qmin);
+        }
       }
       __syncthreads();
       smax = __uint_as_float(sh.bcast[0]);
@@ -726,10 +733,11 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
     if (a.P > 1) {
       if (tid == 0) st_agent(&ix[4 * p + 2], tot);
       const bool ok = group_barrier(grp.bar, (uint32_t)a.P, ++nbar, grp.local, grp.wait);
-      if (tid == 0) {
-        uint32_t t = ok ? 0u : tot;
-        for (int q = 0; q < a.P && ok; ++q) t += ld_agent(&ix[4 * q + 2]);
-        sh.bcast[2] = t;
+      if (wave_id() == 0) {
+        const int l = lane_id();
+        const uint32_t e = (ok && l < a.P) ? ld_agent(&ix[4 * l + 2]) : 0u;
+        const uint32_t t = ok ? wave_sum_u32(e) : tot;
+        if (l == 0) sh.bcast[2] = t;
       }
       __syncthreads();
       tot = sh.bcast[2];

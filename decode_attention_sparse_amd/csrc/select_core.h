@@ -511,12 +511,21 @@ __device__ __forceinline__ bool sample_window_select(const uint32_t (&key)[SPT],
   // --- threshold bin from the counts above and the summed count tables --------
   if (tid < P) s_qcnt[tid] = ld_agent(&g.xchg[2 * tid]);
   {
+    // eight tables' entries requested before any is added (one round trip
+    // to L2 per eight workgroups instead of one per workgroup)
     uint32_t h0 = 0, h1 = 0;
-    for (int q = 0; q < P; ++q) {
-      const uint64_t e = __hip_atomic_load((const uint64_t*)(wt + (int64_t)q * 2048 + 2 * tid),
-                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      h0 += (uint32_t)e & 0xFFFFu;
-      h1 += (uint32_t)(e >> 32) & 0xFFFFu;
+    for (int q0 = 0; q0 < P; q0 += 8) {
+      uint64_t e[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        e[k] = __hip_atomic_load((const uint64_t*)(wt + (int64_t)min(q0 + k, P - 1) * 2048 + 2 * tid),
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint64_t ek = (q0 + k < P) ? e[k] : 0ull;
+        h0 += (uint32_t)ek & 0xFFFFu;
+        h1 += (uint32_t)(ek >> 32) & 0xFFFFu;
+      }
     }
     sh.hist[2 * tid] = h0;
     sh.hist[2 * tid + 1] = h1;
