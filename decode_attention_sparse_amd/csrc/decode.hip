@@ -524,12 +524,19 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   float* sh_g = a.s_high + ((int64_t)row * a.P + p) * a.chunk;
   uint32_t nsel;
   const uint32_t lbase = block_excl_scan<SNW>((uint32_t)__popc(sel), sh.tmp, &nsel);
+  if (nsel <= (uint32_t)kListCap) {
+    // (the usual case, no per-token test of the list's capacity)
 #pragma unroll
-  for (int j = 0; j < SPT; ++j) {
-    if ((sel >> j) & 1u) {
-      const uint32_t r = lbase + (uint32_t)__popc(sel & ((1u << j) - 1u));
-      if (r < (uint32_t)kListCap) s_lt[r] = (uint16_t)(j * SB + tid);
-      else sel_g[r] = (int32_t)(t0 + (int64_t)j * SB + tid);
+    for (int j = 0; j < SPT; ++j)
+      if ((sel >> j) & 1u) s_lt[lbase + (uint32_t)__popc(sel & ((1u << j) - 1u))] = (uint16_t)(j * SB + tid);
+  } else {
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) {
+      if ((sel >> j) & 1u) {
+        const uint32_t r = lbase + (uint32_t)__popc(sel & ((1u << j) - 1u));
+        if (r < (uint32_t)kListCap) s_lt[r] = (uint16_t)(j * SB + tid);
+        else sel_g[r] = (int32_t)(t0 + (int64_t)j * SB + tid);
+      }
     }
   }
   const int64_t cnt = nsel;
@@ -768,7 +775,11 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   const int sexp = (vbound > 0.f) ? 30 - ilogbf(vbound) - 1 : 0;
   const float S = ldexpf(1.f, min(sexp, 100));
   int32_t* s_w = (int32_t*)s_u;
-  for (int i = tid; i < a.N; i += SB) s_w[i] = 0;
+  {
+    const int n4 = a.N >> 2;
+    for (int i = tid; i < n4; i += SB) ((int4*)s_w)[i] = make_int4(0, 0, 0, 0);
+    for (int i = (n4 << 2) + tid; i < a.N; i += SB) s_w[i] = 0;
+  }
   if (!in_lds) __threadfence_block();
   __syncthreads();
   float lsum = 0.f;
@@ -844,11 +855,12 @@ __global__ __launch_bounds__(SB) void k_rows(RowsArgs a) {
   // (streaming stores: the partials are read once, by the next kernel)
   for (int i = tid; i < n8; i += SB) {
     const int4 v0 = ((const int4*)s_w)[2 * i], v1 = ((const int4*)s_w)[2 * i + 1];
+    // (pairs converted together: one v_cvt_pk_f16_f32, round to nearest even)
     u32x4 h;
-    h[0] = f32_to_f16_bits((float)v0.x * 0x1p-16f) | (f32_to_f16_bits((float)v0.y * 0x1p-16f) << 16);
-    h[1] = f32_to_f16_bits((float)v0.z * 0x1p-16f) | (f32_to_f16_bits((float)v0.w * 0x1p-16f) << 16);
-    h[2] = f32_to_f16_bits((float)v1.x * 0x1p-16f) | (f32_to_f16_bits((float)v1.y * 0x1p-16f) << 16);
-    h[3] = f32_to_f16_bits((float)v1.z * 0x1p-16f) | (f32_to_f16_bits((float)v1.w * 0x1p-16f) << 16);
+    h[0] = f32x2_to_f16x2_bits((float)v0.x * 0x1p-16f, (float)v0.y * 0x1p-16f);
+    h[1] = f32x2_to_f16x2_bits((float)v0.z * 0x1p-16f, (float)v0.w * 0x1p-16f);
+    h[2] = f32x2_to_f16x2_bits((float)v1.x * 0x1p-16f, (float)v1.y * 0x1p-16f);
+    h[3] = f32x2_to_f16x2_bits((float)v1.z * 0x1p-16f, (float)v1.w * 0x1p-16f);
     __builtin_nontemporal_store(h, (u32x4*)(dst + 8 * i));
   }
   for (int i = (n8 << 3) + tid; i < a.N; i += SB)

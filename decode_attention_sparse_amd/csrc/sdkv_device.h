@@ -37,6 +37,13 @@ __device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
   _Float16 h = (_Float16)f;  // v_cvt_f16_f32, round to nearest even
   return (uint32_t)__builtin_bit_cast(uint16_t, h);
 }
+// two fp32 values as packed binary16 (lo, hi), each rounded to nearest even
+typedef _Float16 f16x2v __attribute__((ext_vector_type(2)));
+typedef float f32x2c __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_f16x2_bits(float lo, float hi) {
+  const f32x2c v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2v));
+}
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
 }

@@ -33,6 +33,7 @@ struct int4 {
 };
 inline float2 make_float2(float x, float y) { return float2{x, y}; }
 inline float4 make_float4(float x, float y, float z, float w) { return float4{x, y, z, w}; }
+inline int4 make_int4(int x, int y, int z, int w) { return int4{x, y, z, w}; }
 inline float __expf(float x) { return expf(x); }
 inline int __clz(uint32_t x) { return x ? __builtin_clz(x) : 32; }
 inline int __clzll(unsigned long long x) { return x ? __builtin_clzll(x) : 64; }
@@ -161,6 +162,9 @@ inline uint32_t f32_to_f16_bits(float x) {
   if (m == 2048u) { m = 1024u; ++E; }
   if (E >= 31u) return s | 0x7C00u;
   return s | (E << 10) | (m - 1024u);
+}
+inline uint32_t f32x2_to_f16x2_bits(float lo, float hi) {
+  return f32_to_f16_bits(lo) | (f32_to_f16_bits(hi) << 16);
 }
 inline uint32_t code_idx(uint32_t w) { return w & 0xFFFFu; }
 inline float code_coef(uint32_t w) { return f16_bits_to_f32(w >> 16); }
