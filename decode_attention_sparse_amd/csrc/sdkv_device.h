@@ -260,10 +260,17 @@ struct WaitCtl {
 __device__ __forceinline__ uint32_t hw_xcc_id() {
   return (uint32_t)__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 0xFu;  // HW_REG_XCC_ID
 }
+// `seen`: the counter's value as this workgroup's own arrival left it (the
+// arrival's returned value plus its increment): the last workgroup to arrive
+// sees the target there and needs no poll.
 __device__ __forceinline__ bool spin_until(uint32_t* ctr, uint32_t mask, uint32_t target,
-                                           const WaitCtl& w, uint32_t* last) {
-  uint32_t spins = 0, v;
+                                           const WaitCtl& w, uint32_t* last, uint32_t seen) {
+  uint32_t spins = 0, v = seen;
   bool ok = true;
+  if ((v & mask) >= target) {
+    *last = v;
+    return true;
+  }
   while (((v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) & mask) < target) {
     __builtin_amdgcn_s_sleep(1);
     if (++spins > w.limit) {
@@ -284,22 +291,24 @@ __device__ __forceinline__ bool group_barrier(uint32_t* bar, uint32_t P, uint32_
   if (threadIdx.x == 0 && !local) {
     // rows spread over XCDs: everyone releases, arrives, waits, acquires
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __hip_atomic_fetch_add(&bar[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t seen = __hip_atomic_fetch_add(&bar[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
     uint32_t v;
-    const bool ok = spin_until(&bar[0], 0xFFFFu, target, w, &v);
+    const bool ok = spin_until(&bar[0], 0xFFFFu, target, w, &v, seen);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     s_ok = ok;
   } else if (threadIdx.x == 0) {
     const bool remote = hw_xcc_id() != (blockIdx.x & 7u);
     if (remote) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __hip_atomic_fetch_add(&bar[0], 1u | ((uint32_t)remote << 16), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t inc = 1u | ((uint32_t)remote << 16);
+    const uint32_t seen = __hip_atomic_fetch_add(&bar[0], inc, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT) + inc;
     uint32_t v;
-    bool ok = spin_until(&bar[0], 0xFFFFu, target, w, &v);
+    bool ok = spin_until(&bar[0], 0xFFFFu, target, w, &v, seen);
     if ((v >> 16) != 0u) {
       if (!remote) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      __hip_atomic_fetch_add(&bar[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      ok = spin_until(&bar[1], 0xFFFFFFFFu, target, w, &v) && ok;
+      const uint32_t seen1 =
+          __hip_atomic_fetch_add(&bar[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+      ok = spin_until(&bar[1], 0xFFFFFFFFu, target, w, &v, seen1) && ok;
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     s_ok = ok;
