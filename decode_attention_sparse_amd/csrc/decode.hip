@@ -81,6 +81,24 @@ __global__ __launch_bounds__(256) void k_utable_bf16(UArgs a) {
     const bool split = kind == 1 || a.q_f32;
     for (int p0 = 0; p0 < nrows; p0 += UQR) {
       __syncthreads();  // the previous pass's fragments have been read
+      if (!split) {
+        // bf16 query rows: every item's 16 bytes requested before any is
+        // stored (one round trip instead of one per item)
+        constexpr int IT = UQR * 16 / 256;  // items per thread at d = 128
+        u32x4 raw[IT];
+#pragma unroll
+        for (int k = 0; k < IT; ++k) {
+          const int it = tid + 256 * k, r = it / segs, sg = it % segs, row = p0 + r;
+          raw[k] = u32x4{0u, 0u, 0u, 0u};
+          if (it < UQR * segs && row < nrows)
+            raw[k] = *(const u32x4*)((const uint16_t*)a.q + (int64_t)row * a.d + 8 * sg);
+        }
+#pragma unroll
+        for (int k = 0; k < IT; ++k) {
+          const int it = tid + 256 * k, r = it / segs, sg = it % segs;
+          if (it < UQR * segs) *(u32x4*)(s_qh + r * UQP + 8 * sg) = raw[k];
+        }
+      } else
       // stage: item = (row, 8-element segment), UQR * segs <= 1024 items
       for (int it = tid; it < UQR * segs; it += 256) {
         const int r = it / segs, sg = it % segs, row = p0 + r;
